@@ -1,0 +1,120 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the
+pins in test_oracle_pins.py catch each one."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.nf4_oracle as core
+import test_oracle_pins as pins
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(core, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(test_fn):
+    with pytest.raises(AssertionError):
+        test_fn()
+
+
+def test_swapped_nibble_order_is_caught(monkeypatch):
+    def bad(codes):
+        c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+        if c.size % 2:
+            c = np.concatenate([c, np.array([7], np.uint8)])
+        return (c[1::2] | (c[0::2] << 4)).astype(np.uint8)
+    _patch(monkeypatch, "pack_nibbles", bad)
+    _fails(pins.test_pack_layout_by_hand_and_odd_tail)
+
+
+def test_dropped_lora_scale_is_caught(monkeypatch):
+    def bad(x, w, a, b, s):
+        t = x @ a.T
+        return x @ w.T + t @ b.T, t
+    _patch(monkeypatch, "forward_f64", bad)
+    _fails(pins.test_forward_equals_triple_loop)
+
+
+def test_wrong_sign_in_backward_is_caught(monkeypatch):
+    def bad(dy, x, w, a, b, s, t=None):
+        t = x @ a.T if t is None else t
+        g = dy @ b
+        return dy @ w - s * (g @ a), s * (g.T @ x), s * (dy.T @ t)
+    _patch(monkeypatch, "backward_f64", bad)
+    _fails(pins.test_backward_matches_finite_differences)
+
+
+def test_missing_scale_on_adapter_grad_is_caught(monkeypatch):
+    def bad(dy, x, w, a, b, s, t=None):
+        t = x @ a.T if t is None else t
+        g = dy @ b
+        return dy @ w + s * (g @ a), g.T @ x, s * (dy.T @ t)
+    _patch(monkeypatch, "backward_f64", bad)
+    _fails(pins.test_backward_matches_finite_differences)
+
+
+def test_ties_to_upper_code_is_caught(monkeypatch):
+    real_t = core.nf4_thresholds
+
+    def bad_codes(w, absmax):
+        flat = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+        c = absmax[np.arange(flat.size) // 64]
+        n = np.where(c != 0, flat / np.where(c != 0, c, 1), 0).astype(np.float32)
+        return (n[:, None] >= real_t()[None, :]).sum(1).astype(np.uint8)
+    _patch(monkeypatch, "nf4_codes", bad_codes)
+    _fails(pins.test_ties_at_thresholds_go_to_lower_code)
+
+
+def test_round_half_up_in_dq_is_caught(monkeypatch):
+    def bad(absmax):
+        c = np.asarray(absmax, np.float32)
+        ng = -(-c.size // 256)
+        q = np.zeros(c.size, np.uint8)
+        d = np.zeros(ng, np.float32)
+        for g in range(ng):
+            seg = c[256 * g: 256 * g + 256]
+            if seg.max() == 0:
+                continue
+            d[g] = np.float32(seg.max()) / np.float32(255)
+            q[256 * g: 256 * g + 256] = np.minimum(np.floor(seg / d[g] + np.float32(0.5)), 255)
+        return q, d
+    _patch(monkeypatch, "double_quantize", bad)
+    _fails(pins.test_dq_rint_half_even_and_clamp_by_hand)
+
+
+def test_swapped_level_split_is_caught(monkeypatch):
+    import statistics
+    inv = statistics.NormalDist().inv_cdf
+    dl = pins.DELTA
+
+    def bad():
+        pos = [inv(dl + (0.5 - dl) * i / 7.0) for i in range(7)]
+        neg = [-inv(dl + (0.5 - dl) * i / 8.0) for i in range(8)]
+        v = sorted(pos + neg + [0.0])
+        return (np.array(v) / max(v)).astype(np.float32)
+    monkeypatch.setattr(pins, "L", bad())
+    _fails(pins.test_levels_shape_order_and_anchor_values)
+
+
+def test_truncating_bf16_is_caught(monkeypatch):
+    def bad(x):
+        return (np.ascontiguousarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    _patch(monkeypatch, "bf16_rne_bits", bad)
+    _fails(pins.test_bf16_rne_matches_torch_cast)
+
+
+def test_dq_without_rounding_cprime_is_caught(monkeypatch):
+    # dequantizing with the fp32 block constant instead of q*d breaks the
+    # decoded value of the absmax element
+    real = core.nf4_dequantize
+
+    def bad(packed, q, d, numel):
+        lv = core.nf4_levels()
+        codes = core.unpack_nibbles(packed, numel)
+        blk = np.arange(numel) // 64
+        cprime = (q.astype(np.float32) + np.float32(0.5))[blk] * d[blk // 256]
+        return core.bf16_rne_bits(lv[codes] * cprime)
+    _patch(monkeypatch, "nf4_dequantize", bad)
+    _fails(pins.test_absmax_element_decodes_to_plus_minus_cprime)

@@ -1,0 +1,380 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each test checks the oracle against what the source pages print (fixtures in
+tests/golden/, with citations), a closed form, an independent library
+routine, or brute force on tiny inputs.  No GPU; no HIP library.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from bit_nf4_quantized_14_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+FACTS = json.load(open(GOLDEN))
+
+L = oracle.nf4_levels()
+T = oracle.nf4_thresholds()
+DELTA = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0)
+
+
+# --------------------------------------------------------------------------
+# Codebook
+# --------------------------------------------------------------------------
+
+def test_levels_shape_order_and_anchor_values():
+    # "Qlora Expert", Core Concept: 16 levels; spec: sorted, with -1, 0, +1
+    assert L.dtype == np.float32 and L.shape == (FACTS["nf4_level_count"]["value"],)
+    assert np.all(np.diff(L.astype(np.float64)) > 0)
+    assert L[0] == -1.0 and L[7] == 0.0 and L[15] == 1.0
+    assert int((L < 0).sum()) == 7 and int((L > 0).sum()) == 8
+
+
+def _phi(x):
+    """Standard normal CDF through math.erfc (a route independent of the
+    inverse CDF the oracle uses)."""
+    return 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def test_levels_are_normal_quantiles_of_equally_spaced_probabilities():
+    # "Qlora Expert", Core Concept: levels at the quantiles of N(0,1).
+    # Undo the normalisation with z_max = Phi^-1(delta) from scipy (a second
+    # library), then check with the CDF that the positive levels sit at
+    # probabilities spaced (delta-1/2)/8 and the negative at (delta-1/2)/7.
+    zmax = float(scipy.special.ndtri(DELTA))
+    pos = [_phi(float(v) * zmax) for v in L[8:]]          # ascending
+    neg = [_phi(-float(v) * zmax) for v in L[:7]]         # 1 - Phi(|v|)
+    step8 = (DELTA - 0.5) / 8.0
+    step7 = (DELTA - 0.5) / 7.0
+    for i, p in enumerate(reversed(pos)):
+        assert abs(p - (DELTA - i * step8)) < 2e-7
+    for i, p in enumerate(neg):
+        assert abs(p - (DELTA - i * step7)) < 2e-7
+
+
+def test_thresholds_are_fp32_midpoints():
+    assert T.dtype == np.float32 and T.shape == (15,)
+    for j in range(15):
+        exact = (Fraction(float(L[j])) + Fraction(float(L[j + 1]))) / 2
+        # the midpoint of two fp32 in [-1,1] is exactly representable in f64
+        assert Fraction(float(np.float64(L[j]) / 2 + np.float64(L[j + 1]) / 2)) == exact
+        assert T[j] == np.float32(float(exact))
+        assert L[j] < T[j] < L[j + 1]
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding and fp32 division
+# --------------------------------------------------------------------------
+
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(0.03),
+        rng.standard_normal(1000).astype(np.float32) * np.float32(1e30),
+        np.array([0.0, -0.0, 1.0, -1.0, 1e-38, 3e-41], dtype=np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_rne_bits(x), ref)
+
+
+def test_bf16_rne_ties_to_even_by_hand():
+    # 1 + 2^-8 is the exact midpoint of 1 and 1 + 2^-7: ties to 1 (even)
+    # 1 + 3*2^-8 is the midpoint of 1+2^-7 and 1+2^-6: ties to 1+2^-6 (even)
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20],
+                 dtype=np.float32)
+    got = oracle.bf16_bits_to_f64(oracle.bf16_rne_bits(x))
+    assert got.tolist() == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7]
+
+
+def test_fp32_division_is_correctly_rounded():
+    # The oracle's n = w / c must be the IEEE fp32 quotient.  An f64 quotient
+    # of two fp32 rounded once more to fp32 is correctly rounded (53 >= 2*24+2),
+    # which is an independent route to the same value.
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((512, 64)) * 0.02).astype(np.float32)
+    c = oracle.block_absmax(w)
+    codes = oracle.nf4_codes(w, c)
+    n_ref = (w.astype(np.float64) / c[:, None].astype(np.float64)).astype(np.float32)
+    codes_ref = np.array([[int((T < v).sum()) for v in row] for row in n_ref[:64]])
+    assert np.array_equal(codes.reshape(512, 64)[:64], codes_ref)
+
+
+# --------------------------------------------------------------------------
+# Quantization: round-trip bounds and brute force
+# --------------------------------------------------------------------------
+
+def _small_weight(seed=3, shape=(256, 512)):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    mask = rng.random(shape) < 2e-3
+    w[mask] = (0.1 * rng.standard_t(3, size=int(mask.sum()))).astype(np.float32)
+    return w
+
+
+def test_codes_equal_brute_force_nearest_level():
+    w = _small_weight()
+    flat = w.reshape(-1)
+    c = oracle.block_absmax(w)
+    codes = oracle.nf4_codes(w, c)
+    n = flat.astype(np.float64) / np.repeat(c, 64).astype(np.float64)
+    dist = np.abs(n[:, None] - L.astype(np.float64)[None, :])
+    nearest = dist.argmin(axis=1)
+    near_tie = np.min(np.abs(n[:, None] - T.astype(np.float64)[None, :]), axis=1) < 2.0 ** -22
+    assert int(near_tie.sum()) < 5
+    assert np.array_equal(codes[~near_tie], nearest[~near_tie])
+
+
+def test_absmax_brute_force():
+    w = _small_weight(seed=5, shape=(7, 100))          # 700 = 10 full blocks + 60
+    c = oracle.block_absmax(w)
+    flat = w.reshape(-1)
+    ref = [max(abs(float(v)) for v in flat[s:s + 64]) for s in range(0, 700, 64)]
+    assert c.tolist() == [np.float32(v) for v in ref]
+
+
+def test_roundtrip_without_dq_within_half_gap_times_absmax():
+    # spec: quantize->dequantize error <= half the level gap x absmax
+    w = _small_weight()
+    c = oracle.block_absmax(w)
+    codes = oracle.nf4_codes(w, c)
+    cb = np.repeat(c, 64).astype(np.float64)
+    err = np.abs(w.reshape(-1).astype(np.float64) - L.astype(np.float64)[codes] * cb)
+    gaps = np.diff(L.astype(np.float64))
+    n = w.reshape(-1).astype(np.float64) / cb
+    j = np.clip(np.searchsorted(L.astype(np.float64), n) - 1, 0, 14)
+    assert np.all(err <= (0.5 * gaps[j] + 2.0 ** -22) * cb)
+    assert np.all(err <= (0.5 * gaps.max() + 2.0 ** -22) * cb)
+    assert abs(gaps.max() - (L[1] - L[0])) < 1e-7 and gaps.max() < 0.304
+
+
+def test_roundtrip_with_dq_bound():
+    w = _small_weight(seed=9)
+    packed, q, d = oracle.nf4_quantize(w)
+    c = oracle.block_absmax(w)
+    codes = oracle.unpack_nibbles(packed, w.size)
+    wq = oracle.bf16_bits_to_f64(oracle.nf4_dequantize(packed, q, d, w.size))
+    blk = np.arange(w.size) // 64
+    dg = d.astype(np.float64)[blk // 256]
+    cprime = q.astype(np.float64) * d.astype(np.float64)[np.arange(q.size) // 256]
+    # |c - c'| <= d/2 (rint) plus fp32 rounding of c/d and of q*d
+    assert np.all(np.abs(c - cprime) <= d.astype(np.float64)[np.arange(q.size) // 256] * (0.5 + 2.0 ** -20) + 2.0 ** -23 * c)
+    gaps = np.diff(L.astype(np.float64))
+    cb = c.astype(np.float64)[blk]
+    bound = (0.5 * gaps.max() + 2.0 ** -22) * cb + np.abs(L.astype(np.float64)[codes]) * dg * (0.5 + 2.0 ** -20) \
+        + 2.0 ** -8 * np.abs(wq) + 2.0 ** -22 * cb
+    assert np.all(np.abs(w.reshape(-1) - wq) <= bound)
+
+
+# --------------------------------------------------------------------------
+# Double quantization: closed forms and hand-built cases
+# --------------------------------------------------------------------------
+
+def test_dq_rint_half_even_and_clamp_by_hand():
+    # group max 255 -> d = 1 exactly; c = 2.5 -> 2, 3.5 -> 4, 254.5 -> 254
+    c = np.array([255.0, 2.5, 3.5, 254.5, 0.49, 0.0], dtype=np.float32)
+    q, d = oracle.double_quantize(c)
+    assert d.tolist() == [1.0]
+    assert q.tolist() == [255, 2, 4, 254, 0, 0]
+
+
+def test_dq_groups_of_256_and_tail_group():
+    rng = np.random.default_rng(1)
+    c = np.abs(rng.standard_normal(256 * 3 + 17)).astype(np.float32)
+    q, d = oracle.double_quantize(c)
+    assert q.shape == (c.size,) and d.shape == (4,)
+    for g in range(4):
+        seg = c[256 * g: 256 * g + 256]
+        assert d[g] == np.float32(seg.max()) / np.float32(255)
+        assert q[256 * g + int(seg.argmax())] == 255
+
+
+def test_dq_zero_group():
+    q, d = oracle.double_quantize(np.zeros(300, dtype=np.float32))
+    assert d.tolist() == [0.0, 0.0] and not q.any()
+
+
+def test_dq_accounting_matches_pages():
+    # "Qlora Expert", Core Concept: DQ saves about 0.37 bits/param; the
+    # 32->8 bit constants of "The 4-bit Revolution", section 2.
+    rows, cols = 1024, 4096
+    w = (np.random.default_rng(2).standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    packed, q, d = oracle.nf4_quantize(w)
+    numel = rows * cols
+    bits = 8.0 * (packed.nbytes + q.nbytes + d.nbytes) / numel
+    code_bits = 8.0 * packed.nbytes / numel
+    assert code_bits == FACTS["bits_per_weight_code"]["value"]
+    overhead = bits - code_bits
+    assert overhead == pytest.approx(8 / 64 + 32 / (64 * 256), abs=1e-12)
+    no_dq = FACTS["dq_constant_bits"]["from"] / FACTS["block_size"]["value"]   # 0.5
+    saving = no_dq - overhead
+    assert saving == pytest.approx(FACTS["dq_saving_bits_per_param"]["value"],
+                                   abs=FACTS["dq_saving_bits_per_param"]["tolerance"])
+
+
+def test_storage_matches_page_model_sizes():
+    # "The 4-bit Revolution": 7B 14 GB fp16 -> 3.5 GB NF4 (codes alone, 4x);
+    # "QLoRA Guide": 70B bf16 ~140 GB; about 35 GB in 4 bit.
+    f7 = FACTS["model_7b_gb"]
+    assert 7e9 * 16 / 8 / 1e9 == f7["fp16"]
+    assert 7e9 * FACTS["bits_per_weight_code"]["value"] / 8 / 1e9 == f7["nf4"]
+    assert f7["fp16"] / f7["nf4"] == FACTS["compression_vs_fp16"]["value"]
+    f70 = FACTS["model_70b_gb"]
+    bits = 4 + 8 / 64 + 32 / (64 * 256)
+    assert 70e9 * 16 / 8 / 1e9 == f70["bf16"]
+    assert abs(70e9 * bits / 8 / 1e9 - f70["nf4_about"]) < 1.2
+    assert FACTS["lora_scale_example"]["alpha"] / FACTS["lora_scale_example"]["r"] \
+        == FACTS["lora_scale_example"]["scale"]
+
+
+# --------------------------------------------------------------------------
+# Special cases of the codec
+# --------------------------------------------------------------------------
+
+def test_zero_block_codes_are_zero_level():
+    w = np.zeros(128, dtype=np.float32)
+    w[64 + 5] = -0.25
+    packed, q, d = oracle.nf4_quantize(w)
+    codes = oracle.unpack_nibbles(packed, 128)
+    assert np.all(codes[:64] == 7)
+    # a block with one nonzero value: that element is the extreme level
+    assert codes[64 + 5] == 0 and np.all(np.delete(codes[64:], 5) == 7)
+    assert q.tolist() == [0, 255]
+    wq = oracle.bf16_bits_to_f64(oracle.nf4_dequantize(packed, q, d, 128))
+    assert np.all(wq[:64] == 0) and wq[64 + 5] < 0
+
+
+def test_absmax_element_decodes_to_plus_minus_cprime():
+    w = _small_weight(seed=13, shape=(4, 256))
+    packed, q, d = oracle.nf4_quantize(w)
+    codes = oracle.unpack_nibbles(packed, w.size)
+    flat = w.reshape(-1)
+    wq = oracle.nf4_dequantize(packed, q, d, w.size)
+    for b in range(w.size // 64):
+        i = 64 * b + int(np.abs(flat[64 * b: 64 * b + 64]).argmax())
+        assert codes[i] == (15 if flat[i] > 0 else 0)
+        cprime = np.float32(q[b]) * d[b // 256]
+        assert wq[i] == oracle.bf16_rne_bits(np.float32(np.sign(flat[i])) * cprime)
+
+
+def test_exact_levels_roundtrip_without_dq():
+    # w = L_j * 2^k: n = L_j exactly, so the code is j
+    vals = np.array([float(v) * 2.0 ** -5 for v in L] * 4, dtype=np.float32)
+    c = oracle.block_absmax(vals)
+    assert c.tolist() == [2.0 ** -5]
+    assert oracle.nf4_codes(vals, c).tolist() == list(range(16)) * 4
+
+
+def test_pack_layout_by_hand_and_odd_tail():
+    codes = np.array([1, 2, 3, 4, 15, 0, 9], dtype=np.uint8)
+    packed = oracle.pack_nibbles(codes)
+    assert packed.tolist() == [0x21, 0x43, 0x0F, 0x79]
+    assert oracle.unpack_nibbles(packed, 7).tolist() == codes.tolist()
+
+
+def test_nonfinite_weight_raises():
+    w = np.zeros(64, dtype=np.float32)
+    w[3] = np.inf
+    with pytest.raises(ValueError):
+        oracle.nf4_quantize(w)
+
+
+def test_tail_block_and_group_shapes():
+    numel = 64 * 256 * 2 + 64 * 3 + 21
+    w = (np.random.default_rng(4).standard_normal(numel) * 0.02).astype(np.float32)
+    packed, q, d = oracle.nf4_quantize(w)
+    assert packed.size == (numel + 1) // 2
+    assert q.size == -(-numel // 64) and d.size == -(-q.size // 256)
+    wq = oracle.bf16_bits_to_f64(oracle.nf4_dequantize(packed, q, d, numel))
+    assert wq.size == numel and np.max(np.abs(wq - w)) < 0.05
+
+
+# --------------------------------------------------------------------------
+# Forward/backward: brute force, finite differences, identities
+# --------------------------------------------------------------------------
+
+def _tiny_problem(m=3, n=5, k=64, r=4, seed=21):
+    rng = np.random.default_rng(seed)
+    bits = lambda shape, s: wl.to_bf16_bits((rng.standard_normal(shape) * s).astype(np.float32))
+    return bits((m, k), 1.0), bits((n, k), 0.05), bits((r, k), 0.125), bits((n, r), 0.1), bits((m, n), 1.0)
+
+
+def test_forward_equals_triple_loop():
+    x, w, a, b, _ = _tiny_problem()
+    alpha, r = 8.0, 4
+    y, t = oracle.qlora_forward(x, w, a, b, alpha, r)
+    X, W, A, B = (oracle.bf16_bits_to_f64(v).tolist() for v in (x, w, a, b))
+    m, k = len(X), len(X[0])
+    n = len(W)
+    s = alpha / r
+    for i in range(m):
+        for j in range(n):
+            base = sum(X[i][kk] * W[j][kk] for kk in range(k))
+            lora = 0.0
+            for q in range(r):
+                tq = sum(X[i][kk] * A[q][kk] for kk in range(k))
+                assert abs(tq - t[i, q]) <= 1e-12 * (1 + abs(tq))
+                lora += tq * B[j][q]
+            ref = base + s * lora
+            assert abs(ref - y[i, j]) <= 1e-12 * (1 + abs(ref))
+
+
+def test_backward_matches_finite_differences():
+    x, w, a, b, dy = _tiny_problem()
+    X, W, A, B, DY = (oracle.bf16_bits_to_f64(v) for v in (x, w, a, b, dy))
+    s = 2.0
+    dx, da, db = oracle.backward_f64(DY, X, W, A, B, s)
+    loss = lambda X_, A_, B_: float(np.sum(DY * oracle.forward_f64(X_, W, A_, B_, s)[0]))
+    h = 1e-6
+    rng = np.random.default_rng(0)
+    for arr, grad, which in ((X, dx, 0), (A, da, 1), (B, db, 2)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, sz)) for sz in arr.shape)
+            args = [X.copy(), A.copy(), B.copy()]
+            args[which][idx] += h
+            lp = loss(*args)
+            args[which][idx] -= 2 * h
+            lm = loss(*args)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(grad[idx]))
+
+
+def test_no_gradient_to_base_and_bilinear_identities():
+    x, w, a, b, dy = _tiny_problem(m=6, n=7, k=128, r=3, seed=5)
+    alpha, r = 6.0, 3
+    y, t = oracle.qlora_forward(x, w, a, b, alpha, r)
+    out = oracle.qlora_backward(dy, x, w, a, b, alpha, r, t)
+    assert len(out) == 3          # dX, dA, dB; the frozen base has no gradient
+    dx, da, db = out
+    X, A, B, DY = (oracle.bf16_bits_to_f64(v) for v in (x, a, b, dy))
+    s = alpha / r
+    assert np.sum(DY * y) == pytest.approx(np.sum(dx * X), rel=1e-12)
+    lora = np.sum(DY * (s * t @ B.T))
+    assert np.sum(db * B) == pytest.approx(lora, rel=1e-12)
+    assert np.sum(da * A) == pytest.approx(lora, rel=1e-12)
+
+
+def test_zero_adapter_reduces_to_plain_matmul():
+    x, w, a, b, _ = _tiny_problem(m=4, n=9, k=192, r=2, seed=8)
+    b0 = np.zeros_like(b)
+    y, _ = oracle.qlora_forward(x, w, a, b0, 4.0, 2)
+    ref = np.matmul(oracle.bf16_bits_to_f64(x), oracle.bf16_bits_to_f64(w).T)
+    assert np.array_equal(y, ref)
+    y2, _ = oracle.qlora_forward(x, w, a, b, 0.0, 2)
+    assert np.array_equal(y2, ref)
+
+
+def test_ties_at_thresholds_go_to_lower_code():
+    # A block whose absmax is 1 has n = w exactly; w = t_j sits on a tie.
+    vals = np.concatenate([[1.0], T.astype(np.float64), [-1.0] * 48]).astype(np.float32)
+    c = oracle.block_absmax(vals)
+    assert c.tolist() == [1.0]
+    codes = oracle.nf4_codes(vals, c)
+    assert codes[:16].tolist() == [15] + list(range(15))
