@@ -1,0 +1,368 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA linear layer on one MI355X.
+
+One step = qlora_linear_fwd + qlora_linear_bwd of the Llama-7B gate
+projection (W 11008x4096 NF4 + double quant, X 4096 tokens, r=16, alpha=32,
+bf16 Y and dX).  The NF4 weight is dequantized on the fly inside the fused
+kernels every step.  ``value`` is fwd+bwd TFLOP/s counting only algorithmic
+matmul flops 4MNK + 6Mr(K+N).
+
+The same JSON line also reports, each timed on its own:
+  dequant7b  nf4_dequantize over the 7 projections of a 7B-class layer, HBM
+             GB/s over 2.516 B/param (packed + block codes + group scales in,
+             bf16 out)
+  quantize7b nf4_quantize over the same projections, 4.516 B/param
+  skinny70b  qlora_linear_fwd with M=8 over the 7 projections of a
+             70B-class layer, GB/s over NF4 + adapters + X + Y bytes
+  layer70b   fwd+bwd over the 7 70B-class projections, M=2048, r=64
+and the roofline of the dominant kernel from per-launch HIP events recorded
+on the library's stream, plus the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+METRIC = "fused QLoRA linear fwd+bwd TFLOP/s (7B shapes) + NF4 dequant HBM GB/s"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def linear_flops(m, n, k, r, backward=True):
+    fwd = 2 * m * n * k + 2 * m * r * (k + n)
+    bwd = 2 * m * n * k + 4 * m * r * (k + n)
+    return fwd + (bwd if backward else 0)
+
+
+class Problem:
+    """Device inputs of one projection: NF4 weight + bf16 X, A, B, dY."""
+
+    def __init__(self, wk, proj, backward=True, y_dtype=None):
+        import numpy as np
+        import torch
+        from bit_nf4_quantized_14_amd import capi
+        from bit_nf4_quantized_14_amd import workloads as wl
+
+        self.capi = capi
+        _, self.n, self.k = wk.projections[proj]
+        self.m, self.r, self.alpha = wk.m, wk.r, wk.alpha
+        dev = "cuda"
+
+        def up(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        w = torch.from_numpy(wl.weight(wk, proj)).to(dev)
+        self.w = capi.nf4_quantize(w)
+        del w
+        self.x = up(wl.activations(wk, proj))
+        self.a = up(wl.lora_a(wk, proj))
+        self.b = up(wl.lora_b(wk, proj))
+        self.dy = up(wl.grad_out(wk, proj)) if backward else None
+        ydt = capi.QN_BF16 if y_dtype is None else y_dtype
+        self.ydt = ydt
+        tdt = torch.bfloat16 if ydt == capi.QN_BF16 else torch.float32
+        self.y = torch.empty((self.m, self.n), dtype=tdt, device=dev)
+        self.t = torch.empty((self.m, self.r), dtype=torch.float32, device=dev)
+        if backward:
+            self.dx = torch.empty((self.m, self.k), dtype=tdt, device=dev)
+            self.da = torch.empty((self.r, self.k), dtype=torch.float32, device=dev)
+            self.db = torch.empty((self.n, self.r), dtype=torch.float32, device=dev)
+            nbytes = capi.qlora_workspace_bytes(self.m, self.n, self.k, self.r,
+                                                capi.QN_BWD)
+            self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    def fwd(self):
+        self.capi.qlora_linear_fwd(self.x, self.w, self.a, self.b, self.r,
+                                   self.alpha, y=self.y, y_dtype=self.ydt,
+                                   t_save=self.t)
+
+    def bwd(self):
+        self.capi.qlora_linear_bwd(self.dy, self.x, self.w, self.a, self.b,
+                                   self.r, self.alpha, self.t, dx=self.dx,
+                                   dx_dtype=self.ydt, dA=self.da, dB=self.db,
+                                   ws=self.ws)
+
+
+def kernel_times_ms(capi, name, fn, launches_per_call, reps):
+    """Average duration (ms) of each launch of kernel `name` while calling
+    fn() `reps` times, from HIP events the library records around it."""
+    import torch
+    cap = launches_per_call * reps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(cap)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(cap)]
+    capi.qn_profile_kernel(name, starts, stops)
+    for _ in range(reps):
+        fn()
+    n = capi.qn_profile_kernel(None)
+    torch.cuda.synchronize()
+    if n == 0:
+        return None, 0
+    return sum(s.elapsed_time(e) for s, e in zip(starts[:n], stops[:n])) / n, n
+
+
+def timed(fn, reps, warmup=2):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps
+
+
+def bench_dequant_quant(reps):
+    """7B-class layer: dequant and quantize GB/s over all 7 projections."""
+    import torch
+    from bit_nf4_quantized_14_amd import capi
+    from bit_nf4_quantized_14_amd import workloads as wl
+    wk = wl.workload("dequant7b")
+    tens, outs, ws32 = [], [], []
+    params = 0
+    for p in range(len(wk.projections)):
+        w = torch.from_numpy(wl.weight(wk, p)).to("cuda")
+        tens.append(capi.nf4_quantize(w))
+        ws32.append(w)
+        outs.append(torch.empty((w.shape[0], w.shape[1]), dtype=torch.bfloat16,
+                                device="cuda"))
+        params += w.numel()
+    npk = sum(t.packed.numel() + t.qabs.numel() + 4 * t.gscale.numel() for t in tens)
+    deq_bytes = npk + 2 * params
+    q_bytes = 4 * params + npk
+
+    def deq():
+        for t, o in zip(tens, outs):
+            capi.nf4_dequantize(t, o)
+
+    def quant():
+        for w, t in zip(ws32, tens):
+            capi.nf4_quantize(w, t)
+
+    res = {}
+    for name, fn, kname, nbytes in (("dequant7b", deq, "k_dequant", deq_bytes),
+                                    ("quantize7b", quant, "k_quantize", q_bytes)):
+        sec = timed(fn, reps)
+        kt, _ = kernel_times_ms(capi, kname, fn, len(tens), reps)
+        ksum = kt * len(tens) * 1e-3
+        res[name] = {"params": params, "bytes_per_pass": nbytes,
+                     "ms_per_pass": sec * 1e3,
+                     "GB/s": nbytes / sec / 1e9,
+                     "kernel": kname, "kernel_ms_per_pass": ksum * 1e3,
+                     "kernel_GB/s": nbytes / ksum / 1e9,
+                     "frac_hbm_peak": nbytes / ksum / 1e9 / HBM_PEAK_GBS}
+        log(f"{name}: {res[name]['GB/s']:.0f} GB/s wall, "
+            f"{res[name]['kernel_GB/s']:.0f} GB/s kernel")
+    del tens, outs, ws32
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_70b(reps, do_train=True):
+    import torch
+    from bit_nf4_quantized_14_amd import capi
+    from bit_nf4_quantized_14_amd import workloads as wl
+    res = {}
+    # skinny forward (M = 8)
+    wk = wl.workload("skinny70b")
+    probs = [Problem(wk, p, backward=False, y_dtype=capi.QN_F32)
+             for p in range(len(wk.projections))]
+    nbytes = 0
+    for pr in probs:
+        npk = pr.w.packed.numel() + pr.w.qabs.numel() + 4 * pr.w.gscale.numel()
+        nbytes += npk + 2 * pr.r * (pr.n + pr.k) + 2 * pr.m * pr.k + 4 * pr.m * pr.n
+
+    def skinny():
+        for pr in probs:
+            pr.fwd()
+    sec = timed(skinny, reps)
+    res["skinny70b"] = {"bytes_per_pass": nbytes, "ms_per_pass": sec * 1e3,
+                        "GB/s": nbytes / sec / 1e9,
+                        "frac_hbm_peak": nbytes / sec / 1e9 / HBM_PEAK_GBS}
+    log(f"skinny70b: {res['skinny70b']['GB/s']:.0f} GB/s")
+    del probs
+    torch.cuda.empty_cache()
+    if not do_train:
+        return res
+    wk = wl.workload("layer70b")
+    flops = 0
+    total = 0.0
+    per = {}
+    for p, (name, n, k) in enumerate(wk.projections):
+        pr = Problem(wk, p)
+
+        def step():
+            pr.fwd()
+            pr.bwd()
+        sec = timed(step, reps)
+        f = linear_flops(pr.m, n, k, pr.r)
+        per[name] = {"ms": sec * 1e3, "TFLOP/s": f / sec / 1e12}
+        flops += f
+        total += sec
+        del pr
+        torch.cuda.empty_cache()
+    res["layer70b"] = {"flops_per_pass": flops, "ms_per_pass": total * 1e3,
+                       "TFLOP/s": flops / total / 1e12,
+                       "frac_mfma_peak": flops / total / 1e12 / BF16_PEAK_TFLOPS,
+                       "per_projection": per}
+    log(f"layer70b: {res['layer70b']['TFLOP/s']:.1f} TFLOP/s")
+    return res
+
+
+def cpu_baseline(m_sample: int):
+    """The CPU oracle (as it stands) on a bounded sample of the same step:
+    the full weight is dequantized, forward+backward run on m_sample tokens."""
+    import numpy as np
+
+    import oracle
+    from bit_nf4_quantized_14_amd import workloads as wl
+    wk = wl.workload("gate7b")
+    w = wl.weight(wk, 0)
+    n, k = w.shape
+    x = wl.activations(wk, 0, m=m_sample)
+    a, b = wl.lora_a(wk, 0), wl.lora_b(wk, 0)
+    dy = wl.grad_out(wk, 0, m=m_sample)
+    packed, q, d = oracle.nf4_quantize(w)       # load-time, not timed
+    t0 = time.perf_counter()
+    wbits = oracle.nf4_dequantize(packed, q, d, w.size).reshape(n, k)
+    y, t = oracle.qlora_forward(x, wbits, a, b, wk.alpha, wk.r)
+    oracle.qlora_backward(dy, x, wbits, a, b, wk.alpha, wk.r, t)
+    sec = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    flops = linear_flops(m_sample, n, k, wk.r)
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": sec,
+            "sample": f"gate7b step on {m_sample} of {wk.m} tokens: oracle "
+                      f"dequantization of the full 11008x4096 weight + float64 "
+                      f"forward/backward; flops 4MNK+6Mr(K+N) at M={m_sample}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true",
+                    help="only the main step (no components, no CPU baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-70b", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the QLoRA linear layer is benchmarked on "
+              f"one MI355X and multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_nf4_quantized_14_amd import capi
+    from bit_nf4_quantized_14_amd import workloads as wl
+
+    capi.lib()
+    wk = wl.workload("gate7b")
+    log("generating gate7b inputs")
+    pr = Problem(wk, 0)
+    m, n, k, r = pr.m, pr.n, pr.k, pr.r
+    flops = linear_flops(m, n, k, r)
+
+    def step():
+        pr.fwd()
+        pr.bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel breakdown (outside the timed region)
+    kernels = {}
+    for kname, per_step in (("k_fwd_gemm", 1), ("k_bwd_dx_gemm", 1),
+                            ("k_rank_nt", 2), ("k_rank_tn_partial", 2),
+                            ("k_rank_tn_reduce", 2), ("k_transpose_b", 1)):
+        ms, cnt = kernel_times_ms(capi, kname, step, per_step, 3)
+        if ms is not None:
+            kernels[kname] = {"avg_ms": ms, "launches_per_step": per_step}
+    gemm_flops = {"k_fwd_gemm": 2 * m * n * k + 2 * m * n * r,
+                  "k_bwd_dx_gemm": 2 * m * n * k + 2 * m * k * r}
+    for kname, f in gemm_flops.items():
+        kernels[kname]["TFLOP/s"] = f / (kernels[kname]["avg_ms"] * 1e-3) / 1e12
+    dom = max(gemm_flops, key=lambda kn: kernels[kn]["avg_ms"])
+
+    # timed region: exactly K steps; the dominant kernel's launches are
+    # bracketed by HIP events on the library's stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    capi.qn_profile_kernel(dom, starts, stops)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    nrec = capi.qn_profile_kernel(None)
+    dom_ms = sum(s.elapsed_time(e) for s, e in zip(starts[:nrec], stops[:nrec])) / nrec
+    achieved = gemm_flops[dom] / (dom_ms * 1e-3) / 1e12
+    value = flops / sec / 1e12
+    log(f"gate7b fwd+bwd: {sec*1e3:.3f} ms/step, {value:.1f} TFLOP/s; "
+        f"{dom} {dom_ms:.3f} ms = {achieved:.1f} TFLOP/s")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,sigma^2) weights/activations of the "
+                "Llama-7B gate projection shape; no checkpoint or dataset)",
+        "config": {"workload": "gate7b: QLoRA linear fwd+bwd, W 11008x4096 "
+                               "NF4+DQ, X 4096 tokens, r=16, alpha=32, bf16 "
+                               "Y/dX",
+                   "M": m, "N": n, "K": k, "r": r, "alpha": pr.alpha,
+                   "flops_per_step": flops, "parallelism": "single-gpu"},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "avg_ms": dom_ms, "flops_per_launch": gemm_flops[dom]},
+        "kernels": kernels,
+    }
+    del pr
+    torch.cuda.empty_cache()
+    if not args.quick:
+        comps = bench_dequant_quant(max(5, args.steps // 2))
+        if not args.no_70b:
+            comps.update(bench_70b(max(3, args.steps // 4)))
+        out["components"] = comps
+        if "dequant7b" in comps:
+            out["dequant_GBps"] = comps["dequant7b"]["kernel_GB/s"]
+    if not args.quick and not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,948 @@
+// HIP kernels (gfx950 / CDNA4) and C-ABI entry points of the QLoRA NF4
+// linear-layer library.  Declarations and the contract of every entry point
+// are in include/qlora_nf4.h.
+//
+// What is computed follows the pages "Qlora Expert" (Core Concept: NF4 at
+// N(0,1) quantiles, double quantization of the block constants, bf16
+// compute), "QLoRA Implementation Details (2025 Edition)" (Step 1 NF4 Math:
+// 64-value blocks; Step 4: scale alpha/r), "QLoRA Guide" (Forward pass
+// diagram: W_bf16 x + B(A(x)); only A and B get gradients) and the "QLORA ...
+// paper summary" (Notes: load 4-bit, dequantize to BF16, multiply, adapter
+// gradients only).
+//
+// Kernels
+//   k_quantize     one workgroup per double-quant group (256 blocks)
+//   k_dequant      packed-nibble stream, 32 weights per thread
+//   k_fwd_gemm     Y = X W'^T (+ s T B^T as extra reduction steps), W'
+//                  dequantized into LDS tile by tile, bf16 MFMA 32x32x16
+//   k_bwd_dx_gemm  dX = dY W' (+ s G A), W' tile dequantized and written
+//                  transposed into LDS
+//   k_rank_nt      out[m][j] = sum_c P[m][c] R[j][c]  (T = X A^T, G = dY B)
+//   k_rank_tn_*    out[c][j] = s sum_m P[m][c] Q[m][j] (dB, dA) as split-M
+//                  partials plus a fixed-order reduction (no atomics)
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "qlora_nf4.h"
+#include "qn_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Codebook passed by value as a kernel argument (lands in SGPRs).
+struct Codebook {
+  float L[16];
+  float T[15];
+};
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1,
+                                         uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// (mask & a) | (~mask & b), a single v_bfi_b32.
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a,
+                                        uint32_t b) {
+  return (mask & a) | (~mask & b);
+}
+
+// ---------------------------------------------------------------------------
+// NF4 decode: per-block 16-entry bf16 table, byte-sliced for v_perm_b32.
+//
+// For one block with constant c' = float(q) * d, entry j is
+// bf16_rne(L[j] * c') (both products fp32).  The 16 bf16 entries are kept as
+// four 8-byte tables: low bytes of entries 0-7 (ll) and 8-15 (lh), high
+// bytes of entries 0-7 (hl) and 8-15 (hh).  A code's low 3 bits select a
+// byte with v_perm_b32; its bit 3 chooses between the two halves.
+// ---------------------------------------------------------------------------
+struct Lut {
+  uint32_t ll0, ll1, lh0, lh1, hl0, hl1, hh0, hh1;
+};
+
+__device__ __forceinline__ float block_cprime(const uint8_t* __restrict__ qabs,
+                                              const float* __restrict__ gscale,
+                                              int64_t block) {
+  return static_cast<float>(qabs[block]) * gscale[block >> 8];
+}
+
+__device__ __forceinline__ Lut make_lut(const Codebook& cb, float cp) {
+  uint32_t P[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    P[k] = pack_bf16x2(cb.L[2 * k] * cp, cb.L[2 * k + 1] * cp);
+  Lut t;
+  // P[k] bytes: [lo e2k, hi e2k, lo e2k+1, hi e2k+1]
+  t.ll0 = perm(P[1], P[0], 0x06040200u);
+  t.hl0 = perm(P[1], P[0], 0x07050301u);
+  t.ll1 = perm(P[3], P[2], 0x06040200u);
+  t.hl1 = perm(P[3], P[2], 0x07050301u);
+  t.lh0 = perm(P[5], P[4], 0x06040200u);
+  t.hh0 = perm(P[5], P[4], 0x07050301u);
+  t.lh1 = perm(P[7], P[6], 0x06040200u);
+  t.hh1 = perm(P[7], P[6], 0x07050301u);
+  return t;
+}
+
+// 8 codes (one packed dword, element i in bits 4i..4i+3) -> 8 bf16 in
+// natural order (out[i] holds elements 2i, 2i+1, low half first).
+__device__ __forceinline__ u32x4 decode8(uint32_t p, const Lut& t) {
+  const uint32_t se = p & 0x07070707u;          // codes 0,2,4,6 (low 3 bits)
+  const uint32_t so = (p >> 4) & 0x07070707u;   // codes 1,3,5,7
+  // 0xFF per byte where bit 3 of the code is set (v_perm sign replication)
+  const uint32_t me = perm(p << 4, p << 12, 0x0B090A08u);
+  const uint32_t mo = perm(p, p << 8, 0x0B090A08u);
+  const uint32_t le = bfi(me, perm(t.lh1, t.lh0, se), perm(t.ll1, t.ll0, se));
+  const uint32_t he = bfi(me, perm(t.hh1, t.hh0, se), perm(t.hl1, t.hl0, se));
+  const uint32_t lo = bfi(mo, perm(t.lh1, t.lh0, so), perm(t.ll1, t.ll0, so));
+  const uint32_t ho = bfi(mo, perm(t.hh1, t.hh0, so), perm(t.hl1, t.hl0, so));
+  // low bytes of elements 0..3 and 4..7, then high bytes
+  const uint32_t l03 = perm(lo, le, 0x05010400u);
+  const uint32_t l47 = perm(lo, le, 0x07030602u);
+  const uint32_t h03 = perm(ho, he, 0x05010400u);
+  const uint32_t h47 = perm(ho, he, 0x07030602u);
+  u32x4 r;
+  r.x = perm(h03, l03, 0x05010400u);
+  r.y = perm(h03, l03, 0x07030602u);
+  r.z = perm(h47, l47, 0x05010400u);
+  r.w = perm(h47, l47, 0x07030602u);
+  return r;
+}
+
+// One element, used for ragged tails.
+__device__ __forceinline__ uint16_t decode1(const Codebook& cb, uint32_t code,
+                                            float cp) {
+  return static_cast<uint16_t>(pack_bf16x2(cb.L[code] * cp, 0.0f) & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// K1: quantization + double quantization.  One workgroup per group of 256
+// blocks (16384 weights); each thread owns 8 consecutive weights in each of
+// 8 passes (8 lanes per 64-weight block).
+// ---------------------------------------------------------------------------
+constexpr int QZ_THREADS = 256;
+constexpr int QZ_PASSES = 8;  // 8 * 256 * 8 = 16384 weights
+
+__global__ __launch_bounds__(QZ_THREADS) void k_quantize(
+    const float* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ qabs, float* __restrict__ gscale,
+    int32_t* __restrict__ status, Codebook cb) {
+  __shared__ float s_c[256];
+  __shared__ float s_wmax[QZ_THREADS / 64];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int64_t gbase = g * (int64_t)(QN_BLOCK * QN_GROUP);
+  const int64_t nb_total = (numel + QN_BLOCK - 1) / QN_BLOCK;
+
+  float v[QZ_PASSES][8];
+  float cmine[QZ_PASSES];
+  bool finite = true;
+#pragma unroll
+  for (int it = 0; it < QZ_PASSES; ++it) {
+    const int64_t e0 = gbase + it * (QZ_THREADS * 8) + tid * 8;
+    if (e0 + 8 <= numel) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(w + e0);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(w + e0 + 4);
+      v[it][0] = a.x; v[it][1] = a.y; v[it][2] = a.z; v[it][3] = a.w;
+      v[it][4] = b.x; v[it][5] = b.y; v[it][6] = b.z; v[it][7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[it][i] = (e0 + i < numel) ? w[e0 + i] : 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      finite = finite && __builtin_isfinite(v[it][i]);
+      m = fmaxf(m, fabsf(v[it][i]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    cmine[it] = m;
+    if ((tid & 7) == 0) s_c[it * (QZ_THREADS / 8) + (tid >> 3)] = m;
+  }
+  if (!finite && status != nullptr) *status = QN_ENONFINITE;
+  __syncthreads();
+
+  // group absmax
+  const float cb_t = s_c[tid];
+  float gm = cb_t;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+  if ((tid & 63) == 0) s_wmax[tid >> 6] = gm;
+  __syncthreads();
+  float smax = s_wmax[0];
+#pragma unroll
+  for (int i = 1; i < QZ_THREADS / 64; ++i) smax = fmaxf(smax, s_wmax[i]);
+  const float d = (smax == 0.0f) ? 0.0f : smax / 255.0f;
+  const int64_t b_this = g * QN_GROUP + tid;
+  if (b_this < nb_total) {
+    float qv = 0.0f;
+    if (smax != 0.0f) qv = fminf(rintf(cb_t / d), 255.0f);
+    qabs[b_this] = static_cast<uint8_t>(qv);
+  }
+  if (tid == 0) gscale[g] = d;
+
+  // NF4 codes against the un-quantized block constant
+  const int64_t nbytes = (numel + 1) / 2;
+#pragma unroll
+  for (int it = 0; it < QZ_PASSES; ++it) {
+    const int64_t e0 = gbase + it * (QZ_THREADS * 8) + tid * 8;
+    if (e0 >= numel) break;
+    const float c = cmine[it];
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float n = (c == 0.0f) ? 0.0f : v[it][i] / c;
+      uint32_t code = 0;
+#pragma unroll
+      for (int j = 0; j < 15; ++j) code += (n > cb.T[j]) ? 1u : 0u;
+      word |= code << (4 * i);
+    }
+    const int64_t byte0 = e0 >> 1;
+    if (byte0 + 4 <= nbytes) {
+      *reinterpret_cast<uint32_t*>(packed + byte0) = word;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (byte0 + i < nbytes) packed[byte0 + i] = (word >> (8 * i)) & 0xFFu;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: dequantization stream.  Each thread turns 16 packed bytes (32 weights,
+// inside one block) into 64 bytes of bf16.
+// ---------------------------------------------------------------------------
+constexpr int DQ_THREADS = 256;
+
+__global__ __launch_bounds__(DQ_THREADS) void k_dequant(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
+    const float* __restrict__ gscale, int64_t numel,
+    uint16_t* __restrict__ out, Codebook cb) {
+  const int64_t chunk = (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x;
+  const int64_t e0 = chunk * 32;
+  if (e0 >= numel) return;
+  const float cp = block_cprime(qabs, gscale, e0 >> 6);
+  if (e0 + 32 <= numel) {
+    const u32x4 p = *reinterpret_cast<const u32x4*>(packed + (e0 >> 1));
+    const Lut t = make_lut(cb, cp);
+    u32x4* o = reinterpret_cast<u32x4*>(out + e0);
+    o[0] = decode8(p.x, t);
+    o[1] = decode8(p.y, t);
+    o[2] = decode8(p.z, t);
+    o[3] = decode8(p.w, t);
+  } else {
+    for (int64_t e = e0; e < numel; ++e) {
+      const uint32_t byte = packed[e >> 1];
+      const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xFu);
+      out[e] = decode1(cb, code, cp);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA helpers.  v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of A
+// and column (l % 32) of B, each with 8 consecutive reduction elements
+// starting at 8 * (l / 32).  Accumulator register v of lane l holds
+// C[8 * (v / 4) + 4 * (l / 32) + (v % 4)][l % 32].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b,
+                                         const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+      0);
+}
+
+// v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of A and column
+// (l % 16) of B with 8 reduction elements from 8 * (l / 16); accumulator v
+// of lane l holds C[4 * (l / 16) + v][l % 16].
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b,
+                                        const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+      0);
+}
+
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi,
+                                           uint16_t& lo) {
+  const uint32_t h = pack_bf16x2(x, 0.0f) & 0xFFFFu;
+  const float rest = x - bf16_to_f32(h);
+  hi = static_cast<uint16_t>(h);
+  lo = static_cast<uint16_t>(pack_bf16x2(rest, 0.0f) & 0xFFFFu);
+}
+
+__device__ __forceinline__ void store_out(void* out, int out_bf16,
+                                          int64_t idx, float v) {
+  if (out_bf16)
+    reinterpret_cast<uint16_t*>(out)[idx] =
+        static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+  else
+    reinterpret_cast<float*>(out)[idx] = v;
+}
+
+// ---------------------------------------------------------------------------
+// K3: fused forward GEMM.  Tile 128 (M) x 128 (N) x 64 (K), 4 waves in a
+// 2 x 2 arrangement, each owning 64 x 64 of the output (2 x 2 MFMA tiles).
+// After the K loop the adapter term runs as 2r more reduction steps:
+// A-side (s T) split into bf16 hi + lo, B-side B repeated.
+// ---------------------------------------------------------------------------
+constexpr int G_BM = 128, G_BN = 128, G_BK = 64, G_PITCH = G_BK + 8;
+
+__device__ __forceinline__ void mma_tile_step(const uint16_t* sA,
+                                              const uint16_t* sB, int wm,
+                                              int wn, int lane,
+                                              f32x16 (&acc)[2][2]) {
+#pragma unroll
+  for (int kk = 0; kk < G_BK; kk += 16) {
+    u32x4 a[2], b[2];
+    const int koff = kk + (lane >> 5) * 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      a[i] = *reinterpret_cast<const u32x4*>(
+          sA + (wm * 64 + i * 32 + (lane & 31)) * G_PITCH + koff);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      b[j] = *reinterpret_cast<const u32x4*>(
+          sB + (wn * 64 + j * 32 + (lane & 31)) * G_PITCH + koff);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  }
+}
+
+__device__ __forceinline__ void store_acc_tile(void* out, int out_bf16,
+                                               int64_t ld, int rows, int cols,
+                                               int r0, int c0, int wm, int wn,
+                                               int lane,
+                                               const f32x16 (&acc)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = r0 + wm * 64 + i * 32 + 8 * (v >> 2) +
+                        4 * (lane >> 5) + (v & 3);
+        const int col = c0 + wn * 64 + j * 32 + (lane & 31);
+        if (row < rows && col < cols)
+          store_out(out, out_bf16, (int64_t)row * ld + col, acc[i][j][v]);
+      }
+}
+
+__global__ __launch_bounds__(256) void k_fwd_gemm(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
+    const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
+    const uint16_t* __restrict__ Bm, const float* __restrict__ T, int M, int N,
+    int K, int r, float s, void* __restrict__ Y, int y_bf16, Codebook cb) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[G_BM * G_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[G_BN * G_PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * G_BM, n0 = blockIdx.x * G_BN;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  for (int k0 = 0; k0 < K; k0 += G_BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx >> 3, c8 = idx & 7;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m0 + row < M)
+        v = *reinterpret_cast<const u32x4*>(X + (int64_t)(m0 + row) * K + k0 +
+                                            c8 * 8);
+      *reinterpret_cast<u32x4*>(sA + row * G_PITCH + c8 * 8) = v;
+    }
+    {
+      const int row = tid >> 1, half = tid & 1;
+      u32x4 o[4] = {};
+      if (n0 + row < N) {
+        const int64_t e = (int64_t)(n0 + row) * K + k0 + half * 32;
+        const u32x4 p = *reinterpret_cast<const u32x4*>(packed + (e >> 1));
+        const Lut t = make_lut(cb, block_cprime(qabs, gscale, e >> 6));
+        o[0] = decode8(p.x, t);
+        o[1] = decode8(p.y, t);
+        o[2] = decode8(p.z, t);
+        o[3] = decode8(p.w, t);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(sB + row * G_PITCH + half * 32 + i * 8) = o[i];
+    }
+    __syncthreads();
+    mma_tile_step(sA, sB, wm, wn, lane, acc);
+    __syncthreads();
+  }
+
+  // adapter term: reduction index jj in [0, 2r): hi part then lo part
+  const int width = 2 * r;
+  for (int j0 = 0; j0 < width; j0 += G_BK) {
+    for (int idx = tid; idx < G_BM * G_BK; idx += 256) {
+      const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
+      uint16_t va = 0, vb = 0;
+      if (jj < width) {
+        const int j = jj < r ? jj : jj - r;
+        if (m0 + row < M) {
+          uint16_t hi, lo;
+          split_bf16(s * T[(int64_t)(m0 + row) * r + j], hi, lo);
+          va = jj < r ? hi : lo;
+        }
+        if (n0 + row < N) vb = Bm[(int64_t)(n0 + row) * r + j];
+      }
+      sA[row * G_PITCH + kk] = va;
+      sB[row * G_PITCH + kk] = vb;
+    }
+    __syncthreads();
+    mma_tile_step(sA, sB, wm, wn, lane, acc);
+    __syncthreads();
+  }
+  store_acc_tile(Y, y_bf16, N, M, N, m0, n0, wm, wn, lane, acc);
+}
+
+// ---------------------------------------------------------------------------
+// K4: backward dX GEMM.  dX[M,K] = dY[M,N] W'[N,K] (+ s G A).  Tile 128 (M)
+// x 128 (K out) x 64 (N reduction).  The W' tile is dequantized along its
+// rows and written transposed into LDS so that the MFMA B operand reads 8
+// consecutive reduction (N) elements.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_dx_gemm(
+    const uint16_t* __restrict__ dY, const uint8_t* __restrict__ packed,
+    const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
+    const uint16_t* __restrict__ Am, const float* __restrict__ G, int M,
+    int N, int K, int r, float s, void* __restrict__ dX, int dx_bf16,
+    Codebook cb) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[G_BM * G_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[G_BN * G_PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * G_BM, k0 = blockIdx.x * G_BN;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  for (int n0 = 0; n0 < N; n0 += G_BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx >> 3, c8 = idx & 7;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m0 + row < M && n0 + c8 * 8 < N)
+        v = *reinterpret_cast<const u32x4*>(dY + (int64_t)(m0 + row) * N + n0 +
+                                            c8 * 8);
+      *reinterpret_cast<u32x4*>(sA + row * G_PITCH + c8 * 8) = v;
+    }
+    {
+      const int nr = tid >> 2, chunk = tid & 3;
+      const int kc = k0 + chunk * 32;
+      u32x4 o[4] = {};
+      if (n0 + nr < N && kc < K) {
+        const int64_t e = (int64_t)(n0 + nr) * K + kc;
+        const u32x4 p = *reinterpret_cast<const u32x4*>(packed + (e >> 1));
+        const Lut t = make_lut(cb, block_cprime(qabs, gscale, e >> 6));
+        o[0] = decode8(p.x, t);
+        o[1] = decode8(p.y, t);
+        o[2] = decode8(p.z, t);
+        o[3] = decode8(p.w, t);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w4[4] = {o[i].x, o[i].y, o[i].z, o[i].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int kk = chunk * 32 + i * 8 + h * 2;
+          sB[kk * G_PITCH + nr] = static_cast<uint16_t>(w4[h] & 0xFFFFu);
+          sB[(kk + 1) * G_PITCH + nr] = static_cast<uint16_t>(w4[h] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    mma_tile_step(sA, sB, wm, wn, lane, acc);
+    __syncthreads();
+  }
+
+  const int width = 2 * r;
+  for (int j0 = 0; j0 < width; j0 += G_BK) {
+    for (int idx = tid; idx < G_BM * G_BK; idx += 256) {
+      const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
+      uint16_t va = 0, vb = 0;
+      if (jj < width) {
+        const int j = jj < r ? jj : jj - r;
+        if (m0 + row < M) {
+          uint16_t hi, lo;
+          split_bf16(s * G[(int64_t)(m0 + row) * r + j], hi, lo);
+          va = jj < r ? hi : lo;
+        }
+        if (k0 + row < K) vb = Am[(int64_t)j * K + k0 + row];
+      }
+      sA[row * G_PITCH + kk] = va;
+      sB[row * G_PITCH + kk] = vb;
+    }
+    __syncthreads();
+    mma_tile_step(sA, sB, wm, wn, lane, acc);
+    __syncthreads();
+  }
+  store_acc_tile(dX, dx_bf16, K, M, K, m0, k0, wm, wn, lane, acc);
+}
+
+// ---------------------------------------------------------------------------
+// K5a: out[m][j] = sum_c P[m][c] R[j][c] (fp32), M x r output, C % 8 == 0.
+// One workgroup per 16 rows; the 4 waves take interleaved 32-wide slices of
+// C and are summed through LDS in a fixed order.
+// ---------------------------------------------------------------------------
+template <int JT>
+__global__ __launch_bounds__(256) void k_rank_nt(
+    const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ R,
+    int64_t ldr, int M, int C, int r, float* __restrict__ out) {
+  __shared__ float s_red[4][16][JT * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * 16;
+  f32x4 acc[JT];
+#pragma unroll
+  for (int t = 0; t < JT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int row = lane & 15, g = lane >> 4;
+  for (int c0 = wave * 32; c0 < C; c0 += 128) {
+    const int c = c0 + g * 8;
+    u32x4 a = {0u, 0u, 0u, 0u};
+    if (m0 + row < M && c < C)
+      a = *reinterpret_cast<const u32x4*>(P + (int64_t)(m0 + row) * ldp + c);
+#pragma unroll
+    for (int t = 0; t < JT; ++t) {
+      const int j = t * 16 + row;
+      u32x4 b = {0u, 0u, 0u, 0u};
+      if (j < r && c < C)
+        b = *reinterpret_cast<const u32x4*>(R + (int64_t)j * ldr + c);
+      acc[t] = mfma16(a, b, acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < JT; ++t) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = t * 16 + row;
+      if (j < r) s_red[wave][4 * g + v][j] = acc[t][v];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * r; idx += 256) {
+    const int mi = idx / r, j = idx % r;
+    if (m0 + mi < M)
+      out[(int64_t)(m0 + mi) * r + j] =
+          ((s_red[0][mi][j] + s_red[1][mi][j]) + s_red[2][mi][j]) +
+          s_red[3][mi][j];
+  }
+}
+
+// Bt[j][n] = B[n][j]
+__global__ __launch_bounds__(256) void k_transpose_b(
+    const uint16_t* __restrict__ B, int N, int r, uint16_t* __restrict__ Bt) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)N * r) return;
+  const int64_t n = idx / r, j = idx % r;
+  Bt[j * N + n] = B[idx];
+}
+
+// ---------------------------------------------------------------------------
+// K5b: split-M partials part[chunk][c][j] = sum_{m in chunk} P[m][c] Q[m][j]
+// with P bf16 [M, C] and Q fp32 [M, r] (Q split into bf16 hi + lo).  Tile 64
+// columns of C per workgroup (16 per wave); P and Q are staged transposed
+// into LDS so both MFMA operands read 8 consecutive rows m.
+// ---------------------------------------------------------------------------
+constexpr int TN_MCHUNK = 256;
+constexpr int TN_MSTEP = 32;
+constexpr int TN_PITCH = TN_MSTEP + 8;
+
+template <int JT>
+__global__ __launch_bounds__(256) void k_rank_tn_partial(
+    const uint16_t* __restrict__ P, int64_t ldp, const float* __restrict__ Q,
+    int M, int C, int r, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t sP[64 * TN_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sQh[JT * 16 * TN_PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t sQl[JT * 16 * TN_PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * 64;
+  const int chunk = blockIdx.y;
+  const int mbeg = chunk * TN_MCHUNK;
+  const int mend = min(M, mbeg + TN_MCHUNK);
+  const int rpad = JT * 16;
+  f32x4 acc[JT];
+#pragma unroll
+  for (int t = 0; t < JT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int col = lane & 15, g = lane >> 4;
+
+  for (int ms = mbeg; ms < mend; ms += TN_MSTEP) {
+    {
+      const int mi = tid >> 3, c8 = tid & 7;
+      const int c = c0 + c8 * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ms + mi < mend && c < C)
+        v = *reinterpret_cast<const u32x4*>(P + (int64_t)(ms + mi) * ldp + c);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        sP[(c8 * 8 + 2 * h) * TN_PITCH + mi] =
+            static_cast<uint16_t>(w4[h] & 0xFFFFu);
+        sP[(c8 * 8 + 2 * h + 1) * TN_PITCH + mi] =
+            static_cast<uint16_t>(w4[h] >> 16);
+      }
+    }
+    for (int idx = tid; idx < TN_MSTEP * rpad; idx += 256) {
+      const int mi = idx / rpad, j = idx % rpad;
+      uint16_t hi = 0, lo = 0;
+      if (ms + mi < mend && j < r) split_bf16(Q[(int64_t)(ms + mi) * r + j], hi, lo);
+      sQh[j * TN_PITCH + mi] = hi;
+      sQl[j * TN_PITCH + mi] = lo;
+    }
+    __syncthreads();
+    const u32x4 a = *reinterpret_cast<const u32x4*>(
+        sP + (wave * 16 + col) * TN_PITCH + g * 8);
+#pragma unroll
+    for (int t = 0; t < JT; ++t) {
+      const u32x4 bh = *reinterpret_cast<const u32x4*>(
+          sQh + (t * 16 + col) * TN_PITCH + g * 8);
+      const u32x4 bl = *reinterpret_cast<const u32x4*>(
+          sQl + (t * 16 + col) * TN_PITCH + g * 8);
+      acc[t] = mfma16(a, bh, acc[t]);
+      acc[t] = mfma16(a, bl, acc[t]);
+    }
+    __syncthreads();
+  }
+  // acc[t][v] = C-tile[c = wave*16 + 4g + v][j = t*16 + col]
+#pragma unroll
+  for (int t = 0; t < JT; ++t) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c = c0 + wave * 16 + 4 * g + v;
+      const int j = t * 16 + col;
+      if (c < C && j < r)
+        part[((int64_t)chunk * C + c) * r + j] = acc[t][v];
+    }
+  }
+}
+
+// out[c * sc + j * sj] = s * sum_chunk part[chunk][c][j], chunks in order.
+__global__ __launch_bounds__(256) void k_rank_tn_reduce(
+    const float* __restrict__ part, int chunks, int C, int r, float s,
+    float* __restrict__ out, int64_t sc, int64_t sj) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)C * r;
+  if (idx >= total) return;
+  float acc = 0.0f;
+  for (int ch = 0; ch < chunks; ++ch) acc += part[(int64_t)ch * total + idx];
+  const int64_t c = idx / r, j = idx % r;
+  out[c * sc + j * sj] = s * acc;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+const Codebook& codebook() {
+  static const Codebook cb = [] {
+    Codebook c;
+    qn::derive_codebook(c.L, c.T);
+    return c;
+  }();
+  return cb;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int check_launch() {
+  return hipGetLastError() == hipSuccess ? QN_OK : QN_EHIP;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool valid_tensor(const nf4_tensor* w) {
+  return w != nullptr && w->packed != nullptr && w->qabs != nullptr &&
+         w->gscale != nullptr && w->rows > 0 && w->cols > 0 &&
+         aligned16(w->packed);
+}
+
+bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
+  if (!valid_tensor(w) || M <= 0) return false;
+  if (r < 1 || r > QN_MAX_RANK) return false;
+  const int64_t N = w->rows, K = w->cols;
+  if (K % QN_BLOCK != 0 || N % 8 != 0) return false;
+  // 32-bit index arithmetic inside the GEMM kernels
+  if (M > (1LL << 30) || N > (1LL << 30) || K > (1LL << 30)) return false;
+  return true;
+}
+
+// Per-launch event recording for one named kernel (qn_profile_kernel).
+struct ProfileHook {
+  char name[64] = {0};
+  void** ev_start = nullptr;
+  void** ev_stop = nullptr;
+  int32_t capacity = 0;
+  int32_t count = 0;
+} g_prof;
+
+struct ProfScope {
+  hipStream_t st;
+  int slot = -1;
+  ProfScope(const char* kname, hipStream_t s) : st(s) {
+    if (g_prof.capacity > 0 && g_prof.count < g_prof.capacity &&
+        std::strcmp(g_prof.name, kname) == 0) {
+      slot = g_prof.count++;
+      (void)hipEventRecord((hipEvent_t)g_prof.ev_start[slot], st);
+    }
+  }
+  ~ProfScope() {
+    if (slot >= 0) (void)hipEventRecord((hipEvent_t)g_prof.ev_stop[slot], st);
+  }
+};
+
+#define QN_LAUNCH(kname, kernel, grid, block, st, ...)                \
+  do {                                                                \
+    ProfScope qn_prof_scope_(kname, st);                              \
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, __VA_ARGS__);      \
+  } while (0)
+
+// Rank-tile dispatch: JT = number of 16-wide tiles of r, rounded up to a
+// power of two (1, 2, 4, 8, 16 covers r <= 256).
+int rank_tiles(int r) {
+  int jt = 1;
+  while (jt * 16 < r) jt *= 2;
+  return jt;
+}
+
+template <int JT>
+void launch_rank_nt_t(dim3 grid, hipStream_t st, const uint16_t* P,
+                      int64_t ldp, const uint16_t* R, int64_t ldr, int M,
+                      int C, int r, float* out) {
+  QN_LAUNCH("k_rank_nt", k_rank_nt<JT>, grid, dim3(256), st, P, ldp, R, ldr,
+            M, C, r, out);
+}
+
+void launch_rank_nt(hipStream_t st, const uint16_t* P, int64_t ldp,
+                    const uint16_t* R, int64_t ldr, int M, int C, int r,
+                    float* out) {
+  const dim3 grid((unsigned)cdiv(M, 16));
+  switch (rank_tiles(r)) {
+    case 1: launch_rank_nt_t<1>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
+    case 2: launch_rank_nt_t<2>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
+    case 4: launch_rank_nt_t<4>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
+    case 8: launch_rank_nt_t<8>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
+    default: launch_rank_nt_t<16>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
+  }
+}
+
+template <int JT>
+void launch_rank_tn_t(dim3 grid, hipStream_t st, const uint16_t* P,
+                      int64_t ldp, const float* Q, int M, int C, int r,
+                      float* part) {
+  QN_LAUNCH("k_rank_tn_partial", k_rank_tn_partial<JT>, grid, dim3(256), st,
+            P, ldp, Q, M, C, r, part);
+}
+
+void launch_rank_tn(hipStream_t st, const uint16_t* P, int64_t ldp,
+                    const float* Q, int M, int C, int r, int chunks,
+                    float* part) {
+  const dim3 grid((unsigned)cdiv(C, 64), (unsigned)chunks);
+  switch (rank_tiles(r)) {
+    case 1: launch_rank_tn_t<1>(grid, st, P, ldp, Q, M, C, r, part); break;
+    case 2: launch_rank_tn_t<2>(grid, st, P, ldp, Q, M, C, r, part); break;
+    case 4: launch_rank_tn_t<4>(grid, st, P, ldp, Q, M, C, r, part); break;
+    case 8: launch_rank_tn_t<8>(grid, st, P, ldp, Q, M, C, r, part); break;
+    default: launch_rank_tn_t<16>(grid, st, P, ldp, Q, M, C, r, part); break;
+  }
+}
+
+}  // namespace
+
+namespace qn {
+
+BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K,
+                                  int32_t r) {
+  BwdWorkspace L{};
+  L.chunks = cdiv(M, TN_MCHUNK);
+  size_t off = 0;
+  L.bt = off;
+  off += align256(size_t(r) * N * 2);
+  L.g = off;
+  off += align256(size_t(M) * r * 4);
+  L.part_db = off;
+  off += align256(size_t(L.chunks) * N * r * 4);
+  L.part_da = off;
+  off += align256(size_t(L.chunks) * K * r * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace qn
+
+extern "C" {
+
+int qn_profile_kernel(const char* name, void** ev_start, void** ev_stop,
+                      int32_t capacity) {
+  const int32_t recorded = g_prof.count;
+  if (name == nullptr) {
+    g_prof = ProfileHook();
+    return recorded;
+  }
+  if (ev_start == nullptr || ev_stop == nullptr || capacity < 0 ||
+      std::strlen(name) >= sizeof(g_prof.name))
+    return QN_EINVAL;
+  g_prof = ProfileHook();
+  std::strcpy(g_prof.name, name);
+  g_prof.ev_start = ev_start;
+  g_prof.ev_stop = ev_stop;
+  g_prof.capacity = capacity;
+  return recorded;
+}
+
+const char* qn_strerror(int code) {
+  switch (code) {
+    case QN_OK: return "success";
+    case QN_EINVAL: return "invalid argument";
+    case QN_EWORKSPACE: return "workspace too small";
+    case QN_EHIP: return "HIP launch error";
+    case QN_ENONFINITE: return "non-finite weight";
+    default: return "unknown error";
+  }
+}
+
+int nf4_quantize(const float* w, const nf4_tensor* out, int32_t* status_dev,
+                 void* stream) {
+  if (w == nullptr || !valid_tensor(out) || !aligned16(w)) return QN_EINVAL;
+  const int64_t numel = out->rows * out->cols;
+  const int64_t nb = cdiv(numel, QN_BLOCK);
+  const int64_t ng = cdiv(nb, QN_GROUP);
+  if (ng > 0x7FFFFFFFLL) return QN_EINVAL;
+  QN_LAUNCH("k_quantize", k_quantize, dim3((unsigned)ng), dim3(QZ_THREADS),
+            (hipStream_t)stream, w, numel, out->packed, out->qabs,
+            out->gscale, status_dev, codebook());
+  return check_launch();
+}
+
+int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream) {
+  if (!valid_tensor(w) || w_bf16 == nullptr || !aligned16(w_bf16))
+    return QN_EINVAL;
+  const int64_t numel = w->rows * w->cols;
+  const int64_t chunks = cdiv(numel, 32);
+  const int64_t grid = cdiv(chunks, DQ_THREADS);
+  if (grid > 0x7FFFFFFFLL) return QN_EINVAL;
+  QN_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(DQ_THREADS),
+            (hipStream_t)stream, w->packed, w->qabs, w->gscale, numel, w_bf16,
+            codebook());
+  return check_launch();
+}
+
+size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
+                             int32_t which) {
+  if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QN_MAX_RANK) return 0;
+  if (which == QN_FWD) return 0;
+  if (which == QN_BWD) return qn::bwd_workspace_layout(M, N, K, r).total;
+  return 0;
+}
+
+int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
+                     const uint16_t* A, const uint16_t* B, int32_t r,
+                     float alpha, void* y, int32_t y_dtype, float* t_save,
+                     void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (x == nullptr || A == nullptr || B == nullptr || y == nullptr ||
+      t_save == nullptr)
+    return QN_EINVAL;
+  if (!valid_linear(M, w, r)) return QN_EINVAL;
+  if (y_dtype != QN_F32 && y_dtype != QN_BF16) return QN_EINVAL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(y) || !aligned16(t_save))
+    return QN_EINVAL;
+  const int N = (int)w->rows, K = (int)w->cols, Mi = (int)M;
+  const float s = alpha / (float)r;
+  hipStream_t st = (hipStream_t)stream;
+  launch_rank_nt(st, x, K, A, K, Mi, K, (int)r, t_save);
+  QN_LAUNCH("k_fwd_gemm", k_fwd_gemm,
+            dim3((unsigned)cdiv(N, G_BN), (unsigned)cdiv(M, G_BM)), dim3(256),
+            st, x, w->packed, w->qabs, w->gscale, B, t_save, Mi, N, K, (int)r,
+            s, y, (int)(y_dtype == QN_BF16), codebook());
+  return check_launch();
+}
+
+int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
+                     const nf4_tensor* w, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha,
+                     const float* t_saved, void* dx, int32_t dx_dtype,
+                     float* dA, float* dB, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (dy == nullptr || x == nullptr || A == nullptr || B == nullptr ||
+      t_saved == nullptr || dx == nullptr || dA == nullptr || dB == nullptr)
+    return QN_EINVAL;
+  if (!valid_linear(M, w, r)) return QN_EINVAL;
+  if (dx_dtype != QN_F32 && dx_dtype != QN_BF16) return QN_EINVAL;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(A) || !aligned16(dx))
+    return QN_EINVAL;
+  const int64_t N = w->rows, K = w->cols;
+  const qn::BwdWorkspace L = qn::bwd_workspace_layout(M, N, K, r);
+  if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
+    return QN_EWORKSPACE;
+  char* base = static_cast<char*>(ws);
+  uint16_t* Bt = reinterpret_cast<uint16_t*>(base + L.bt);
+  float* G = reinterpret_cast<float*>(base + L.g);
+  float* part_db = reinterpret_cast<float*>(base + L.part_db);
+  float* part_da = reinterpret_cast<float*>(base + L.part_da);
+  const float s = alpha / (float)r;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+  hipStream_t st = (hipStream_t)stream;
+
+  QN_LAUNCH("k_transpose_b", k_transpose_b, dim3((unsigned)cdiv(N * r, 256)),
+            dim3(256), st, B, Ni, (int)r, Bt);
+  // G = dY B
+  launch_rank_nt(st, dy, N, Bt, N, Mi, Ni, (int)r, G);
+  // dB = s dY^T T
+  launch_rank_tn(st, dy, N, t_saved, Mi, Ni, (int)r, (int)L.chunks, part_db);
+  QN_LAUNCH("k_rank_tn_reduce", k_rank_tn_reduce,
+            dim3((unsigned)cdiv(N * r, 256)), dim3(256), st, part_db,
+            (int)L.chunks, Ni, (int)r, s, dB, (int64_t)r, (int64_t)1);
+  // dX = dY W' + s G A
+  QN_LAUNCH("k_bwd_dx_gemm", k_bwd_dx_gemm,
+            dim3((unsigned)cdiv(K, G_BN), (unsigned)cdiv(M, G_BM)), dim3(256),
+            st, dy, w->packed, w->qabs, w->gscale, A, G, Mi, Ni, Ki, (int)r, s,
+            dx, (int)(dx_dtype == QN_BF16), codebook());
+  // dA = s G^T X  (out[k][j] -> dA[j][k])
+  launch_rank_tn(st, x, K, G, Mi, Ki, (int)r, (int)L.chunks, part_da);
+  QN_LAUNCH("k_rank_tn_reduce", k_rank_tn_reduce,
+            dim3((unsigned)cdiv(K * r, 256)), dim3(256), st, part_da,
+            (int)L.chunks, Ki, (int)r, s, dA, (int64_t)1, K);
+  return check_launch();
+}
+
+}  // extern "C"

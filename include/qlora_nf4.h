@@ -1,0 +1,215 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA linear-layer library.
+ *
+ * The library computes the hot path of QLoRA fine-tuning on one GPU:
+ *   1. blockwise NF4 quantization of a frozen fp32 weight (64-weight blocks,
+ *      absmax scale, 16 levels at N(0,1) quantiles),
+ *   2. double quantization of the per-block constants to 8-bit codes in
+ *      groups of 256 with one fp32 scale per group,
+ *   3. dequantization to bf16,
+ *   4. the fused forward Y = X W'^T + (alpha/r) (X A^T) B^T and its backward
+ *      (dX through the dequantized frozen base W', dA and dB for the bf16
+ *      adapters; the base gets no gradient).
+ *
+ * Sources for what each call computes are the pages "Qlora Expert" (Core
+ * Concept), "QLoRA: The 4-bit Revolution" (sections 1 and 2), "QLoRA Guide"
+ * (How QLoRA Works: Forward pass; NF4 vs uniform INT4), "QLoRA Implementation
+ * Details (2025 Edition)" (Step 1 NF4 Math; Step 4 LoRA adapters) and
+ * "QLORA: Efficient Finetuning of Quantized LLMs" (paper summary: Methods,
+ * Notes).  The fixed configuration follows the pages' BitsAndBytesConfig:
+ * quant type NF4, double quantization on, bf16 compute; and their LoraConfig:
+ * rank r, lora_alpha, bias "none", no dropout.
+ *
+ * Conventions for every call
+ *   - Shapes follow the Linear convention: W is [N, K] (out, in), X [M, K],
+ *     Y [M, N], A [r, K], B [N, r].  All matrices are dense row-major.
+ *   - bf16 tensors are passed as raw uint16_t bit patterns.
+ *   - Pointers marked "device" are device (HBM) addresses; the caller owns
+ *     every buffer, including workspaces.  The library never allocates,
+ *     frees, or keeps a pointer after a call returns, and holds no global
+ *     device state, so calls are reentrant.
+ *   - All device work is enqueued asynchronously on `stream` (a hipStream_t
+ *     passed as void*; NULL is the default stream).  Outputs are valid once
+ *     the stream reaches them; inputs must stay unchanged until then.
+ *   - Return value: 0 on success or a negative QN_E* code.  Argument errors
+ *     are detected on the host before anything is launched.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QN_OK 0
+#define QN_EINVAL (-1)      /* null pointer, bad size, r out of range,
+                               K % 64 != 0 in a fused call, unknown dtype,
+                               misaligned pointer */
+#define QN_EWORKSPACE (-2)  /* workspace smaller than qlora_workspace_bytes */
+#define QN_EHIP (-3)        /* the HIP runtime reported a launch error */
+#define QN_ENONFINITE (-4)  /* written to *status_dev by nf4_quantize */
+
+#define QN_F32 0            /* output element type: fp32 */
+#define QN_BF16 1           /* output element type: bf16 (RNE) */
+
+#define QN_FWD 0
+#define QN_BWD 1
+
+#define QN_BLOCK 64         /* weights per absmax block */
+#define QN_GROUP 256        /* block constants per double-quant group */
+#define QN_MAX_RANK 256
+
+/*
+ * An NF4 + double-quantized weight of rows x cols elements (numel =
+ * rows*cols), flattened row-major:
+ *   packed : device, ceil(numel/2) bytes.  Element 2i sits in bits 0-3 of
+ *            byte i, element 2i+1 in bits 4-7; an odd tail nibble is 7.
+ *   qabs   : device, nb = ceil(numel/64) bytes, the 8-bit code of each
+ *            block's absmax.
+ *   gscale : device, ng = ceil(nb/256) floats, the fp32 scale d of each
+ *            group of 256 block codes.
+ * The dequantized value of element e in block b = e/64, group g = b/256 is
+ *   bf16_rne( L[code_e] * (float(qabs[b]) * gscale[g]) )
+ * with both products in fp32 and L the 16 levels of nf4_codebook().
+ * packed must be 16-byte aligned.
+ */
+typedef struct {
+  uint8_t* packed;
+  uint8_t* qabs;
+  float* gscale;
+  int64_t rows;
+  int64_t cols;
+} nf4_tensor;
+
+/*
+ * nf4_codebook -- the 16 NF4 levels and the 15 decision thresholds (host).
+ *
+ * "Qlora Expert", Core Concept: the 16 levels sit at quantiles of N(0,1).
+ * Construction: 8 positive levels at the normal quantiles of the
+ * probabilities delta - i*(delta-1/2)/8 (i = 0..7), 7 negative levels at the
+ * negated quantiles of delta - i*(delta-1/2)/7 (i = 0..6), and 0, divided by
+ * the largest, with delta = 1 - (1/32 + 1/30)/2; computed in double, rounded
+ * once to float.  thresholds[j] = float((double(L[j]) + double(L[j+1])) / 2).
+ * levels: 16 floats, ascending (L[0] = -1, L[7] = 0, L[15] = 1).
+ * Either pointer may be NULL.  Returns 0.
+ */
+int nf4_codebook(float levels[16], float thresholds[15]);
+
+/*
+ * nf4_quantize -- NF4 block quantization + double quantization (device).
+ *
+ * "Qlora Expert", Core Concept (NF4; DQ of the per-block fp32 constants to
+ * 8 bit); "QLoRA Implementation Details", NF4 Math (blocks of 64 values);
+ * "QLoRA: The 4-bit Revolution", section 2 (scaling factors 32 -> 8 bit).
+ * For each block of 64 consecutive elements of the flattened weight
+ * (the last block may be shorter):
+ *   c = max |w|;  n = w / c (IEEE fp32 division; n = 0 if c = 0);
+ *   code = number of thresholds t_j with n > t_j (nearest level, ties low).
+ * For each group of 256 consecutive blocks (the last may be shorter):
+ *   s = max c;  d = s / 255 (fp32; d = 0 if s = 0);
+ *   qabs = min(255, rint_half_even(c / d)) (0 if s = 0).
+ * w       : device, rows*cols floats, 16-byte aligned.
+ * out     : host struct; its device buffers receive packed, qabs, gscale
+ *           (rows and cols give the element count).
+ * status_dev : device int32 or NULL.  If any weight is non-finite the
+ *           kernel stores QN_ENONFINITE there and the outputs are undefined;
+ *           otherwise it is left untouched (clear it before the call).
+ * Errors: QN_EINVAL (null pointer, rows or cols <= 0, misalignment),
+ *         QN_EHIP.
+ */
+int nf4_quantize(const float* w, const nf4_tensor* out, int32_t* status_dev,
+                 void* stream);
+
+/*
+ * nf4_dequantize -- NF4 + DQ weight to bf16 (device).
+ *
+ * "QLORA ... paper summary", Notes: load the 4-bit weights and dequantize
+ * to BF16; "QLoRA Guide", Forward pass: dequantize to BF16 on the fly.
+ * w_bf16 : device, rows*cols uint16 (bf16 bits), 16-byte aligned, the
+ *          row-major dequantized weight (formula at nf4_tensor).
+ * Errors: QN_EINVAL, QN_EHIP.
+ */
+int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream);
+
+/*
+ * qlora_workspace_bytes -- device workspace a fused call needs (host).
+ * which: QN_FWD or QN_BWD.  Returns 0 for invalid arguments.
+ */
+size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
+                             int32_t which);
+
+/*
+ * qlora_linear_fwd -- fused QLoRA linear forward (device).
+ *
+ * "QLoRA Guide", How QLoRA Works / Forward pass: the dequantized frozen W
+ * times x is summed with the adapter branch B(A(x)); "QLoRA Implementation
+ * Details", Step 4: the branch is scaled by alpha/r.  With s = alpha / r:
+ *   T = X A^T            (fp32, written to t_save)
+ *   Y = X W'^T + s T B^T (fp32 accumulation)
+ * W' is dequantized inside the kernel and never written to memory.
+ * x      : device bf16 [M, K];  w: NF4 tensor with rows = N, cols = K;
+ * A      : device bf16 [r, K];  B: device bf16 [N, r];  1 <= r <= 256;
+ * y      : device [M, N] of y_dtype (QN_F32 or QN_BF16);
+ * t_save : device fp32 [M, r], T for the backward;
+ * ws     : device workspace of ws_bytes >= qlora_workspace_bytes(M, N, K,
+ *          r, QN_FWD) (may be NULL if that is 0).
+ * Requires K % 64 == 0 (blocks never straddle rows), M, N >= 1, and all
+ * matrix pointers 16-byte aligned.
+ * Errors: QN_EINVAL, QN_EWORKSPACE, QN_EHIP.
+ */
+int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
+                     const uint16_t* A, const uint16_t* B, int32_t r,
+                     float alpha, void* y, int32_t y_dtype, float* t_save,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd -- fused QLoRA linear backward (device).
+ *
+ * "QLoRA Guide", Forward pass: only A and B receive gradients, the
+ * dequantized W is treated as a constant; "QLORA ... paper summary", Notes:
+ * gradients only for the LoRA adapters.  With s = alpha / r and G = dY B:
+ *   dX = dY W' + s G A   (output dtype dx_dtype)
+ *   dA = s G^T X         (fp32 [r, K])
+ *   dB = s dY^T T        (fp32 [N, r])
+ * No gradient is formed for the frozen base.
+ * dy     : device bf16 [M, N];  x: device bf16 [M, K];
+ * t_saved: device fp32 [M, r] from qlora_linear_fwd;
+ * dx     : device [M, K] of dx_dtype;  dA, dB: device fp32 outputs;
+ * ws     : device workspace, ws_bytes >= qlora_workspace_bytes(M, N, K, r,
+ *          QN_BWD).
+ * Same shape and alignment rules as qlora_linear_fwd.
+ * Errors: QN_EINVAL, QN_EWORKSPACE, QN_EHIP.
+ */
+int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
+                     const nf4_tensor* w, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha,
+                     const float* t_saved, void* dx, int32_t dx_dtype,
+                     float* dA, float* dB, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* qn_strerror -- static text for a QN_* code (host). */
+const char* qn_strerror(int code);
+
+/*
+ * qn_profile_kernel -- measurement hook (host), for benchmarks.
+ *
+ * Arms per-launch timing of one internal kernel: each later launch of the
+ * kernel called `name` (e.g. "k_fwd_gemm", "k_bwd_dx_gemm", "k_dequant")
+ * records ev_start[i] on its stream right before the launch and ev_stop[i]
+ * right after, for i = 0, 1, ... up to `capacity` launches.  ev_start and
+ * ev_stop are host arrays of hipEvent_t (as void*) created by the caller and
+ * must stay valid while armed.  name == NULL disarms.  Returns the number of
+ * launches recorded since the last arming (>= 0), or QN_EINVAL.  Process
+ * global and not thread-safe.
+ */
+int qn_profile_kernel(const char* name, void** ev_start, void** ev_stop,
+                      int32_t capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

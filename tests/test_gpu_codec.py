@@ -1,0 +1,119 @@
+"""GPU parity of the NF4 + double-quant codec against the CPU oracle.
+
+Bit-exact: packed codes, 8-bit block codes, fp32 group scales (compared as
+bits) and the dequantized bf16 weights, on the seeded workloads (tiny, the
+seven 7B-layer projections with Student-t outliers) and on ragged and
+degenerate inputs.  Calls go through the C ABI (capi -> libqlora_nf4.so).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_nf4_quantized_14_amd import capi
+from bit_nf4_quantized_14_amd import workloads as wl
+
+from gpu_util import DEV, bits_host, f32_dev, nf4_host, quantize_dev
+
+pytestmark = pytest.mark.gpu
+
+GROUP_ELEMS = 64 * 256
+
+
+def _check_full(w: np.ndarray):
+    """Quantize + dequantize on the GPU and compare everything bit-exact."""
+    numel = w.size
+    print(f"[codec] numel={numel} shape={w.shape}", flush=True)
+    t, status = quantize_dev(w)
+    deq = capi.nf4_dequantize(t)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    packed, q, d = nf4_host(t)
+    rp, rq, rd = oracle.nf4_quantize(w)
+    assert np.array_equal(packed, rp)
+    assert np.array_equal(q, rq)
+    assert np.array_equal(d.view(np.uint32), rd.view(np.uint32))
+    ref = oracle.nf4_dequantize(rp, rq, rd, numel)
+    assert np.array_equal(bits_host(deq).reshape(-1), ref)
+
+
+def test_codec_tiny_workload():
+    _check_full(wl.weight(wl.workload("tiny"), 0))
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 63), (1, 64), (1, 65), (3, 21),
+                                   (1, GROUP_ELEMS + 17), (5, 7000),
+                                   (1, 3 * GROUP_ELEMS + 64 * 5 + 33),
+                                   (37, 192), (257, 128)])
+def test_codec_ragged_sizes(shape):
+    rng = np.random.default_rng(sum(shape))
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    _check_full(w)
+
+
+def test_codec_degenerate_blocks():
+    lv = oracle.nf4_levels()
+    th = oracle.nf4_thresholds()
+    parts = [
+        np.zeros(64, np.float32),                               # zero block
+        np.where(np.arange(64) == 9, -0.3, 0.0).astype(np.float32),  # one value
+        (lv.astype(np.float64) * 2.0 ** -6).repeat(4).astype(np.float32),  # exact levels
+        np.concatenate([[1.0], th, -np.ones(48)]).astype(np.float32),  # ties
+        np.full(64, 7.5, np.float32),                           # constant block
+        np.full(64, -1e-30, np.float32),                        # tiny
+        (np.arange(64, dtype=np.float32) - 31.5) * np.float32(1e3),  # large
+    ]
+    w = np.concatenate(parts + [np.zeros(64 * 249, np.float32)])  # one group
+    w = np.concatenate([w, np.zeros(GROUP_ELEMS, np.float32)])   # + zero group
+    _check_full(w.reshape(2, -1))
+
+
+def test_quantize_flags_nonfinite_weights():
+    for bad in (np.inf, -np.inf, np.nan):
+        w = np.zeros((4, 64), np.float32)
+        w[2, 5] = bad
+        _, status = quantize_dev(w)
+        torch.cuda.synchronize()
+        assert int(status.item()) == capi.QN_ENONFINITE
+
+
+def test_codec_deterministic():
+    w = wl.weight(wl.workload("tiny"), 0)
+    a, _ = quantize_dev(w)
+    b, _ = quantize_dev(w)
+    torch.cuda.synchronize()
+    for x, y in zip(nf4_host(a), nf4_host(b)):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def _sampled_groups(ng: int, rng):
+    pick = {0, ng - 1}
+    pick.update(int(g) for g in rng.choice(ng, size=min(ng, 14), replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("proj", range(7))
+def test_codec_7b_layer_projection_sampled(proj):
+    """Full-size 7B-layer projections (with outliers); the oracle checks
+    randomly sampled double-quant groups (each group is independent)."""
+    wk = wl.workload("dequant7b")
+    name, n, k = wk.projections[proj]
+    w = wl.weight(wk, proj)
+    print(f"[codec7b] proj={name} {n}x{k}", flush=True)
+    t, status = quantize_dev(w)
+    deq = capi.nf4_dequantize(t)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    packed, q, d = nf4_host(t)
+    deq_bits = bits_host(deq).reshape(-1)
+    flat = w.reshape(-1)
+    ng = d.size
+    for g in _sampled_groups(ng, np.random.default_rng(proj)):
+        seg = flat[g * GROUP_ELEMS:(g + 1) * GROUP_ELEMS]
+        rp, rq, rd = oracle.nf4_quantize(seg)
+        assert np.array_equal(packed[g * GROUP_ELEMS // 2:(g + 1) * GROUP_ELEMS // 2], rp)
+        assert np.array_equal(q[g * 256:(g + 1) * 256], rq)
+        assert d[g].view(np.uint32) == rd[0].view(np.uint32)
+        ref = oracle.nf4_dequantize(rp, rq, rd, seg.size)
+        assert np.array_equal(deq_bits[g * GROUP_ELEMS:(g + 1) * GROUP_ELEMS], ref)
