@@ -303,217 +303,353 @@ __device__ __forceinline__ void store_out(void* out, int out_bf16,
 }
 
 // ---------------------------------------------------------------------------
-// K3: fused forward GEMM.  Tile 128 (M) x 128 (N) x 64 (K), 4 waves in a
-// 2 x 2 arrangement, each owning 64 x 64 of the output (2 x 2 MFMA tiles).
-// After the K loop the adapter term runs as 2r more reduction steps:
-// A-side (s T) split into bf16 hi + lo, B-side B repeated.
+// K3/K4: fused dequant + MFMA GEMM, one template for both directions.
+//
+//   forward  (BWD = false): Y[M,N]  = X[M,K]  W'^T  + (s T) B^T
+//   backward (BWD = true) : dX[M,K] = dY[M,N] W'    + (s G) A
+//
+// Output tile BM x BN, reduction step 64, 256 threads = 4 waves in a 2 x 2
+// arrangement, each wave owning (BM/2) x (BN/2) of the output as
+// (BM/64) x (BN/64) tiles of v_mfma_f32_32x32x16_bf16 with fp32
+// accumulators.
+//
+// Per reduction step:
+//  * the A tile (X or dY rows, bf16) goes global -> LDS directly
+//    (buffer_load ... lds, 1 KB per wave instruction), 128-byte rows with
+//    the 16-byte chunk index XOR-swizzled by (row & 7) so the MFMA operand
+//    reads hit distinct banks;
+//  * the weight tile arrives as packed nibbles + 8-bit block codes + group
+//    scales in registers and each thread dequantizes BN/4 weights of one
+//    64-weight block (per-block v_perm LUT) into LDS in the weight's natural
+//    row-major layout.  The forward reads W' rows as MFMA B operands with
+//    ds_read_b128; the backward reads W' columns with ds_read_b64_tr_b16.
+// LDS is double-buffered.  While the MFMAs consume step i, the A tile of
+// step i+1 streams into the other buffer and the weight tile of step i+1
+// (loaded one step earlier) is dequantized into it; the dequantization is
+// interleaved with the MFMAs by sched_group_barrier.  Global loads go
+// through buffer resources whose range check returns zeros, which covers
+// ragged M, N and K tiles without branches.
+// The adapter term is 2r extra reduction steps with the A side s*T (or s*G)
+// split into bf16 hi + lo parts, so the fp32 intermediate keeps ~16
+// mantissa bits.
 // ---------------------------------------------------------------------------
-constexpr int G_BM = 128, G_BN = 128, G_BK = 64, G_PITCH = G_BK + 8;
+constexpr int G_BK = 64;
+constexpr uint32_t G_OOB = 0x80000000u;   // buffer offset past every range
+constexpr int G_RSRC_FLAGS = 0x00020000;
 
-__device__ __forceinline__ void mma_tile_step(const uint16_t* sA,
-                                              const uint16_t* sB, int wm,
-                                              int wn, int lane,
-                                              f32x16 (&acc)[2][2]) {
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, G_RSRC_FLAGS);
+}
+
+template <int BM, int BN, bool BWD>
+struct GemmCfg {
+  static constexpr int WM = BM / 2, WN = BN / 2;        // per-wave tile
+  static constexpr int TM = WM / 32, TN = WN / 32;      // MFMA tiles per wave
+  static constexpr int A_BYTES = BM * 128;              // swizzled, unpadded
+  static constexpr int A_LOADS = BM / 32;               // 1 KB loads per wave
+  static constexpr int EPT = BN / 4;                    // weights per thread
+  static constexpr int WDW = EPT / 8;                   // packed dwords
+  static constexpr int TPR = 64 / EPT;                  // forward threads/row
+  // W tile in LDS: forward [BN rows n][64 k], backward [64 rows n][BN k]
+  static constexpr int PW = BWD ? BN + 16 : G_BK + 8;
+  static constexpr int W_ROWS = BWD ? G_BK : BN;
+  static constexpr int W_BYTES = W_ROWS * PW * 2;
+  static constexpr int LDS_BYTES = 2 * A_BYTES + 2 * W_BYTES;
+  static constexpr int MFMAS = 4 * TM * TN;             // per step per wave
+  static constexpr int DS_READS = 4 * (TM + (BWD ? 2 : 1) * TN);
+};
+
+// Packed weight bytes of one step for one thread, plus its block code and
+// group scale (raw; c' = q * d is formed when the tile is dequantized).
+struct WRegs {
+  u32x4 w0, w1;
+  uint32_t q;
+  float d;
+};
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_load_w(WRegs& R, rsrc_t rp, rsrc_t rq,
+                                            rsrc_t rd, int N, int K, int c0,
+                                            int red0, int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+  int n, k;
+  if (!BWD) {
+    n = c0 + tid / C::TPR;           // output column = weight row
+    k = red0 + (tid % C::TPR) * C::EPT;
+  } else {
+    n = red0 + (tid >> 2);           // reduction index = weight row
+    k = c0 + (tid & 3) * C::EPT;
+  }
+  const bool ok = n < N && k < K;
+  const int64_t e = (int64_t)n * K + k;
+  const uint32_t op = ok ? (uint32_t)(e >> 1) : G_OOB;
+  const uint32_t ob = ok ? (uint32_t)(e >> 6) : G_OOB;
+  const uint32_t og = ok ? (uint32_t)((e >> 14) << 2) : G_OOB;
+  R.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op, 0, 0));
+  if (C::WDW == 8)
+    R.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op + 16, 0, 0));
+  else
+    R.w1 = u32x4{0u, 0u, 0u, 0u};
+  R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, ob, 0, 0);
+  R.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, og, 0, 0));
+}
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_dequant_w(const WRegs& R, uint16_t* sW,
+                                               const Codebook& cb, int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+  uint16_t* dst = BWD ? sW + (tid >> 2) * C::PW + (tid & 3) * C::EPT
+                      : sW + (tid / C::TPR) * C::PW + (tid % C::TPR) * C::EPT;
+  const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
+  const uint32_t wd[8] = {R.w0.x, R.w0.y, R.w0.z, R.w0.w,
+                          R.w1.x, R.w1.y, R.w1.z, R.w1.w};
 #pragma unroll
-  for (int kk = 0; kk < G_BK; kk += 16) {
-    u32x4 a[2], b[2];
-    const int koff = kk + (lane >> 5) * 8;
+  for (int d = 0; d < C::WDW; ++d)
+    *reinterpret_cast<u32x4*>(dst + 8 * d) = decode8(wd[d], t);
+}
+
+// A tile of one step straight into LDS: wave w issues 1 KB chunks
+// q = w, w+4, ...; chunk q holds rows 8q..8q+7, and lane l of the
+// instruction fills row 8q + l/8, slot l%8, with global 16-byte chunk
+// (l%8) ^ (row & 7).
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_load_a(rsrc_t ra, char* sA, int M,
+                                            int KRED, int m0, int red0,
+                                            int wave, int lane) {
+  using C = GemmCfg<BM, BN, BWD>;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const u32x4*>(
-          sA + (wm * 64 + i * 32 + (lane & 31)) * G_PITCH + koff);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const u32x4*>(
-          sB + (wn * 64 + j * 32 + (lane & 31)) * G_PITCH + koff);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int q = wave + 4 * i;
+    const int row = 8 * q + (lane >> 3);
+    const int col = red0 + 8 * ((lane & 7) ^ (row & 7));
+    const bool ok = m0 + row < M && col < KRED;
+    const uint32_t off =
+        ok ? (uint32_t)(((int64_t)(m0 + row) * KRED + col) * 2) : G_OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + q * 1024),
+                                             16, off, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_acc_tile(void* out, int out_bf16,
-                                               int64_t ld, int rows, int cols,
-                                               int r0, int c0, int wm, int wn,
-                                               int lane,
-                                               const f32x16 (&acc)[2][2]) {
+// Transposed B operand for the backward: lane l needs 8 consecutive
+// reduction rows (8 * (l / 32) ...) of output column (col0 + l % 32).  Each
+// ds_read_b64_tr_b16 serves 4 rows: in every group of 16 lanes, lane
+// q = 4j + p addresses row j, columns 4p..4p+3 of the group's 16 columns,
+// and lane q receives column q of the 4 rows.
+__device__ __forceinline__ u32x4 lds_read_bT(const uint16_t* sW, int pitch,
+                                             int row0, int col0, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int grp = lane >> 4, q = lane & 15;
+  const int row = row0 + 8 * (grp >> 1) + (q >> 2);
+  const int col = col0 + 16 * (grp & 1) + 4 * (q & 3);
+  const uint16_t* p0 = sW + row * pitch + col;
+  const uint16_t* p1 = p0 + 4 * pitch;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const_cast<uint16_t*>(p0)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const_cast<uint16_t*>(p1)));
+  u32x4 r;
+  r.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  r.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  r.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  r.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return r;
+}
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_mma(
+    const char* sA, const uint16_t* sW, int wm, int wn, int lane,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int kk = 0; kk < 4; ++kk) {
+    u32x4 a[C::TM], b[C::TN];
+    const int chunk = 2 * kk + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < C::TM; ++i) {
+      const int r = wm * C::WM + i * 32 + (lane & 31);
+      a[i] = *reinterpret_cast<const u32x4*>(sA + r * 128 +
+                                             ((chunk ^ (r & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      if (!BWD)
+        b[j] = *reinterpret_cast<const u32x4*>(
+            sW + (wn * C::WN + j * 32 + (lane & 31)) * C::PW + kk * 16 +
+            (lane >> 5) * 8);
+      else
+        b[j] = lds_read_bT(sW, C::PW, kk * 16, wn * C::WN + j * 32, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  }
+}
+
+// Interleave one step's work: the fragments of the first k16 slice are read
+// up front; each later slice's fragments are read during the previous
+// slice's MFMAs, and every MFMA is followed by a slice of the dequantization
+// VALU work; the LDS writes of the next tile trail behind.
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_schedule() {
+  using C = GemmCfg<BM, BN, BWD>;
+  constexpr int RPK = C::DS_READS / 4;         // fragment reads per k16
+  constexpr int MPK = C::MFMAS / 4;            // MFMAs per k16
+  __builtin_amdgcn_sched_group_barrier(0x020, C::A_LOADS + 4, 0);  // VMEM rd
+  __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);             // DS rd
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int g = 0; g < MPK; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);           // VALU
+      if (kk < 3 && g < RPK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (kk >= 1 && (g & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+}
+
+// Maps the linear workgroup index to an output tile so that each XCD (the
+// hardware deals workgroups round-robin over 8 XCDs) works on a contiguous
+// run of tiles, and runs walk the N direction first: a run shares A rows in
+// that XCD's L2.
+__device__ __forceinline__ void gemm_tile_of(int tiles_m, int tiles_n,
+                                             int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  tm = pid / tiles_n;
+  tn = pid % tiles_n;
+}
+
+// One reduction step: MFMAs on (sAc, sWc) while the next A tile streams into
+// sAn and the weight tile held in Wc is dequantized into sWn.
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_step(
+    int st, char* sAc, uint16_t* sWc, char* sAn, uint16_t* sWn, WRegs& Wc,
+    rsrc_t ra, rsrc_t rp, rsrc_t rq, rsrc_t rd, int M, int N, int K, int KRED,
+    int m0, int c0, int wave, int wm, int wn, int tid, int lane,
+    const Codebook& cb,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  WRegs Wn;
+  gemm_load_a<BM, BN, BWD>(ra, sAn, M, KRED, m0, (st + 1) * G_BK, wave, lane);
+  gemm_load_w<BM, BN, BWD>(Wn, rp, rq, rd, N, K, c0, (st + 2) * G_BK, tid);
+  gemm_mma<BM, BN, BWD>(sAc, sWc, wm, wn, lane, acc);
+  gemm_dequant_w<BM, BN, BWD>(Wc, sWn, cb, tid);
+  gemm_schedule<BM, BN, BWD>();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  Wc = Wn;
+}
+
+template <int BM, int BN, bool BWD>
+__global__ __launch_bounds__(256, 1) void k_gemm(
+    const uint16_t* __restrict__ Aop, const uint8_t* __restrict__ packed,
+    const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
+    const uint16_t* __restrict__ Lb, const float* __restrict__ La, int M,
+    int N, int K, int r, float s, void* __restrict__ out, int out_bf16,
+    Codebook cb) {
+  using C = GemmCfg<BM, BN, BWD>;
+  // Four distinct LDS buffers so that the compiler can see that the tiles
+  // being filled never alias the tiles being read.
+  __shared__ __attribute__((aligned(16))) char sA0[C::A_BYTES];
+  __shared__ __attribute__((aligned(16))) char sA1[C::A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t sW0[C::W_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t sW1[C::W_BYTES / 2];
+  const int NOUT = BWD ? K : N;        // output columns
+  const int KRED = BWD ? N : K;        // reduction length
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  gemm_tile_of((M + BM - 1) / BM, (NOUT + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, c0 = tn * BN;
+
+  const int64_t numel = (int64_t)N * K;
+  const rsrc_t ra = make_rsrc(Aop, (uint32_t)((int64_t)M * KRED * 2));
+  const rsrc_t rp = make_rsrc(packed, (uint32_t)((numel + 1) >> 1));
+  const rsrc_t rq = make_rsrc(qabs, (uint32_t)((numel + 63) >> 6));
+  const rsrc_t rd = make_rsrc(gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
+
+  f32x16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // Steps past the end read out of range: their tiles are zeros (a zero
+  // block constant dequantizes every code to zero), so the loop runs whole
+  // pairs of steps without branches.
+  const int nsteps = (KRED + G_BK - 1) / G_BK;
+  WRegs Wc;
+  gemm_load_a<BM, BN, BWD>(ra, sA0, M, KRED, m0, 0, wave, lane);
+  gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, 0, tid);
+  gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);
+  gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, G_BK, tid);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int st = 0; st < nsteps; st += 2) {
+    gemm_step<BM, BN, BWD>(st, sA0, sW0, sA1, sW1, Wc, ra, rp, rq, rd, M, N, K,
+                           KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
+    gemm_step<BM, BN, BWD>(st + 1, sA1, sW1, sA0, sW0, Wc, ra, rp, rq, rd, M, N,
+                           K, KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
+  }
+
+  // adapter term: reduction index jj in [0, 2r): hi part then lo part.
+  // A side: s * La[m][j] (La = T forward, G backward) split into bf16 hi/lo,
+  // stored in the swizzled A layout.  B side forward: Lb = B [N][r] read as
+  // [out col][j]; backward: Lb = A [r][K] read as [j (reduction row)][col].
+  const int width = 2 * r;
+  uint16_t* sAe = reinterpret_cast<uint16_t*>(sA0);
+  for (int j0 = 0; j0 < width; j0 += G_BK) {
+    for (int idx = tid; idx < BM * G_BK; idx += 256) {
+      const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
+      uint16_t va = 0;
+      if (jj < width && m0 + row < M) {
+        const int j = jj < r ? jj : jj - r;
+        uint16_t hi, lo;
+        split_bf16(s * La[(int64_t)(m0 + row) * r + j], hi, lo);
+        va = jj < r ? hi : lo;
+      }
+      sAe[row * 64 + ((((kk >> 3) ^ (row & 7))) << 3) + (kk & 7)] = va;
+    }
+    for (int idx = tid; idx < BN * G_BK; idx += 256) {
+      uint16_t vb = 0;
+      if (!BWD) {
+        const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
+        if (jj < width && c0 + row < NOUT)
+          vb = Lb[(int64_t)(c0 + row) * r + (jj < r ? jj : jj - r)];
+        sW0[row * C::PW + kk] = vb;
+      } else {
+        const int kk = idx / BN, col = idx % BN, jj = j0 + kk;
+        if (jj < width && c0 + col < NOUT)
+          vb = Lb[(int64_t)(jj < r ? jj : jj - r) * K + c0 + col];
+        sW0[kk * C::PW + col] = vb;
+      }
+    }
+    __syncthreads();
+    gemm_mma<BM, BN, BWD>(sA0, sW0, wm, wn, lane, acc);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = r0 + wm * 64 + i * 32 + 8 * (v >> 2) +
+        const int row = m0 + wm * C::WM + i * 32 + 8 * (v >> 2) +
                         4 * (lane >> 5) + (v & 3);
-        const int col = c0 + wn * 64 + j * 32 + (lane & 31);
-        if (row < rows && col < cols)
-          store_out(out, out_bf16, (int64_t)row * ld + col, acc[i][j][v]);
+        const int col = c0 + wn * C::WN + j * 32 + (lane & 31);
+        if (row < M && col < NOUT)
+          store_out(out, out_bf16, (int64_t)row * NOUT + col, acc[i][j][v]);
       }
-}
-
-__global__ __launch_bounds__(256) void k_fwd_gemm(
-    const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed,
-    const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
-    const uint16_t* __restrict__ Bm, const float* __restrict__ T, int M, int N,
-    int K, int r, float s, void* __restrict__ Y, int y_bf16, Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[G_BM * G_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[G_BN * G_PITCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * G_BM, n0 = blockIdx.x * G_BN;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  for (int k0 = 0; k0 < K; k0 += G_BK) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx >> 3, c8 = idx & 7;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m0 + row < M)
-        v = *reinterpret_cast<const u32x4*>(X + (int64_t)(m0 + row) * K + k0 +
-                                            c8 * 8);
-      *reinterpret_cast<u32x4*>(sA + row * G_PITCH + c8 * 8) = v;
-    }
-    {
-      const int row = tid >> 1, half = tid & 1;
-      u32x4 o[4] = {};
-      if (n0 + row < N) {
-        const int64_t e = (int64_t)(n0 + row) * K + k0 + half * 32;
-        const u32x4 p = *reinterpret_cast<const u32x4*>(packed + (e >> 1));
-        const Lut t = make_lut(cb, block_cprime(qabs, gscale, e >> 6));
-        o[0] = decode8(p.x, t);
-        o[1] = decode8(p.y, t);
-        o[2] = decode8(p.z, t);
-        o[3] = decode8(p.w, t);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(sB + row * G_PITCH + half * 32 + i * 8) = o[i];
-    }
-    __syncthreads();
-    mma_tile_step(sA, sB, wm, wn, lane, acc);
-    __syncthreads();
-  }
-
-  // adapter term: reduction index jj in [0, 2r): hi part then lo part
-  const int width = 2 * r;
-  for (int j0 = 0; j0 < width; j0 += G_BK) {
-    for (int idx = tid; idx < G_BM * G_BK; idx += 256) {
-      const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
-      uint16_t va = 0, vb = 0;
-      if (jj < width) {
-        const int j = jj < r ? jj : jj - r;
-        if (m0 + row < M) {
-          uint16_t hi, lo;
-          split_bf16(s * T[(int64_t)(m0 + row) * r + j], hi, lo);
-          va = jj < r ? hi : lo;
-        }
-        if (n0 + row < N) vb = Bm[(int64_t)(n0 + row) * r + j];
-      }
-      sA[row * G_PITCH + kk] = va;
-      sB[row * G_PITCH + kk] = vb;
-    }
-    __syncthreads();
-    mma_tile_step(sA, sB, wm, wn, lane, acc);
-    __syncthreads();
-  }
-  store_acc_tile(Y, y_bf16, N, M, N, m0, n0, wm, wn, lane, acc);
-}
-
-// ---------------------------------------------------------------------------
-// K4: backward dX GEMM.  dX[M,K] = dY[M,N] W'[N,K] (+ s G A).  Tile 128 (M)
-// x 128 (K out) x 64 (N reduction).  The W' tile is dequantized along its
-// rows and written transposed into LDS so that the MFMA B operand reads 8
-// consecutive reduction (N) elements.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bwd_dx_gemm(
-    const uint16_t* __restrict__ dY, const uint8_t* __restrict__ packed,
-    const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
-    const uint16_t* __restrict__ Am, const float* __restrict__ G, int M,
-    int N, int K, int r, float s, void* __restrict__ dX, int dx_bf16,
-    Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[G_BM * G_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[G_BN * G_PITCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * G_BM, k0 = blockIdx.x * G_BN;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  for (int n0 = 0; n0 < N; n0 += G_BK) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx >> 3, c8 = idx & 7;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m0 + row < M && n0 + c8 * 8 < N)
-        v = *reinterpret_cast<const u32x4*>(dY + (int64_t)(m0 + row) * N + n0 +
-                                            c8 * 8);
-      *reinterpret_cast<u32x4*>(sA + row * G_PITCH + c8 * 8) = v;
-    }
-    {
-      const int nr = tid >> 2, chunk = tid & 3;
-      const int kc = k0 + chunk * 32;
-      u32x4 o[4] = {};
-      if (n0 + nr < N && kc < K) {
-        const int64_t e = (int64_t)(n0 + nr) * K + kc;
-        const u32x4 p = *reinterpret_cast<const u32x4*>(packed + (e >> 1));
-        const Lut t = make_lut(cb, block_cprime(qabs, gscale, e >> 6));
-        o[0] = decode8(p.x, t);
-        o[1] = decode8(p.y, t);
-        o[2] = decode8(p.z, t);
-        o[3] = decode8(p.w, t);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w4[4] = {o[i].x, o[i].y, o[i].z, o[i].w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int kk = chunk * 32 + i * 8 + h * 2;
-          sB[kk * G_PITCH + nr] = static_cast<uint16_t>(w4[h] & 0xFFFFu);
-          sB[(kk + 1) * G_PITCH + nr] = static_cast<uint16_t>(w4[h] >> 16);
-        }
-      }
-    }
-    __syncthreads();
-    mma_tile_step(sA, sB, wm, wn, lane, acc);
-    __syncthreads();
-  }
-
-  const int width = 2 * r;
-  for (int j0 = 0; j0 < width; j0 += G_BK) {
-    for (int idx = tid; idx < G_BM * G_BK; idx += 256) {
-      const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
-      uint16_t va = 0, vb = 0;
-      if (jj < width) {
-        const int j = jj < r ? jj : jj - r;
-        if (m0 + row < M) {
-          uint16_t hi, lo;
-          split_bf16(s * G[(int64_t)(m0 + row) * r + j], hi, lo);
-          va = jj < r ? hi : lo;
-        }
-        if (k0 + row < K) vb = Am[(int64_t)j * K + k0 + row];
-      }
-      sA[row * G_PITCH + kk] = va;
-      sB[row * G_PITCH + kk] = vb;
-    }
-    __syncthreads();
-    mma_tile_step(sA, sB, wm, wn, lane, acc);
-    __syncthreads();
-  }
-  store_acc_tile(dX, dx_bf16, K, M, K, m0, k0, wm, wn, lane, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -729,11 +865,39 @@ struct ProfScope {
   }
 };
 
-#define QN_LAUNCH(kname, kernel, grid, block, st, ...)                \
+#define QN_LAUNCH_SHM(kname, kernel, grid, block, shm, st, ...)       \
   do {                                                                \
     ProfScope qn_prof_scope_(kname, st);                              \
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, __VA_ARGS__);      \
+    hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);    \
   } while (0)
+#define QN_LAUNCH(kname, kernel, grid, block, st, ...) \
+  QN_LAUNCH_SHM(kname, kernel, grid, block, 0, st, __VA_ARGS__)
+
+// Fused GEMM launch: 256 x 256 tiles when they give at least ~one
+// workgroup per CU, otherwise 128 x 128.
+template <int BM, int BN, bool BWD>
+void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
+                   const uint16_t* Lb, const float* La, int M, int r, float s,
+                   void* out, int out_bf16) {
+  const int N = (int)w->rows, K = (int)w->cols;
+  const int nout = BWD ? K : N;
+  const unsigned tiles = (unsigned)(cdiv(M, BM) * cdiv(nout, BN));
+  QN_LAUNCH_SHM(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD>),
+                dim3(tiles), dim3(256), 0, st, Aop, w->packed,
+                w->qabs, w->gscale, Lb, La, M, N, K, r, s, out, out_bf16,
+                codebook());
+}
+
+template <bool BWD>
+void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
+                 const uint16_t* Lb, const float* La, int M, int r, float s,
+                 void* out, int out_bf16) {
+  const int64_t nout = BWD ? w->cols : w->rows;
+  if (cdiv(M, 256) * cdiv(nout, 256) >= 192)
+    launch_gemm_t<256, 256, BWD>(st, Aop, w, Lb, La, M, r, s, out, out_bf16);
+  else
+    launch_gemm_t<128, 128, BWD>(st, Aop, w, Lb, La, M, r, s, out, out_bf16);
+}
 
 // Rank-tile dispatch: JT = number of 16-wide tiles of r, rounded up to a
 // power of two (1, 2, 4, 8, 16 covers r <= 256).
@@ -890,10 +1054,8 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   const float s = alpha / (float)r;
   hipStream_t st = (hipStream_t)stream;
   launch_rank_nt(st, x, K, A, K, Mi, K, (int)r, t_save);
-  QN_LAUNCH("k_fwd_gemm", k_fwd_gemm,
-            dim3((unsigned)cdiv(N, G_BN), (unsigned)cdiv(M, G_BM)), dim3(256),
-            st, x, w->packed, w->qabs, w->gscale, B, t_save, Mi, N, K, (int)r,
-            s, y, (int)(y_dtype == QN_BF16), codebook());
+  launch_gemm<false>(st, x, w, B, t_save, Mi, (int)r, s, y,
+                     (int)(y_dtype == QN_BF16));
   return check_launch();
 }
 
@@ -933,10 +1095,8 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
             dim3((unsigned)cdiv(N * r, 256)), dim3(256), st, part_db,
             (int)L.chunks, Ni, (int)r, s, dB, (int64_t)r, (int64_t)1);
   // dX = dY W' + s G A
-  QN_LAUNCH("k_bwd_dx_gemm", k_bwd_dx_gemm,
-            dim3((unsigned)cdiv(K, G_BN), (unsigned)cdiv(M, G_BM)), dim3(256),
-            st, dy, w->packed, w->qabs, w->gscale, A, G, Mi, Ni, Ki, (int)r, s,
-            dx, (int)(dx_dtype == QN_BF16), codebook());
+  launch_gemm<true>(st, dy, w, A, G, Mi, (int)r, s, dx,
+                    (int)(dx_dtype == QN_BF16));
   // dA = s G^T X  (out[k][j] -> dA[j][k])
   launch_rank_tn(st, x, K, G, Mi, Ki, (int)r, (int)L.chunks, part_da);
   QN_LAUNCH("k_rank_tn_reduce", k_rank_tn_reduce,
