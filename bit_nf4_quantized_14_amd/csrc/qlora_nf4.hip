@@ -460,46 +460,68 @@ __device__ __forceinline__ u32x4 lds_read_bT(const uint16_t* sW, int pitch,
   return r;
 }
 
+// Fragments of one k16 slice: A rows (ds_read_b128 from the swizzled tile)
+// and B columns (ds_read_b128 forward, ds_read_b64_tr_b16 backward).
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_frags(const char* sA, const uint16_t* sW,
+                                           int wm, int wn, int lane, int kk,
+                                           u32x4 (&a)[GemmCfg<BM, BN, BWD>::TM],
+                                           u32x4 (&b)[GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
+  const int chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int r = wm * C::WM + i * 32 + (lane & 31);
+    a[i] = *reinterpret_cast<const u32x4*>(sA + r * 128 + ((chunk ^ (r & 7)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    if (!BWD)
+      b[j] = *reinterpret_cast<const u32x4*>(
+          sW + (wn * C::WN + j * 32 + (lane & 31)) * C::PW + kk * 16 +
+          (lane >> 5) * 8);
+    else
+      b[j] = lds_read_bT(sW, C::PW, kk * 16, wn * C::WN + j * 32, lane);
+  }
+}
+
+// The four k16 slices of one step; slice kk+1's fragments are read while
+// slice kk's MFMAs run.
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_mma(
     const char* sA, const uint16_t* sW, int wm, int wn, int lane,
     f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
   using C = GemmCfg<BM, BN, BWD>;
+  u32x4 a[2][C::TM], b[2][C::TN];
+  gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, 0, a[0], b[0]);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    u32x4 a[C::TM], b[C::TN];
-    const int chunk = 2 * kk + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const int r = wm * C::WM + i * 32 + (lane & 31);
-      a[i] = *reinterpret_cast<const u32x4*>(sA + r * 128 +
-                                             ((chunk ^ (r & 7)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      if (!BWD)
-        b[j] = *reinterpret_cast<const u32x4*>(
-            sW + (wn * C::WN + j * 32 + (lane & 31)) * C::PW + kk * 16 +
-            (lane >> 5) * 8);
-      else
-        b[j] = lds_read_bT(sW, C::PW, kk * 16, wn * C::WN + j * 32, lane);
-    }
+    if (kk < 3)
+      gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, kk + 1, a[(kk + 1) & 1],
+                              b[(kk + 1) & 1]);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
   }
 }
 
-// Interleave one step's work: the fragments of the first k16 slice are read
-// up front; each later slice's fragments are read during the previous
-// slice's MFMAs, and every MFMA is followed by a slice of the dequantization
-// VALU work; the LDS writes of the next tile trail behind.
+#ifndef QN_SCHED
+#define QN_SCHED 0
+#endif
+#ifndef QN_DEQ_FIRST
+#define QN_DEQ_FIRST 0
+#endif
+#ifndef QN_VPM
+#define QN_VPM 4
+#endif
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_schedule() {
   using C = GemmCfg<BM, BN, BWD>;
   constexpr int RPK = C::DS_READS / 4;         // fragment reads per k16
   constexpr int MPK = C::MFMAS / 4;            // MFMAs per k16
+#if QN_SCHED == 1
   __builtin_amdgcn_sched_group_barrier(0x020, C::A_LOADS + 4, 0);  // VMEM rd
   __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);             // DS rd
 #pragma unroll
@@ -511,6 +533,21 @@ __device__ __forceinline__ void gemm_schedule() {
       if (kk < 3 && g < RPK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (kk >= 1 && (g & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
+#elif QN_SCHED == 2
+#pragma unroll
+  for (int g = 0; g < C::MFMAS; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, QN_VPM, 0);
+  }
+#elif QN_SCHED == 3
+#pragma unroll
+  for (int g = 0; g < C::MFMAS; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+  }
+#endif
+  (void)RPK; (void)MPK;
 }
 
 // Maps the linear workgroup index to an output tile so that each XCD (the
@@ -538,10 +575,15 @@ __device__ __forceinline__ void gemm_step(
   WRegs Wn;
   gemm_load_a<BM, BN, BWD>(ra, sAn, M, KRED, m0, (st + 1) * G_BK, wave, lane);
   gemm_load_w<BM, BN, BWD>(Wn, rp, rq, rd, N, K, c0, (st + 2) * G_BK, tid);
+#if QN_DEQ_FIRST
+  gemm_dequant_w<BM, BN, BWD>(Wc, sWn, cb, tid);
+  gemm_mma<BM, BN, BWD>(sAc, sWc, wm, wn, lane, acc);
+#else
   gemm_mma<BM, BN, BWD>(sAc, sWc, wm, wn, lane, acc);
   gemm_dequant_w<BM, BN, BWD>(Wc, sWn, cb, tid);
+#endif
   gemm_schedule<BM, BN, BWD>();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);   // all counters: loads landed in LDS/regs
   __syncthreads();
   Wc = Wn;
 }
@@ -550,9 +592,9 @@ template <int BM, int BN, bool BWD>
 __global__ __launch_bounds__(256, 1) void k_gemm(
     const uint16_t* __restrict__ Aop, const uint8_t* __restrict__ packed,
     const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
-    const uint16_t* __restrict__ Lb, const float* __restrict__ La, int M,
-    int N, int K, int r, float s, void* __restrict__ out, int out_bf16,
-    Codebook cb) {
+    const uint16_t* __restrict__ La_hi, const uint16_t* __restrict__ La_lo,
+    const uint16_t* __restrict__ Lb, int M, int N, int K, int rpad,
+    void* __restrict__ out, int out_bf16, Codebook cb) {
   using C = GemmCfg<BM, BN, BWD>;
   // Four distinct LDS buffers so that the compiler can see that the tiles
   // being filled never alias the tiles being read.
@@ -592,7 +634,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(
   gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, 0, tid);
   gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);
   gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, G_BK, tid);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);   // all counters: loads landed in LDS/regs
   __syncthreads();
   for (int st = 0; st < nsteps; st += 2) {
     gemm_step<BM, BN, BWD>(st, sA0, sW0, sA1, sW1, Wc, ra, rp, rq, rd, M, N, K,
@@ -601,41 +643,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm(
                            K, KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
   }
 
-  // adapter term: reduction index jj in [0, 2r): hi part then lo part.
-  // A side: s * La[m][j] (La = T forward, G backward) split into bf16 hi/lo,
-  // stored in the swizzled A layout.  B side forward: Lb = B [N][r] read as
-  // [out col][j]; backward: Lb = A [r][K] read as [j (reduction row)][col].
-  const int width = 2 * r;
-  uint16_t* sAe = reinterpret_cast<uint16_t*>(sA0);
-  for (int j0 = 0; j0 < width; j0 += G_BK) {
-    for (int idx = tid; idx < BM * G_BK; idx += 256) {
-      const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
-      uint16_t va = 0;
-      if (jj < width && m0 + row < M) {
-        const int j = jj < r ? jj : jj - r;
-        uint16_t hi, lo;
-        split_bf16(s * La[(int64_t)(m0 + row) * r + j], hi, lo);
-        va = jj < r ? hi : lo;
+  // Adapter term, 2 * rpad more reduction steps straight from global memory
+  // (small, L2-resident arrays): A side the bf16 hi and lo parts of s*T
+  // (forward) or s*G (backward), [M][rpad]; B side [NOUT][rpad], B (forward)
+  // or A^T (backward), zero-padded to rpad columns.
+  {
+    const rsrc_t rh = make_rsrc(La_hi, (uint32_t)((int64_t)M * rpad * 2));
+    const rsrc_t rl = make_rsrc(La_lo, (uint32_t)((int64_t)M * rpad * 2));
+    const rsrc_t rb = make_rsrc(Lb, (uint32_t)((int64_t)NOUT * rpad * 2));
+    for (int j0 = 0; j0 < rpad; j0 += 16) {
+      const int jc = j0 + 8 * (lane >> 5);
+      u32x4 ah[C::TM], al[C::TM], b[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const uint32_t off =
+            (uint32_t)(((int64_t)(m0 + wm * C::WM + i * 32 + (lane & 31)) * rpad + jc) * 2);
+        ah[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+        al[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
       }
-      sAe[row * 64 + ((((kk >> 3) ^ (row & 7))) << 3) + (kk & 7)] = va;
-    }
-    for (int idx = tid; idx < BN * G_BK; idx += 256) {
-      uint16_t vb = 0;
-      if (!BWD) {
-        const int row = idx / G_BK, kk = idx % G_BK, jj = j0 + kk;
-        if (jj < width && c0 + row < NOUT)
-          vb = Lb[(int64_t)(c0 + row) * r + (jj < r ? jj : jj - r)];
-        sW0[row * C::PW + kk] = vb;
-      } else {
-        const int kk = idx / BN, col = idx % BN, jj = j0 + kk;
-        if (jj < width && c0 + col < NOUT)
-          vb = Lb[(int64_t)(jj < r ? jj : jj - r) * K + c0 + col];
-        sW0[kk * C::PW + col] = vb;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const uint32_t off =
+            (uint32_t)(((int64_t)(c0 + wn * C::WN + j * 32 + (lane & 31)) * rpad + jc) * 2);
+        b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
       }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+          acc[i][j] = mfma32(ah[i], b[j], acc[i][j]);
+          acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
+        }
     }
-    __syncthreads();
-    gemm_mma<BM, BN, BWD>(sA0, sW0, wm, wn, lane, acc);
-    __syncthreads();
   }
 
 #pragma unroll
@@ -653,50 +692,71 @@ __global__ __launch_bounds__(256, 1) void k_gemm(
 }
 
 // ---------------------------------------------------------------------------
-// K5a: out[m][j] = sum_c P[m][c] R[j][c] (fp32), M x r output, C % 8 == 0.
-// One workgroup per 16 rows; the 4 waves take interleaved 32-wide slices of
-// C and are summed through LDS in a fixed order.
+// K5a: out[m][j] = sum_c P[m][c] R[j][c] (fp32), M x r output; C % 8 == 0.
+// Optionally also writes the bf16 hi and lo parts of scale*out, zero-padded
+// to rpad = 16 * JT columns (the MFMA operands of the adapter terms).
+// One workgroup per 16 rows; wave w takes the w-th quarter of C and walks it
+// in batches of U 32-wide slices whose loads are all issued before the
+// batch's MFMAs (v_mfma_f32_16x16x32_bf16), so each lane keeps several
+// 16-byte loads in flight.  The four quarters are summed through LDS in a
+// fixed order.  Buffer loads return zeros past the valid rows of P and R.
 // ---------------------------------------------------------------------------
 template <int JT>
 __global__ __launch_bounds__(256) void k_rank_nt(
     const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ R,
-    int64_t ldr, int M, int C, int r, float* __restrict__ out) {
+    int64_t ldr, int M, int C, int r, float* __restrict__ out, float scale,
+    uint16_t* __restrict__ out_hi, uint16_t* __restrict__ out_lo) {
+  constexpr int U = JT >= 8 ? 1 : 8 / JT;
   __shared__ float s_red[4][16][JT * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m0 = blockIdx.x * 16;
+  const int row = lane & 15, g = lane >> 4;
+  const int rows = min(16, M - m0);
+  const rsrc_t rp = make_rsrc(P + (int64_t)m0 * ldp, (uint32_t)((int64_t)rows * ldp * 2));
+  const rsrc_t rr = make_rsrc(R, (uint32_t)((int64_t)r * ldr * 2));
+  const int cq = ((C + 127) / 128) * 32;
+  const int cbeg = wave * cq, cend = min(C, cbeg + cq);
   f32x4 acc[JT];
 #pragma unroll
   for (int t = 0; t < JT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int row = lane & 15, g = lane >> 4;
-  for (int c0 = wave * 32; c0 < C; c0 += 128) {
-    const int c = c0 + g * 8;
-    u32x4 a = {0u, 0u, 0u, 0u};
-    if (m0 + row < M && c < C)
-      a = *reinterpret_cast<const u32x4*>(P + (int64_t)(m0 + row) * ldp + c);
+  for (int c0 = cbeg; c0 < cend; c0 += 32 * U) {
+    u32x4 a[U], b[U][JT];
 #pragma unroll
-    for (int t = 0; t < JT; ++t) {
-      const int j = t * 16 + row;
-      u32x4 b = {0u, 0u, 0u, 0u};
-      if (j < r && c < C)
-        b = *reinterpret_cast<const u32x4*>(R + (int64_t)j * ldr + c);
-      acc[t] = mfma16(a, b, acc[t]);
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 32 * u + 8 * g;
+      const bool ok = c < cend;
+      a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rp, ok ? (uint32_t)(((int64_t)row * ldp + c) * 2) : G_OOB, 0, 0));
+#pragma unroll
+      for (int t = 0; t < JT; ++t)
+        b[u][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            rr, ok ? (uint32_t)(((int64_t)(16 * t + row) * ldr + c) * 2) : G_OOB,
+            0, 0));
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < JT; ++t) acc[t] = mfma16(a[u], b[u][t], acc[t]);
   }
 #pragma unroll
-  for (int t = 0; t < JT; ++t) {
+  for (int t = 0; t < JT; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = t * 16 + row;
-      if (j < r) s_red[wave][4 * g + v][j] = acc[t][v];
-    }
-  }
+    for (int v = 0; v < 4; ++v) s_red[wave][4 * g + v][t * 16 + row] = acc[t][v];
   __syncthreads();
-  for (int idx = tid; idx < 16 * r; idx += 256) {
-    const int mi = idx / r, j = idx % r;
-    if (m0 + mi < M)
-      out[(int64_t)(m0 + mi) * r + j] =
-          ((s_red[0][mi][j] + s_red[1][mi][j]) + s_red[2][mi][j]) +
-          s_red[3][mi][j];
+  constexpr int RP = JT * 16;
+  for (int idx = tid; idx < 16 * RP; idx += 256) {
+    const int mi = idx / RP, j = idx % RP;
+    if (mi >= rows) continue;
+    const float v = ((s_red[0][mi][j] + s_red[1][mi][j]) + s_red[2][mi][j]) +
+                    s_red[3][mi][j];
+    if (out != nullptr && j < r) out[(int64_t)(m0 + mi) * r + j] = v;
+    if (out_hi != nullptr) {
+      uint16_t h, l;
+      split_bf16(scale * v, h, l);
+      out_hi[(int64_t)(m0 + mi) * RP + j] = h;
+      out_lo[(int64_t)(m0 + mi) * RP + j] = l;
+    }
   }
 }
 
@@ -709,82 +769,143 @@ __global__ __launch_bounds__(256) void k_transpose_b(
   Bt[j * N + n] = B[idx];
 }
 
+// dst_hi/dst_lo[m][j] = bf16 hi/lo parts of s * src[m][j] (j < r), zero for
+// r <= j < rpad.
+__global__ __launch_bounds__(256) void k_split_scale(
+    const float* __restrict__ src, int M, int r, int rpad, float s,
+    uint16_t* __restrict__ dst_hi, uint16_t* __restrict__ dst_lo) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * rpad) return;
+  const int64_t m = idx / rpad, j = idx % rpad;
+  uint16_t h = 0, l = 0;
+  if (j < r) split_bf16(s * src[m * r + j], h, l);
+  dst_hi[idx] = h;
+  dst_lo[idx] = l;
+}
+
+// dst[row][j] = src[row * rs + j * cs] for j < r, 0 for r <= j < rpad:
+// pads B [N][r] or transposes A [r][K] into [rows][rpad] bf16.
+__global__ __launch_bounds__(256) void k_gather_pad(
+    const uint16_t* __restrict__ src, int rows, int r, int rpad, int64_t rs,
+    int64_t cs, uint16_t* __restrict__ dst) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)rows * rpad) return;
+  const int64_t row = idx / rpad, j = idx % rpad;
+  dst[idx] = j < r ? src[row * rs + j * cs] : (uint16_t)0;
+}
+
 // ---------------------------------------------------------------------------
 // K5b: split-M partials part[chunk][c][j] = sum_{m in chunk} P[m][c] Q[m][j]
-// with P bf16 [M, C] and Q fp32 [M, r] (Q split into bf16 hi + lo).  Tile 64
-// columns of C per workgroup (16 per wave); P and Q are staged transposed
-// into LDS so both MFMA operands read 8 consecutive rows m.
+// with P bf16 [M, C] and Q given as bf16 hi + lo parts [M][16 JT].  One
+// workgroup per 64 columns of C and one chunk of rows; the whole chunk of P
+// and Q is loaded at once (every lane keeps its loads in flight) into LDS in
+// natural row-major layout, and both MFMA operands, which need 8
+// consecutive rows m per lane, come from ds_read_b64_tr_b16.
 // ---------------------------------------------------------------------------
-constexpr int TN_MCHUNK = 256;
-constexpr int TN_MSTEP = 32;
-constexpr int TN_PITCH = TN_MSTEP + 8;
+constexpr int TN_PP = 64 + 8;                 // sP pitch (bf16)
+
+__host__ __device__ constexpr int tn_chunk_rows(int jt) {
+  return jt <= 4 ? 256 : (jt == 8 ? 128 : 64);
+}
+
+// Operand of v_mfma_f32_16x16x32_bf16 whose 8 reduction elements per lane
+// run down a column of a row-major LDS tile: lane l takes column
+// col0 + l % 16, rows row0 + 8 * (l / 16) .. + 7 (two transpose reads).
+__device__ __forceinline__ u32x4 lds_read_tr16x(const uint16_t* base, int pitch,
+                                                int row0, int col0, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int g = lane >> 4, q = lane & 15;
+  const uint16_t* p0 = base + (row0 + 8 * g + (q >> 2)) * pitch + col0 + 4 * (q & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const_cast<uint16_t*>(p0)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const_cast<uint16_t*>(p0 + 4 * pitch)));
+  u32x4 v;
+  v.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  v.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  v.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  v.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return v;
+}
 
 template <int JT>
 __global__ __launch_bounds__(256) void k_rank_tn_partial(
-    const uint16_t* __restrict__ P, int64_t ldp, const float* __restrict__ Q,
-    int M, int C, int r, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t sP[64 * TN_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sQh[JT * 16 * TN_PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sQl[JT * 16 * TN_PITCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ Qh,
+    const uint16_t* __restrict__ Ql, int M, int C, int r,
+    float* __restrict__ part) {
+  constexpr int MCH = tn_chunk_rows(JT);
+  constexpr int PQ = JT * 16 + 8;             // sQ pitch (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t sP[MCH * TN_PP];
+  __shared__ __attribute__((aligned(16))) uint16_t sQh[MCH * PQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sQl[MCH * PQ];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = blockIdx.x * 64;
   const int chunk = blockIdx.y;
-  const int mbeg = chunk * TN_MCHUNK;
-  const int mend = min(M, mbeg + TN_MCHUNK);
-  const int rpad = JT * 16;
+  const int mbeg = chunk * MCH;
+  const int rows = min(MCH, M - mbeg);
+  const rsrc_t rp = make_rsrc(P + (int64_t)mbeg * ldp, (uint32_t)((int64_t)rows * ldp * 2));
+
+  // P chunk: MCH rows x 64 columns, 16 bytes per lane per load
+  constexpr int PL = MCH * 8 / 256;
+  u32x4 pv[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int idx = tid + 256 * i, mi = idx >> 3, c = c0 + 8 * (idx & 7);
+    pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        rp, c < C ? (uint32_t)(((int64_t)mi * ldp + c) * 2) : G_OOB, 0, 0));
+  }
+  // Q chunk: bf16 hi and lo rows of RP = 16 JT columns, 16 bytes per load
+  constexpr int RP = JT * 16, QC = RP / 8;             // 16-byte chunks / row
+  constexpr int QL = (MCH * QC + 255) / 256;
+  const rsrc_t rqh = make_rsrc(Qh + (int64_t)mbeg * RP, (uint32_t)(rows * RP * 2));
+  const rsrc_t rql = make_rsrc(Ql + (int64_t)mbeg * RP, (uint32_t)(rows * RP * 2));
+  u32x4 qh[QL], ql[QL];
+#pragma unroll
+  for (int i = 0; i < QL; ++i) {
+    const int idx = tid + 256 * i;
+    const uint32_t off = idx < MCH * QC ? (uint32_t)(idx * 16) : G_OOB;
+    qh[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rqh, off, 0, 0));
+    ql[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rql, off, 0, 0));
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int idx = tid + 256 * i;
+    *reinterpret_cast<u32x4*>(sP + (idx >> 3) * TN_PP + 8 * (idx & 7)) = pv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < QL; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < MCH * QC) {
+      const int mi = idx / QC, j = 8 * (idx % QC);
+      *reinterpret_cast<u32x4*>(sQh + mi * PQ + j) = qh[i];
+      *reinterpret_cast<u32x4*>(sQl + mi * PQ + j) = ql[i];
+    }
+  }
+  __syncthreads();
+
   f32x4 acc[JT];
 #pragma unroll
   for (int t = 0; t < JT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int col = lane & 15, g = lane >> 4;
-
-  for (int ms = mbeg; ms < mend; ms += TN_MSTEP) {
-    {
-      const int mi = tid >> 3, c8 = tid & 7;
-      const int c = c0 + c8 * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ms + mi < mend && c < C)
-        v = *reinterpret_cast<const u32x4*>(P + (int64_t)(ms + mi) * ldp + c);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        sP[(c8 * 8 + 2 * h) * TN_PITCH + mi] =
-            static_cast<uint16_t>(w4[h] & 0xFFFFu);
-        sP[(c8 * 8 + 2 * h + 1) * TN_PITCH + mi] =
-            static_cast<uint16_t>(w4[h] >> 16);
-      }
-    }
-    for (int idx = tid; idx < TN_MSTEP * rpad; idx += 256) {
-      const int mi = idx / rpad, j = idx % rpad;
-      uint16_t hi = 0, lo = 0;
-      if (ms + mi < mend && j < r) split_bf16(Q[(int64_t)(ms + mi) * r + j], hi, lo);
-      sQh[j * TN_PITCH + mi] = hi;
-      sQl[j * TN_PITCH + mi] = lo;
-    }
-    __syncthreads();
-    const u32x4 a = *reinterpret_cast<const u32x4*>(
-        sP + (wave * 16 + col) * TN_PITCH + g * 8);
+#pragma unroll 2
+  for (int s = 0; s < MCH; s += 32) {
+    const u32x4 a = lds_read_tr16x(sP, TN_PP, s, 16 * wave, lane);
 #pragma unroll
     for (int t = 0; t < JT; ++t) {
-      const u32x4 bh = *reinterpret_cast<const u32x4*>(
-          sQh + (t * 16 + col) * TN_PITCH + g * 8);
-      const u32x4 bl = *reinterpret_cast<const u32x4*>(
-          sQl + (t * 16 + col) * TN_PITCH + g * 8);
-      acc[t] = mfma16(a, bh, acc[t]);
-      acc[t] = mfma16(a, bl, acc[t]);
+      acc[t] = mfma16(a, lds_read_tr16x(sQh, PQ, s, 16 * t, lane), acc[t]);
+      acc[t] = mfma16(a, lds_read_tr16x(sQl, PQ, s, 16 * t, lane), acc[t]);
     }
-    __syncthreads();
   }
-  // acc[t][v] = C-tile[c = wave*16 + 4g + v][j = t*16 + col]
+  // acc[t][v] = C-tile[c = 16 * wave + 4 * (lane / 16) + v][j = 16 t + lane % 16]
+  const int g = lane >> 4, col = lane & 15;
 #pragma unroll
-  for (int t = 0; t < JT; ++t) {
+  for (int t = 0; t < JT; ++t)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int c = c0 + wave * 16 + 4 * g + v;
-      const int j = t * 16 + col;
-      if (c < C && j < r)
-        part[((int64_t)chunk * C + c) * r + j] = acc[t][v];
+      const int c = c0 + 16 * wave + 4 * g + v, j = 16 * t + col;
+      if (c < C && j < r) part[((int64_t)chunk * C + c) * r + j] = acc[t][v];
     }
-  }
 }
 
 // out[c * sc + j * sj] = s * sum_chunk part[chunk][c][j], chunks in order.
@@ -838,6 +959,10 @@ bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
   if (K % QN_BLOCK != 0 || N % 8 != 0) return false;
   // 32-bit index arithmetic inside the GEMM kernels
   if (M > (1LL << 30) || N > (1LL << 30) || K > (1LL << 30)) return false;
+  // buffer-resource ranges are 32-bit byte counts (offsets past 2^31 mean
+  // "out of range"): every operand read through one stays below 2 GiB
+  const int64_t lim = 1LL << 31;
+  if (M * K * 2 >= lim || M * N * 2 >= lim || N * K / 2 >= lim) return false;
   return true;
 }
 
@@ -877,91 +1002,109 @@ struct ProfScope {
 // workgroup per CU, otherwise 128 x 128.
 template <int BM, int BN, bool BWD>
 void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
-                   const uint16_t* Lb, const float* La, int M, int r, float s,
-                   void* out, int out_bf16) {
+                   const uint16_t* La_hi, const uint16_t* La_lo,
+                   const uint16_t* Lb, int M, int rpad, void* out,
+                   int out_bf16) {
   const int N = (int)w->rows, K = (int)w->cols;
   const int nout = BWD ? K : N;
   const unsigned tiles = (unsigned)(cdiv(M, BM) * cdiv(nout, BN));
-  QN_LAUNCH_SHM(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD>),
-                dim3(tiles), dim3(256), 0, st, Aop, w->packed,
-                w->qabs, w->gscale, Lb, La, M, N, K, r, s, out, out_bf16,
-                codebook());
+  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD>),
+            dim3(tiles), dim3(256), st, Aop, w->packed, w->qabs, w->gscale,
+            La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16, codebook());
 }
 
 template <bool BWD>
 void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
-                 const uint16_t* Lb, const float* La, int M, int r, float s,
-                 void* out, int out_bf16) {
+                 const uint16_t* La_hi, const uint16_t* La_lo,
+                 const uint16_t* Lb, int M, int rpad, void* out,
+                 int out_bf16) {
   const int64_t nout = BWD ? w->cols : w->rows;
   if (cdiv(M, 256) * cdiv(nout, 256) >= 192)
-    launch_gemm_t<256, 256, BWD>(st, Aop, w, Lb, La, M, r, s, out, out_bf16);
+    launch_gemm_t<256, 256, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
+                                 out_bf16);
   else
-    launch_gemm_t<128, 128, BWD>(st, Aop, w, Lb, La, M, r, s, out, out_bf16);
+    launch_gemm_t<128, 128, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
+                                 out_bf16);
 }
 
 // Rank-tile dispatch: JT = number of 16-wide tiles of r, rounded up to a
-// power of two (1, 2, 4, 8, 16 covers r <= 256).
+// power of two (1, 2, 4, 8, 16 covers r <= 256); rpad = 16 JT.
 int rank_tiles(int r) {
   int jt = 1;
   while (jt * 16 < r) jt *= 2;
   return jt;
 }
 
-template <int JT>
-void launch_rank_nt_t(dim3 grid, hipStream_t st, const uint16_t* P,
-                      int64_t ldp, const uint16_t* R, int64_t ldr, int M,
-                      int C, int r, float* out) {
-  QN_LAUNCH("k_rank_nt", k_rank_nt<JT>, grid, dim3(256), st, P, ldp, R, ldr,
-            M, C, r, out);
-}
+#define QN_RANK_DISPATCH(r, CALL)                \
+  switch (rank_tiles(r)) {                       \
+    case 1: { constexpr int JT = 1; CALL; break; }   \
+    case 2: { constexpr int JT = 2; CALL; break; }   \
+    case 4: { constexpr int JT = 4; CALL; break; }   \
+    case 8: { constexpr int JT = 8; CALL; break; }   \
+    default: { constexpr int JT = 16; CALL; break; } \
+  }
 
 void launch_rank_nt(hipStream_t st, const uint16_t* P, int64_t ldp,
                     const uint16_t* R, int64_t ldr, int M, int C, int r,
-                    float* out) {
+                    float* out, float scale, uint16_t* hi, uint16_t* lo) {
   const dim3 grid((unsigned)cdiv(M, 16));
-  switch (rank_tiles(r)) {
-    case 1: launch_rank_nt_t<1>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
-    case 2: launch_rank_nt_t<2>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
-    case 4: launch_rank_nt_t<4>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
-    case 8: launch_rank_nt_t<8>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
-    default: launch_rank_nt_t<16>(grid, st, P, ldp, R, ldr, M, C, r, out); break;
-  }
-}
-
-template <int JT>
-void launch_rank_tn_t(dim3 grid, hipStream_t st, const uint16_t* P,
-                      int64_t ldp, const float* Q, int M, int C, int r,
-                      float* part) {
-  QN_LAUNCH("k_rank_tn_partial", k_rank_tn_partial<JT>, grid, dim3(256), st,
-            P, ldp, Q, M, C, r, part);
+  QN_RANK_DISPATCH(r, QN_LAUNCH("k_rank_nt", k_rank_nt<JT>, grid, dim3(256),
+                                st, P, ldp, R, ldr, M, C, r, out, scale, hi,
+                                lo));
 }
 
 void launch_rank_tn(hipStream_t st, const uint16_t* P, int64_t ldp,
-                    const float* Q, int M, int C, int r, int chunks,
-                    float* part) {
+                    const uint16_t* Qh, const uint16_t* Ql, int M, int C,
+                    int r, int chunks, float* part) {
   const dim3 grid((unsigned)cdiv(C, 64), (unsigned)chunks);
-  switch (rank_tiles(r)) {
-    case 1: launch_rank_tn_t<1>(grid, st, P, ldp, Q, M, C, r, part); break;
-    case 2: launch_rank_tn_t<2>(grid, st, P, ldp, Q, M, C, r, part); break;
-    case 4: launch_rank_tn_t<4>(grid, st, P, ldp, Q, M, C, r, part); break;
-    case 8: launch_rank_tn_t<8>(grid, st, P, ldp, Q, M, C, r, part); break;
-    default: launch_rank_tn_t<16>(grid, st, P, ldp, Q, M, C, r, part); break;
-  }
+  QN_RANK_DISPATCH(r, QN_LAUNCH("k_rank_tn_partial", k_rank_tn_partial<JT>,
+                                grid, dim3(256), st, P, ldp, Qh, Ql, M, C, r,
+                                part));
+}
+
+template <typename T>
+T* ws_at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
 }  // namespace
 
 namespace qn {
 
+FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
+                                  int32_t r) {
+  (void)K;
+  FwdWorkspace L{};
+  L.rpad = 16 * rank_tiles(r);
+  size_t off = 0;
+  L.th = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.tl = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.bp = off;
+  off += align256(size_t(N) * L.rpad * 2);
+  L.total = off;
+  return L;
+}
+
 BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K,
                                   int32_t r) {
   BwdWorkspace L{};
-  L.chunks = cdiv(M, TN_MCHUNK);
+  L.rpad = 16 * rank_tiles(r);
+  L.chunks = cdiv(M, tn_chunk_rows(rank_tiles(r)));
   size_t off = 0;
   L.bt = off;
   off += align256(size_t(r) * N * 2);
-  L.g = off;
-  off += align256(size_t(M) * r * 4);
+  L.gh = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.gl = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.th = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.tl = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.atp = off;
+  off += align256(size_t(K) * L.rpad * 2);
   L.part_db = off;
   off += align256(size_t(L.chunks) * N * r * 4);
   L.part_da = off;
@@ -1032,7 +1175,7 @@ int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream) {
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
                              int32_t which) {
   if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QN_MAX_RANK) return 0;
-  if (which == QN_FWD) return 0;
+  if (which == QN_FWD) return qn::fwd_workspace_layout(M, N, K, r).total;
   if (which == QN_BWD) return qn::bwd_workspace_layout(M, N, K, r).total;
   return 0;
 }
@@ -1041,8 +1184,6 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
                      const uint16_t* A, const uint16_t* B, int32_t r,
                      float alpha, void* y, int32_t y_dtype, float* t_save,
                      void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (x == nullptr || A == nullptr || B == nullptr || y == nullptr ||
       t_save == nullptr)
     return QN_EINVAL;
@@ -1050,11 +1191,21 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   if (y_dtype != QN_F32 && y_dtype != QN_BF16) return QN_EINVAL;
   if (!aligned16(x) || !aligned16(A) || !aligned16(y) || !aligned16(t_save))
     return QN_EINVAL;
-  const int N = (int)w->rows, K = (int)w->cols, Mi = (int)M;
+  const int64_t N = w->rows, K = w->cols;
+  const qn::FwdWorkspace L = qn::fwd_workspace_layout(M, N, K, r);
+  if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
+    return QN_EWORKSPACE;
+  uint16_t* Th = ws_at<uint16_t>(ws, L.th);
+  uint16_t* Tl = ws_at<uint16_t>(ws, L.tl);
+  uint16_t* Bp = ws_at<uint16_t>(ws, L.bp);
   const float s = alpha / (float)r;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
   hipStream_t st = (hipStream_t)stream;
-  launch_rank_nt(st, x, K, A, K, Mi, K, (int)r, t_save);
-  launch_gemm<false>(st, x, w, B, t_save, Mi, (int)r, s, y,
+  // T = X A^T (fp32, saved) and the hi/lo parts of s T
+  launch_rank_nt(st, x, K, A, K, Mi, Ki, (int)r, t_save, s, Th, Tl);
+  QN_LAUNCH("k_gather_pad", k_gather_pad, dim3((unsigned)cdiv(N * L.rpad, 256)),
+            dim3(256), st, B, Ni, (int)r, L.rpad, (int64_t)r, (int64_t)1, Bp);
+  launch_gemm<false>(st, x, w, Th, Tl, Bp, Mi, L.rpad, y,
                      (int)(y_dtype == QN_BF16));
   return check_launch();
 }
@@ -1076,32 +1227,41 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
   const qn::BwdWorkspace L = qn::bwd_workspace_layout(M, N, K, r);
   if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
     return QN_EWORKSPACE;
-  char* base = static_cast<char*>(ws);
-  uint16_t* Bt = reinterpret_cast<uint16_t*>(base + L.bt);
-  float* G = reinterpret_cast<float*>(base + L.g);
-  float* part_db = reinterpret_cast<float*>(base + L.part_db);
-  float* part_da = reinterpret_cast<float*>(base + L.part_da);
+  uint16_t* Bt = ws_at<uint16_t>(ws, L.bt);
+  uint16_t* Gh = ws_at<uint16_t>(ws, L.gh);
+  uint16_t* Gl = ws_at<uint16_t>(ws, L.gl);
+  uint16_t* Th = ws_at<uint16_t>(ws, L.th);
+  uint16_t* Tl = ws_at<uint16_t>(ws, L.tl);
+  uint16_t* Atp = ws_at<uint16_t>(ws, L.atp);
+  float* part_db = ws_at<float>(ws, L.part_db);
+  float* part_da = ws_at<float>(ws, L.part_da);
   const float s = alpha / (float)r;
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
   hipStream_t st = (hipStream_t)stream;
 
   QN_LAUNCH("k_transpose_b", k_transpose_b, dim3((unsigned)cdiv(N * r, 256)),
             dim3(256), st, B, Ni, (int)r, Bt);
-  // G = dY B
-  launch_rank_nt(st, dy, N, Bt, N, Mi, Ni, (int)r, G);
-  // dB = s dY^T T
-  launch_rank_tn(st, dy, N, t_saved, Mi, Ni, (int)r, (int)L.chunks, part_db);
+  // hi/lo parts of s G, G = dY B
+  launch_rank_nt(st, dy, N, Bt, N, Mi, Ni, (int)r, nullptr, s, Gh, Gl);
+  // hi/lo parts of s T
+  QN_LAUNCH("k_split_scale", k_split_scale, dim3((unsigned)cdiv(M * L.rpad, 256)),
+            dim3(256), st, t_saved, Mi, (int)r, L.rpad, s, Th, Tl);
+  // A^T padded to [K][rpad] for the dX adapter term
+  QN_LAUNCH("k_gather_pad", k_gather_pad, dim3((unsigned)cdiv(K * L.rpad, 256)),
+            dim3(256), st, A, Ki, (int)r, L.rpad, (int64_t)1, K, Atp);
+  // dB = dY^T (s T)
+  launch_rank_tn(st, dy, N, Th, Tl, Mi, Ni, (int)r, (int)L.chunks, part_db);
   QN_LAUNCH("k_rank_tn_reduce", k_rank_tn_reduce,
             dim3((unsigned)cdiv(N * r, 256)), dim3(256), st, part_db,
-            (int)L.chunks, Ni, (int)r, s, dB, (int64_t)r, (int64_t)1);
-  // dX = dY W' + s G A
-  launch_gemm<true>(st, dy, w, A, G, Mi, (int)r, s, dx,
+            (int)L.chunks, Ni, (int)r, 1.0f, dB, (int64_t)r, (int64_t)1);
+  // dX = dY W' + (s G) A
+  launch_gemm<true>(st, dy, w, Gh, Gl, Atp, Mi, L.rpad, dx,
                     (int)(dx_dtype == QN_BF16));
-  // dA = s G^T X  (out[k][j] -> dA[j][k])
-  launch_rank_tn(st, x, K, G, Mi, Ki, (int)r, (int)L.chunks, part_da);
+  // dA = (s G)^T X  (out[k][j] -> dA[j][k])
+  launch_rank_tn(st, x, K, Gh, Gl, Mi, Ki, (int)r, (int)L.chunks, part_da);
   QN_LAUNCH("k_rank_tn_reduce", k_rank_tn_reduce,
             dim3((unsigned)cdiv(K * r, 256)), dim3(256), st, part_da,
-            (int)L.chunks, Ki, (int)r, s, dA, (int64_t)1, K);
+            (int)L.chunks, Ki, (int)r, 1.0f, dA, (int64_t)1, K);
   return check_launch();
 }
 

@@ -11,16 +11,28 @@ namespace qn {
 // precision (codebook.cpp).
 void derive_codebook(float levels[16], float thresholds[15]);
 
-// Workspace layout of the backward pass (byte offsets, 256-byte aligned).
-struct BwdWorkspace {
-  size_t bt;        // bf16 [r, N]   B transposed
-  size_t g;         // fp32 [M, r]   G = dY B
-  size_t part_db;   // fp32 [chunks, N, r] split-M partials of dY^T T
-  size_t part_da;   // fp32 [chunks, K, r] split-M partials of G^T X
+// Workspace layouts of the fused calls (byte offsets, 256-byte aligned).
+// rpad = r rounded up to 16, 32, 64, 128 or 256 (the adapter MFMA width).
+struct FwdWorkspace {
+  size_t th, tl;    // bf16 [M, rpad]  hi/lo parts of s*T
+  size_t bp;        // bf16 [N, rpad]  B zero-padded
   size_t total;
-  int64_t chunks;   // number of M chunks
+  int32_t rpad;
 };
 
+struct BwdWorkspace {
+  size_t bt;        // bf16 [r, N]     B transposed
+  size_t gh, gl;    // bf16 [M, rpad]  hi/lo parts of s*G, G = dY B
+  size_t th, tl;    // bf16 [M, rpad]  hi/lo parts of s*T
+  size_t atp;       // bf16 [K, rpad]  A transposed, zero-padded
+  size_t part_db;   // fp32 [chunks, N, r] split-M partials of dY^T (s T)
+  size_t part_da;   // fp32 [chunks, K, r] split-M partials of (s G)^T X
+  size_t total;
+  int64_t chunks;   // number of M chunks
+  int32_t rpad;
+};
+
+FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
 }  // namespace qn

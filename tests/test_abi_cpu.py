@@ -88,6 +88,7 @@ def test_linear_validation():
     assert fwd(x=p + 2) == capi.QN_EINVAL
     assert fwd(w=_fake_tensor(128, 100)) == capi.QN_EINVAL    # K % 64 != 0
     assert fwd(w=_fake_tensor(100, 256)) == capi.QN_EINVAL    # N % 8 != 0
+    assert fwd() == capi.QN_EWORKSPACE                        # no workspace
 
     need = capi.qlora_workspace_bytes(16, 128, 256, 8, capi.QN_BWD)
     assert need > 0
@@ -102,7 +103,7 @@ def test_linear_validation():
 
 def test_workspace_sizes():
     assert capi.qlora_workspace_bytes(0, 1, 64, 8, capi.QN_BWD) == 0
-    assert capi.qlora_workspace_bytes(16, 256, 512, 8, capi.QN_FWD) == 0
+    assert capi.qlora_workspace_bytes(16, 256, 512, 8, capi.QN_FWD) > 0
     a = capi.qlora_workspace_bytes(4096, 11008, 4096, 16, capi.QN_BWD)
     b = capi.qlora_workspace_bytes(4096, 11008, 4096, 64, capi.QN_BWD)
     assert 0 < a < b
