@@ -13,9 +13,14 @@ void derive_codebook(float levels[16], float thresholds[15]);
 
 // Workspace layouts of the fused calls (byte offsets, 256-byte aligned).
 // rpad = r rounded up to 16, 32, 64, 128 or 256 (the adapter MFMA width).
+// M <= QN_SKINNY_M takes the skinny (GEMV) forward.
+constexpr int64_t QN_SKINNY_M = 16;
+
 struct FwdWorkspace {
-  size_t th, tl;    // bf16 [M, rpad]  hi/lo parts of s*T
-  size_t bp;        // bf16 [N, rpad]  B zero-padded
+  size_t th, tl;    // bf16 [M, rpad]  hi/lo parts of s*T      (GEMM path)
+  size_t bp;        // bf16 [N, rpad]  B zero-padded           (GEMM path)
+  size_t part;      // fp32 [slices, 16, rows] K-slice partials (skinny path)
+  int32_t slices, ks;
   size_t total;
   int32_t rpad;
 };

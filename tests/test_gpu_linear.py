@@ -94,6 +94,10 @@ def test_tiny_workload_bf16_outputs():
     (300, 264, 128, 17, 3.0),    # rank just past a 16-wide tile
     (64, 128, 256, 256, 512.0),  # maximum rank
     (257, 1024, 576, 16, 32.0),  # M spans two split-M chunks
+    (8, 200, 320, 5, 3.0),       # skinny path: N % 16 != 0, K % 256 != 0
+    (13, 1032, 2368, 33, 8.0),   # skinny path: several K slices, r > 32
+    (16, 64, 4160, 256, 64.0),   # skinny path at the largest M and rank
+    (17, 136, 192, 8, 16.0),     # just above the skinny threshold
 ])
 def test_ragged_shapes(m, n, k, r, alpha):
     wk = wl.workload("tiny")
