@@ -264,34 +264,74 @@ __global__ __launch_bounds__(QZ_THREADS) void k_quantize(
 }
 
 // ---------------------------------------------------------------------------
-// K2: dequantization stream.  Each thread turns 16 packed bytes (32 weights,
-// inside one block) into 64 bytes of bf16.
+// K2: dequantization stream.  A wave handles spans of 2048 weights (1 KB of
+// packed codes -> 4 KB of bf16, 32 blocks, inside one double-quant group).
+// Lane l takes packed dword l + 64 j (j = 0..3) of the span, so every load
+// instruction reads 256 contiguous bytes and every store instruction writes
+// 1 KB contiguous (non-temporal); each dword (8 weights) lies in one block
+// and gets that block's 16-entry LUT.  Spans are dealt round-robin to the
+// waves; the next span's loads are issued before the current one is
+// decoded.  Weights past the last whole span are done by k_dequant_tail.
 // ---------------------------------------------------------------------------
 constexpr int DQ_THREADS = 256;
+constexpr int DQ_SPAN = 2048;                 // weights per span
+#ifndef QN_DQ_GRID_CAP
+#define QN_DQ_GRID_CAP 16384
+#endif
+
+struct DqRegs {
+  uint32_t p[4];
+  uint32_t q[4];
+  float d;
+};
 
 __global__ __launch_bounds__(DQ_THREADS) void k_dequant(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
-    const float* __restrict__ gscale, int64_t numel,
+    const float* __restrict__ gscale, int64_t nspans,
     uint16_t* __restrict__ out, Codebook cb) {
-  const int64_t chunk = (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x;
-  const int64_t e0 = chunk * 32;
-  if (e0 >= numel) return;
-  const float cp = block_cprime(qabs, gscale, e0 >> 6);
-  if (e0 + 32 <= numel) {
-    const u32x4 p = *reinterpret_cast<const u32x4*>(packed + (e0 >> 1));
-    const Lut t = make_lut(cb, cp);
-    u32x4* o = reinterpret_cast<u32x4*>(out + e0);
-    o[0] = decode8(p.x, t);
-    o[1] = decode8(p.y, t);
-    o[2] = decode8(p.z, t);
-    o[3] = decode8(p.w, t);
-  } else {
-    for (int64_t e = e0; e < numel; ++e) {
-      const uint32_t byte = packed[e >> 1];
-      const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xFu);
-      out[e] = decode1(cb, code, cp);
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = ((int64_t)blockIdx.x * DQ_THREADS + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * DQ_THREADS) >> 6;
+  auto load = [&](DqRegs& R, int64_t span) {
+    const bool ok = span < nspans;
+    const int64_t sp = ok ? span : 0;
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed) + sp * (DQ_SPAN / 8);
+    const uint8_t* qb = qabs + sp * (DQ_SPAN / 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      R.p[j] = pw[lane + 64 * j];
+      R.q[j] = qb[(lane >> 3) + 8 * j];
     }
+    R.d = ok ? gscale[(sp * (DQ_SPAN / 64)) >> 8] : 0.0f;
+  };
+  DqRegs cur;
+  int64_t span = wave0;
+  load(cur, span);
+  for (; span < nspans; span += nwaves) {
+    DqRegs nxt;
+    load(nxt, span + nwaves);
+    u32x4* o = reinterpret_cast<u32x4*>(out + span * DQ_SPAN);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const Lut t = make_lut(cb, static_cast<float>(cur.q[j]) * cur.d);
+      // streaming store: the output is not re-read here, and keeping it out
+      // of L2 avoids a large write-back when the kernel retires
+      __builtin_nontemporal_store(decode8(cur.p[j], t), &o[lane + 64 * j]);
+    }
+    cur = nxt;
   }
+}
+
+// Weights [e0, numel), e0 a multiple of 2048: one thread per weight.
+__global__ __launch_bounds__(DQ_THREADS) void k_dequant_tail(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
+    const float* __restrict__ gscale, int64_t e0, int64_t numel,
+    uint16_t* __restrict__ out, Codebook cb) {
+  const int64_t e = e0 + (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x;
+  if (e >= numel) return;
+  const uint32_t byte = packed[e >> 1];
+  const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xFu);
+  out[e] = decode1(cb, code, block_cprime(qabs, gscale, e >> 6));
 }
 
 // ---------------------------------------------------------------------------
@@ -1414,12 +1454,20 @@ int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream) {
   if (!valid_tensor(w) || w_bf16 == nullptr || !aligned16(w_bf16))
     return QN_EINVAL;
   const int64_t numel = w->rows * w->cols;
-  const int64_t chunks = cdiv(numel, 32);
-  const int64_t grid = cdiv(chunks, DQ_THREADS);
-  if (grid > 0x7FFFFFFFLL) return QN_EINVAL;
-  QN_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(DQ_THREADS),
-            (hipStream_t)stream, w->packed, w->qabs, w->gscale, numel, w_bf16,
-            codebook());
+  const int64_t nspans = numel / DQ_SPAN;
+  hipStream_t st = (hipStream_t)stream;
+  if (nspans > 0) {
+    // up to 64 waves per CU; larger tensors walk several spans per wave
+    const int64_t grid = std::min<int64_t>(cdiv(nspans, DQ_THREADS / 64), QN_DQ_GRID_CAP);
+    QN_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(DQ_THREADS),
+              st, w->packed, w->qabs, w->gscale, nspans, w_bf16, codebook());
+  }
+  const int64_t e0 = nspans * DQ_SPAN;
+  if (e0 < numel)
+    QN_LAUNCH("k_dequant_tail", k_dequant_tail,
+              dim3((unsigned)cdiv(numel - e0, DQ_THREADS)), dim3(DQ_THREADS),
+              st, w->packed, w->qabs, w->gscale, e0, numel, w_bf16,
+              codebook());
   return check_launch();
 }
 
