@@ -263,6 +263,25 @@ def bench_70b(reps, do_train=True):
     return res
 
 
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch of `kernel_key` from the committed rocprofv3
+    counter summary (profiles/hbm_traffic.json, FETCH_SIZE/WRITE_SIZE scaled
+    by a plain copy of known size), or None when the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    src = os.path.join(ROOT, "bit_nf4_quantized_14_amd", "csrc", "qlora_nf4.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != sha or kernel_key not in rec.get("kernels", {}):
+        return None
+    k = rec["kernels"][kernel_key]
+    return k["read_bytes"] + k["write_bytes"]
+
+
 def cpu_baseline(m_sample: int):
     """The CPU oracle (as it stands) on a bounded sample of the same step:
     the full weight is dequantized, forward+backward run on m_sample tokens."""
@@ -304,6 +323,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-70b", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--only", choices=("dequant", "skinny", "layer70b"),
+                    help="run one component pass only (for profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 256 MiB device-to-device copy, the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -319,6 +343,22 @@ def main():
     from bit_nf4_quantized_14_amd import workloads as wl
 
     capi.lib()
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.only:
+        reps = max(3, args.steps)
+        if args.only == "dequant":
+            res = bench_dequant_quant(reps)
+        elif args.only == "skinny":
+            res = bench_70b(reps, do_train=False)
+        else:
+            res = bench_70b(reps)
+        print(json.dumps({"only": args.only, "components": res}), flush=True)
+        return
     wk = wl.workload("gate7b")
     log("generating gate7b inputs")
     pr = Problem(wk, 0)
@@ -386,7 +426,11 @@ def main():
                    "flops_per_step": flops, "parallelism": "single-gpu"},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(
+                         "k_gemm<256, 256, true>" if dom == "k_bwd_dx_gemm"
+                         else "k_gemm<256, 256, false>"),
+                     "traffic_unit": "HBM bytes per launch",
                      "avg_ms": dom_ms, "flops_per_launch": gemm_flops[dom]},
         "kernels": kernels,
     }
