@@ -388,17 +388,19 @@ __device__ __forceinline__ void store_out(void* out, int out_bf16,
 // Per reduction step:
 //  * the A tile (X or dY rows, bf16) goes global -> LDS directly
 //    (buffer_load ... lds, 1 KB per wave instruction), 128-byte rows with
-//    the 16-byte chunk index XOR-swizzled by (row & 7) so the MFMA operand
-//    reads hit distinct banks;
+//    the 16-byte chunk index XOR-swizzled by (row / 2) & 7: the 16 lanes
+//    of one ds_read_b128 phase (16 rows) cover all 64 LDS banks;
 //  * the weight tile arrives as packed nibbles + 8-bit block codes + group
 //    scales in registers and each thread dequantizes BN/4 weights of one
-//    64-weight block (per-block v_perm LUT) into LDS in the weight's natural
-//    row-major layout.  The forward reads W' rows as MFMA B operands with
-//    ds_read_b128; the backward reads W' columns with ds_read_b64_tr_b16.
+//    64-weight block (per-block v_perm LUT) into LDS, row-major.  The
+//    forward reads W' rows as MFMA B operands with ds_read_b128 (rows padded
+//    to 144 bytes); the backward reads W' columns with ds_read_b64_tr_b16
+//    from unpadded rows whose 16-byte chunks are XOR-swizzled (wswz).
 // LDS is double-buffered.  While the MFMAs consume step i, the A tile of
 // step i+1 streams into the other buffer and the weight tile of step i+1
 // (loaded one step earlier) is dequantized into it; the dequantization is
-// interleaved with the MFMAs by sched_group_barrier.  Global loads go
+// woven between the MFMAs in fenced groups (one MFMA, then up to six VALU
+// ops), so it runs while the matrix core is busy.  Global loads go
 // through buffer resources whose range check returns zeros, which covers
 // ragged M, N and K tiles without branches.
 // The adapter term is 2r extra reduction steps with the A side s*T (or s*G)
@@ -417,6 +419,20 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            (int)bytes, G_RSRC_FLAGS);
 }
 
+// Backward weight tile: thread -> (weight row within the step, block of EPT
+// output columns).
+__device__ __forceinline__ int bwd_wrow(int tid) { return tid >> 2; }
+__device__ __forceinline__ int bwd_wblk(int tid) { return tid & 3; }
+
+// XOR applied to the 16-byte chunk index c of row n of the 64 x 256 backward
+// weight tile.  With it, the 16 lanes of a ds_write_b128 phase (4 rows x 4
+// column blocks of 64) and the 32 lanes of a ds_read_b64_tr_b16 phase
+// (4 rows x 4 chunks) each cover all 64 LDS banks.
+__device__ __forceinline__ int wswz(int n, int c) {
+  const int r = n & 3, h = (c >> 4) & 1;
+  return ((r >> 1) << 3) | ((r & 1) << 2) | (h << 1) | (r >> 1);
+}
+
 template <int BM, int BN, bool BWD>
 struct GemmCfg {
   static constexpr int WM = BM / 2, WN = BN / 2;        // per-wave tile
@@ -427,7 +443,9 @@ struct GemmCfg {
   static constexpr int WDW = EPT / 8;                   // packed dwords
   static constexpr int TPR = 64 / EPT;                  // forward threads/row
   // W tile in LDS: forward [BN rows n][64 k], backward [64 rows n][BN k]
-  static constexpr int PW = BWD ? BN + 16 : G_BK + 8;
+  // backward 256-wide tile: unpadded rows, 16-byte chunks XOR-swizzled
+  static constexpr bool WSWZ = BWD && BN == 256;
+  static constexpr int PW = BWD ? (WSWZ ? BN : BN + 16) : G_BK + 8;
   static constexpr int W_ROWS = BWD ? G_BK : BN;
   static constexpr int W_BYTES = W_ROWS * PW * 2;
   static constexpr int LDS_BYTES = 2 * A_BYTES + 2 * W_BYTES;
@@ -443,6 +461,23 @@ struct WRegs {
   float d;
 };
 
+// Where a thread's dequantized weights go: its 16-byte chunk d (8 weights)
+// is stored at base + 8 * (d ^ x).
+struct WDst {
+  uint16_t* base;
+  int x;
+};
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ WDst gemm_wdst(uint16_t* sW, int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+  if (!BWD) return {sW + (tid / C::TPR) * C::PW + (tid % C::TPR) * C::EPT, 0};
+  const int n = bwd_wrow(tid), b = bwd_wblk(tid);
+  if (!C::WSWZ) return {sW + n * C::PW + b * C::EPT, 0};
+  const int g = wswz(n, 8 * b);
+  return {sW + n * C::PW + 8 * ((8 * b) ^ (g & 8)), g & 7};
+}
+
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_load_w(WRegs& R, rsrc_t rp, rsrc_t rq,
                                             rsrc_t rd, int N, int K, int c0,
@@ -453,8 +488,8 @@ __device__ __forceinline__ void gemm_load_w(WRegs& R, rsrc_t rp, rsrc_t rq,
     n = c0 + tid / C::TPR;           // output column = weight row
     k = red0 + (tid % C::TPR) * C::EPT;
   } else {
-    n = red0 + (tid >> 2);           // reduction index = weight row
-    k = c0 + (tid & 3) * C::EPT;
+    n = red0 + bwd_wrow(tid);        // reduction index = weight row
+    k = c0 + bwd_wblk(tid) * C::EPT;
   }
   const bool ok = n < N && k < K;
   const int64_t e = (int64_t)n * K + k;
@@ -474,14 +509,13 @@ template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_dequant_w(const WRegs& R, uint16_t* sW,
                                                const Codebook& cb, int tid) {
   using C = GemmCfg<BM, BN, BWD>;
-  uint16_t* dst = BWD ? sW + (tid >> 2) * C::PW + (tid & 3) * C::EPT
-                      : sW + (tid / C::TPR) * C::PW + (tid % C::TPR) * C::EPT;
+  const WDst dst = gemm_wdst<BM, BN, BWD>(sW, tid);
   const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
   const uint32_t wd[8] = {R.w0.x, R.w0.y, R.w0.z, R.w0.w,
                           R.w1.x, R.w1.y, R.w1.z, R.w1.w};
 #pragma unroll
   for (int d = 0; d < C::WDW; ++d)
-    *reinterpret_cast<u32x4*>(dst + 8 * d) = decode8(wd[d], t);
+    *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = decode8(wd[d], t);
 }
 
 // A tile of one step straight into LDS: wave w issues 1 KB chunks
@@ -497,7 +531,7 @@ __device__ __forceinline__ void gemm_load_a(rsrc_t ra, char* sA, int M,
   for (int i = 0; i < C::A_LOADS; ++i) {
     const int q = wave + 4 * i;
     const int row = 8 * q + (lane >> 3);
-    const int col = red0 + 8 * ((lane & 7) ^ (row & 7));
+    const int col = red0 + 8 * ((lane & 7) ^ ((row >> 1) & 7));
     const bool ok = m0 + row < M && col < KRED;
     const uint32_t off =
         ok ? (uint32_t)(((int64_t)(m0 + row) * KRED + col) * 2) : G_OOB;
@@ -511,13 +545,15 @@ __device__ __forceinline__ void gemm_load_a(rsrc_t ra, char* sA, int M,
 // ds_read_b64_tr_b16 serves 4 rows: in every group of 16 lanes, lane
 // q = 4j + p addresses row j, columns 4p..4p+3 of the group's 16 columns,
 // and lane q receives column q of the 4 rows.
+template <bool SWZ>
 __device__ __forceinline__ u32x4 lds_read_bT(const uint16_t* sW, int pitch,
                                              int row0, int col0, int lane) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const int grp = lane >> 4, q = lane & 15;
   const int row = row0 + 8 * (grp >> 1) + (q >> 2);
-  const int col = col0 + 16 * (grp & 1) + 4 * (q & 3);
+  int col = col0 + 16 * (grp & 1) + 4 * (q & 3);
+  if (SWZ) col = (((col >> 3) ^ wswz(row, col >> 3)) << 3) | (col & 7);
   const uint16_t* p0 = sW + row * pitch + col;
   const uint16_t* p1 = p0 + 4 * pitch;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -544,7 +580,8 @@ __device__ __forceinline__ void gemm_frags(const char* sA, const uint16_t* sW,
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int r = wm * C::WM + i * 32 + (lane & 31);
-    a[i] = *reinterpret_cast<const u32x4*>(sA + r * 128 + ((chunk ^ (r & 7)) << 4));
+    a[i] = *reinterpret_cast<const u32x4*>(sA + r * 128 +
+                                           ((chunk ^ ((r >> 1) & 7)) << 4));
   }
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) {
@@ -553,73 +590,58 @@ __device__ __forceinline__ void gemm_frags(const char* sA, const uint16_t* sW,
           sW + (wn * C::WN + j * 32 + (lane & 31)) * C::PW + kk * 16 +
           (lane >> 5) * 8);
     else
-      b[j] = lds_read_bT(sW, C::PW, kk * 16, wn * C::WN + j * 32, lane);
+      b[j] = lds_read_bT<C::WSWZ>(sW, C::PW, kk * 16, wn * C::WN + j * 32, lane);
   }
 }
 
-// The four k16 slices of one step; slice kk+1's fragments are read while
-// slice kk's MFMAs run.
+// VALU instructions placed after each MFMA by the interleaving below.
+constexpr int G_VALU_PER_MFMA = 6;
+
+// The four k16 slices of one step with the dequantization of the next weight
+// tile woven in: one decode8 (28 VALU ops and a 16-byte LDS write) after
+// every MPD MFMAs, each group fenced and ordered MFMA / 4 VALU so the VALU
+// work issues in the shadow of the MFMAs instead of after them.
 template <int BM, int BN, bool BWD>
-__device__ __forceinline__ void gemm_mma(
-    const char* sA, const uint16_t* sW, int wm, int wn, int lane,
+__device__ __forceinline__ void gemm_mma_deq(
+    const char* sA, const uint16_t* sW, uint16_t* sWn, const WRegs& R,
+    const Codebook& cb, int wm, int wn, int tid, int lane,
     f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
   using C = GemmCfg<BM, BN, BWD>;
+  constexpr int MPK = C::TM * C::TN;     // MFMAs per k16 slice
+  constexpr int DPK = C::WDW / 4;        // decode8 per k16 slice
+  constexpr int MPD = MPK / DPK;         // MFMAs per decode8
+  static_assert(C::WDW % 4 == 0 && MPK % DPK == 0, "decode split");
+  const WDst dst = gemm_wdst<BM, BN, BWD>(sWn, tid);
+  const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
+  const uint32_t wd[8] = {R.w0.x, R.w0.y, R.w0.z, R.w0.w,
+                          R.w1.x, R.w1.y, R.w1.z, R.w1.w};
   u32x4 a[2][C::TM], b[2][C::TN];
   gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, 0, a[0], b[0]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kk < 3)
       gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, kk + 1, a[(kk + 1) & 1],
                               b[(kk + 1) & 1]);
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
-  }
-}
-
-#ifndef QN_SCHED
-#define QN_SCHED 0
-#endif
-#ifndef QN_DEQ_FIRST
-#define QN_DEQ_FIRST 0
-#endif
-#ifndef QN_VPM
-#define QN_VPM 4
-#endif
-template <int BM, int BN, bool BWD>
-__device__ __forceinline__ void gemm_schedule() {
-  using C = GemmCfg<BM, BN, BWD>;
-  constexpr int RPK = C::DS_READS / 4;         // fragment reads per k16
-  constexpr int MPK = C::MFMAS / 4;            // MFMAs per k16
-#if QN_SCHED == 1
-  __builtin_amdgcn_sched_group_barrier(0x020, C::A_LOADS + 4, 0);  // VMEM rd
-  __builtin_amdgcn_sched_group_barrier(0x100, RPK, 0);             // DS rd
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
     for (int g = 0; g < MPK; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);           // VALU
-      if (kk < 3 && g < RPK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (kk >= 1 && (g & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      const int i = g / C::TN, j = g % C::TN;
+      acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
+      if (g % MPD == MPD - 1) {
+        const int d = kk * DPK + g / MPD;
+        *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = decode8(wd[d], t);
+#pragma unroll
+        for (int h = 0; h < MPD; ++h) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, G_VALU_PER_MFMA, 0);   // VALU
+          if (kk < 3 && h < (C::TM + C::TN) / DPK)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);     // DS write
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-#elif QN_SCHED == 2
-#pragma unroll
-  for (int g = 0; g < C::MFMAS; ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, QN_VPM, 0);
   }
-#elif QN_SCHED == 3
-#pragma unroll
-  for (int g = 0; g < C::MFMAS; ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-  }
-#endif
-  (void)RPK; (void)MPK;
 }
 
 // Maps the linear workgroup index to an output tile so that each XCD (the
@@ -647,14 +669,7 @@ __device__ __forceinline__ void gemm_step(
   WRegs Wn;
   gemm_load_a<BM, BN, BWD>(ra, sAn, M, KRED, m0, (st + 1) * G_BK, wave, lane);
   gemm_load_w<BM, BN, BWD>(Wn, rp, rq, rd, N, K, c0, (st + 2) * G_BK, tid);
-#if QN_DEQ_FIRST
-  gemm_dequant_w<BM, BN, BWD>(Wc, sWn, cb, tid);
-  gemm_mma<BM, BN, BWD>(sAc, sWc, wm, wn, lane, acc);
-#else
-  gemm_mma<BM, BN, BWD>(sAc, sWc, wm, wn, lane, acc);
-  gemm_dequant_w<BM, BN, BWD>(Wc, sWn, cb, tid);
-#endif
-  gemm_schedule<BM, BN, BWD>();
+  gemm_mma_deq<BM, BN, BWD>(sAc, sWc, sWn, Wc, cb, wm, wn, tid, lane, acc);
   __builtin_amdgcn_s_waitcnt(0);   // all counters: loads landed in LDS/regs
   __syncthreads();
   Wc = Wn;
