@@ -376,8 +376,8 @@ def main():
     # per-kernel breakdown (outside the timed region)
     kernels = {}
     for kname, per_step in (("k_fwd_gemm", 1), ("k_bwd_dx_gemm", 1),
-                            ("k_rank_nt", 2), ("k_rank_tn_partial", 2),
-                            ("k_rank_tn_reduce", 2), ("k_transpose_b", 1)):
+                            ("k_rank_stream_t", 1), ("k_rank_stream_dy", 1),
+                            ("k_rank_stream_da", 1), ("k_rank_finish", 3)):
         ms, cnt = kernel_times_ms(capi, kname, step, per_step, 3)
         if ms is not None:
             kernels[kname] = {"avg_ms": ms, "launches_per_step": per_step}

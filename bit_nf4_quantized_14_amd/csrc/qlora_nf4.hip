@@ -15,11 +15,14 @@
 //   k_dequant      packed-nibble stream, 32 weights per thread
 //   k_fwd_gemm     Y = X W'^T (+ s T B^T as extra reduction steps), W'
 //                  dequantized into LDS tile by tile, bf16 MFMA 32x32x16
-//   k_bwd_dx_gemm  dX = dY W' (+ s G A), W' tile dequantized and written
-//                  transposed into LDS
-//   k_rank_nt      out[m][j] = sum_c P[m][c] R[j][c]  (T = X A^T, G = dY B)
-//   k_rank_tn_*    out[c][j] = s sum_m P[m][c] Q[m][j] (dB, dA) as split-M
-//                  partials plus a fixed-order reduction (no atomics)
+//   k_bwd_dx_gemm  dX = dY W' (+ s G A), W' tile dequantized into LDS and
+//                  read transposed
+//   k_rank_stream  one pass over X or dY for the rank-r products: row sums
+//                  (T = X A^T, G = dY B) and column sums (dB = dY^T s T,
+//                  dA = (s G)^T X) as per-block partials
+//   k_rank_finish  fixed-order reduction of those partials (no atomics) and
+//                  the small layout conversions of A, B and T
+//   k_skinny_*     forward for M <= 16 tokens (GEMV over the NF4 weight)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -779,135 +782,117 @@ __global__ __launch_bounds__(256, 1) void k_gemm(
 }
 
 // ---------------------------------------------------------------------------
-// K5a: out[m][j] = sum_c P[m][c] R[j][c] (fp32), M x r output; C % 8 == 0.
-// Optionally also writes the bf16 hi and lo parts of scale*out, zero-padded
-// to rpad = 16 * JT columns (the MFMA operands of the adapter terms).
-// One workgroup per 16 rows; wave w takes the w-th quarter of C and walks it
-// in batches of U 32-wide slices whose loads are all issued before the
-// batch's MFMAs (v_mfma_f32_16x16x32_bf16), so each lane keeps several
-// 16-byte loads in flight.  The four quarters are summed through LDS in a
-// fixed order.  Buffer loads return zeros past the valid rows of P and R.
+// K5: rank-r side products, streamed over one large bf16 operand S [M][C]
+// (X or dY, row-major) in stages of 64 SUB columns:
+//   rows part  prow: P[m][j] = sum_c S[m][c] R[j][c]   (T = X A^T, G = dY B)
+//   cols part  pcol: Q[c][j] = sum_m S[m][c] U[m][j]   (dB = dY^T (s T),
+//                                                       dA^T = X^T (s G))
+// Workgroup (bx, by) owns rows [RM by, RM by + RM) and stages
+// [cpb bx, cpb bx + cpb); its row sums over those stages go to
+// prow[bx][m][j] and its column sums over its rows to pcol[by][c][j]
+// (fp32, rpad = 16 JT columns).  k_rank_finish adds the partials in a fixed
+// order, so results do not depend on scheduling.  The backward's dY is read
+// once for both G and dB.
+//
+// Each stage of S (RM rows) and of R (rpad rows, given [r][C]) goes global
+// -> LDS with buffer_load ... lds into double-buffered tiles of 128-byte
+// rows whose 16-byte chunks are XOR-swizzled by rs_swz(row): the 16 lanes
+// of a ds_read_b128 phase (16 rows) and the 32 lanes of a
+// ds_read_b64_tr_b16 phase (8 rows x 2 chunks) each cover all 64 banks.
+// U (the bf16 hi and lo parts of s T or s G, given transposed [r][ldu]) is
+// staged once per workgroup.  Both parts use v_mfma_f32_16x16x32_bf16: the
+// rows part pairs S rows with R rows, the cols part pairs S columns (read
+// transposed) with U rows; hi and lo are two MFMAs into one accumulator.
+// Buffer loads return zeros outside S, R and U, which covers ragged M, C
+// and r.
 // ---------------------------------------------------------------------------
-template <int JT>
-__global__ __launch_bounds__(256) void k_rank_nt(
-    const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ R,
-    int64_t ldr, int M, int C, int r, float* __restrict__ out, float scale,
-    uint16_t* __restrict__ out_hi, uint16_t* __restrict__ out_lo) {
-  constexpr int U = JT >= 8 ? 1 : 8 / JT;
-  __shared__ float s_red[4][16][JT * 16];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m0 = blockIdx.x * 16;
-  const int row = lane & 15, g = lane >> 4;
-  const int rows = min(16, M - m0);
-  const rsrc_t rp = make_rsrc(P + (int64_t)m0 * ldp, (uint32_t)((int64_t)rows * ldp * 2));
-  const rsrc_t rr = make_rsrc(R, (uint32_t)((int64_t)r * ldr * 2));
-  const int cq = ((C + 127) / 128) * 32;
-  const int cbeg = wave * cq, cend = min(C, cbeg + cq);
-  f32x4 acc[JT];
+enum { RS_ROWS = 1, RS_COLS = 2 };
+
+// RM rows per workgroup, stages of 64 SUB columns, NBUF LDS buffers (NBUF - 1
+// stages in flight): about 32 KB of S per stage for r <= 32, less for the
+// wider adapters whose R and U tiles take more LDS.
+__host__ __device__ constexpr int rs_rm(int mode, int jt) {
+  return mode == RS_ROWS ? 64 : (jt <= 2 ? 256 : 64);
+}
+__host__ __device__ constexpr int rs_sub(int mode, int jt) {
+  return jt >= 8 ? 1 : (jt == 4 ? 2 : (mode == RS_ROWS ? 4 : 1));
+}
+__host__ __device__ constexpr int rs_nbuf(int jt) { return jt >= 16 ? 2 : 3; }
+
+__device__ __forceinline__ int rs_swz(int row) {
+  return (((row >> 3) & 1) << 2) | (((row >> 1) & 1) << 1) | ((row >> 2) & 1);
+}
+
+// NR rows x 64 columns (columns col0.. of rows 0..nvalid-1 of the
+// resource, row pitch ld elements) into a swizzled LDS tile.  Instruction q
+// fills rows 8q..8q+7: lane l writes 16 bytes at tile + 1024 q + 16 l, that
+// is row 8q + l/8, slot l%8, which holds logical chunk (l%8) ^ rs_swz(row).
+template <int NR>
+__device__ __forceinline__ void rs_dma(rsrc_t rs, char* tile, int64_t ld,
+                                       int nvalid, int col0, int C, int wave,
+                                       int lane) {
+  static_assert(NR % 8 == 0, "tile rows");
 #pragma unroll
-  for (int t = 0; t < JT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c0 = cbeg; c0 < cend; c0 += 32 * U) {
-    u32x4 a[U], b[U][JT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 32 * u + 8 * g;
-      const bool ok = c < cend;
-      a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          rp, ok ? (uint32_t)(((int64_t)row * ldp + c) * 2) : G_OOB, 0, 0));
-#pragma unroll
-      for (int t = 0; t < JT; ++t)
-        b[u][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            rr, ok ? (uint32_t)(((int64_t)(16 * t + row) * ldr + c) * 2) : G_OOB,
-            0, 0));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < JT; ++t) acc[t] = mfma16(a[u], b[u][t], acc[t]);
-  }
-#pragma unroll
-  for (int t = 0; t < JT; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) s_red[wave][4 * g + v][t * 16 + row] = acc[t][v];
-  __syncthreads();
-  constexpr int RP = JT * 16;
-  for (int idx = tid; idx < 16 * RP; idx += 256) {
-    const int mi = idx / RP, j = idx % RP;
-    if (mi >= rows) continue;
-    const float v = ((s_red[0][mi][j] + s_red[1][mi][j]) + s_red[2][mi][j]) +
-                    s_red[3][mi][j];
-    if (out != nullptr && j < r) out[(int64_t)(m0 + mi) * r + j] = v;
-    if (out_hi != nullptr) {
-      uint16_t h, l;
-      split_bf16(scale * v, h, l);
-      out_hi[(int64_t)(m0 + mi) * RP + j] = h;
-      out_lo[(int64_t)(m0 + mi) * RP + j] = l;
+  for (int q0 = 0; q0 < NR / 8; q0 += 4) {
+    const int q = q0 + wave;
+    if (q < NR / 8) {
+      const int row = 8 * q + (lane >> 3);
+      const int col = col0 + 8 * ((lane & 7) ^ rs_swz(row));
+      const uint32_t off = (row < nvalid && col < C)
+                               ? (uint32_t)(((int64_t)row * ld + col) * 2)
+                               : G_OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + q * 1024),
+                                               16, off, 0, 0, 0);
     }
   }
 }
 
-// Bt[j][n] = B[n][j]
-__global__ __launch_bounds__(256) void k_transpose_b(
-    const uint16_t* __restrict__ B, int N, int r, uint16_t* __restrict__ Bt) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)N * r) return;
-  const int64_t n = idx / r, j = idx % r;
-  Bt[j * N + n] = B[idx];
+// Same layout, 4 bytes per lane: instruction q fills rows 2q, 2q+1 (lane l
+// writes tile + 256 q + 4 l: row 2q + l/32, dword l%32).  Used for 16-row
+// tiles so that every wave issues the same number of loads.
+template <int NR>
+__device__ __forceinline__ void rs_dma4(rsrc_t rs, char* tile, int64_t ld,
+                                        int nvalid, int col0, int C, int wave,
+                                        int lane) {
+  static_assert(NR % 8 == 0, "tile rows");
+#pragma unroll
+  for (int i = 0; i < NR / 8; ++i) {
+    const int q = wave + 4 * i;
+    const int row = 2 * q + (lane >> 5), d = lane & 31;
+    const int col = col0 + 8 * ((d >> 2) ^ rs_swz(row)) + 2 * (d & 3);
+    const uint32_t off = (row < nvalid && col < C)
+                             ? (uint32_t)(((int64_t)row * ld + col) * 2)
+                             : G_OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + q * 256),
+                                             4, off, 0, 0, 0);
+  }
 }
 
-// dst_hi/dst_lo[m][j] = bf16 hi/lo parts of s * src[m][j] (j < r), zero for
-// r <= j < rpad.
-__global__ __launch_bounds__(256) void k_split_scale(
-    const float* __restrict__ src, int M, int r, int rpad, float s,
-    uint16_t* __restrict__ dst_hi, uint16_t* __restrict__ dst_lo) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)M * rpad) return;
-  const int64_t m = idx / rpad, j = idx % rpad;
-  uint16_t h = 0, l = 0;
-  if (j < r) split_bf16(s * src[m * r + j], h, l);
-  dst_hi[idx] = h;
-  dst_lo[idx] = l;
+// 16 bytes of row `row`, logical chunk lc, of a swizzled tile.
+__device__ __forceinline__ u32x4 rs_read_row(const char* tile, int row, int lc) {
+  return *reinterpret_cast<const u32x4*>(tile + row * 128 +
+                                         ((lc ^ rs_swz(row)) << 4));
 }
 
-// dst[row][j] = src[row * rs + j * cs] for j < r, 0 for r <= j < rpad:
-// pads B [N][r] or transposes A [r][K] into [rows][rpad] bf16.
-__global__ __launch_bounds__(256) void k_gather_pad(
-    const uint16_t* __restrict__ src, int rows, int r, int rpad, int64_t rs,
-    int64_t cs, uint16_t* __restrict__ dst) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)rows * rpad) return;
-  const int64_t row = idx / rpad, j = idx % rpad;
-  dst[idx] = j < r ? src[row * rs + j * cs] : (uint16_t)0;
-}
-
-// ---------------------------------------------------------------------------
-// K5b: split-M partials part[chunk][c][j] = sum_{m in chunk} P[m][c] Q[m][j]
-// with P bf16 [M, C] and Q given as bf16 hi + lo parts [M][16 JT].  One
-// workgroup per 64 columns of C and one chunk of rows; the whole chunk of P
-// and Q is loaded at once (every lane keeps its loads in flight) into LDS in
-// natural row-major layout, and both MFMA operands, which need 8
-// consecutive rows m per lane, come from ds_read_b64_tr_b16.
-// ---------------------------------------------------------------------------
-constexpr int TN_PP = 64 + 8;                 // sP pitch (bf16)
-
-__host__ __device__ constexpr int tn_chunk_rows(int jt) {
-  return jt <= 4 ? 256 : (jt == 8 ? 128 : 64);
-}
-
-// Operand of v_mfma_f32_16x16x32_bf16 whose 8 reduction elements per lane
-// run down a column of a row-major LDS tile: lane l takes column
-// col0 + l % 16, rows row0 + 8 * (l / 16) .. + 7 (two transpose reads).
-__device__ __forceinline__ u32x4 lds_read_tr16x(const uint16_t* base, int pitch,
-                                                int row0, int col0, int lane) {
+// Transposed operand of v_mfma_f32_16x16x32_bf16 from a swizzled tile:
+// lane l gets column col0 + l % 16, rows row0 + 8 (l / 16) .. + 7 (two
+// ds_read_b64_tr_b16; within each 16-lane group, lane q addresses row
+// q / 4 (+ 4), columns 4 (q % 4) .. + 3).
+__device__ __forceinline__ u32x4 rs_read_colT(const char* tile, int row0,
+                                              int col0, int lane) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const int g = lane >> 4, q = lane & 15;
-  const uint16_t* p0 = base + (row0 + 8 * g + (q >> 2)) * pitch + col0 + 4 * (q & 3);
+  const int row = row0 + 8 * g + (q >> 2);
+  const int col = col0 + 4 * (q & 3);
+  const char* p0 = tile + row * 128 +
+                   ((((col >> 3) ^ rs_swz(row)) << 4) | ((col & 7) * 2));
+  const char* p1 = tile + (row + 4) * 128 +
+                   ((((col >> 3) ^ rs_swz(row + 4)) << 4) | ((col & 7) * 2));
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(const_cast<uint16_t*>(p0)));
+      (lds_s16x4*)(const_cast<char*>(p0)));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(const_cast<uint16_t*>(p0 + 4 * pitch)));
+      (lds_s16x4*)(const_cast<char*>(p1)));
   u32x4 v;
   v.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
   v.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
@@ -916,96 +901,329 @@ __device__ __forceinline__ u32x4 lds_read_tr16x(const uint16_t* base, int pitch,
   return v;
 }
 
-template <int JT>
-__global__ __launch_bounds__(256) void k_rank_tn_partial(
-    const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ Qh,
-    const uint16_t* __restrict__ Ql, int M, int C, int r,
-    float* __restrict__ part) {
-  constexpr int MCH = tn_chunk_rows(JT);
-  constexpr int PQ = JT * 16 + 8;             // sQ pitch (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t sP[MCH * TN_PP];
-  __shared__ __attribute__((aligned(16))) uint16_t sQh[MCH * PQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sQl[MCH * PQ];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c0 = blockIdx.x * 64;
-  const int chunk = blockIdx.y;
-  const int mbeg = chunk * MCH;
-  const int rows = min(MCH, M - mbeg);
-  const rsrc_t rp = make_rsrc(P + (int64_t)mbeg * ldp, (uint32_t)((int64_t)rows * ldp * 2));
+template <int MODE, int JT>
+struct RsCfg {
+  static constexpr bool ROWS = (MODE & RS_ROWS) != 0;
+  static constexpr bool COLS = (MODE & RS_COLS) != 0;
+  static constexpr int RM = rs_rm(MODE, JT), SUB = rs_sub(MODE, JT);
+  static constexpr int NBUF = rs_nbuf(JT);
+  static constexpr int RP = 16 * JT, PU = RM + 8, TR = RM / 64;
+  static constexpr int S_BYTES = SUB * RM * 128;
+  static constexpr int R_BYTES = ROWS ? SUB * RP * 128 : 16;
+  static constexpr int U_ELEMS = COLS ? RP * PU : 8;
+  // vector-memory instructions per wave for one stage (the same in every
+  // wave, so a vmcnt immediate can wait for all but the newest stage)
+  static constexpr int DMA = SUB * (RM / 32 + (ROWS ? (RP == 16 ? 2 : RP / 32) : 0));
+  static_assert(DMA < 64, "vmcnt range");
+};
 
-  // P chunk: MCH rows x 64 columns, 16 bytes per lane per load
-  constexpr int PL = MCH * 8 / 256;
-  u32x4 pv[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int idx = tid + 256 * i, mi = idx >> 3, c = c0 + 8 * (idx & 7);
-    pv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        rp, c < C ? (uint32_t)(((int64_t)mi * ldp + c) * 2) : G_OOB, 0, 0));
-  }
-  // Q chunk: bf16 hi and lo rows of RP = 16 JT columns, 16 bytes per load
-  constexpr int RP = JT * 16, QC = RP / 8;             // 16-byte chunks / row
-  constexpr int QL = (MCH * QC + 255) / 256;
-  const rsrc_t rqh = make_rsrc(Qh + (int64_t)mbeg * RP, (uint32_t)(rows * RP * 2));
-  const rsrc_t rql = make_rsrc(Ql + (int64_t)mbeg * RP, (uint32_t)(rows * RP * 2));
-  u32x4 qh[QL], ql[QL];
-#pragma unroll
-  for (int i = 0; i < QL; ++i) {
-    const int idx = tid + 256 * i;
-    const uint32_t off = idx < MCH * QC ? (uint32_t)(idx * 16) : G_OOB;
-    qh[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rqh, off, 0, 0));
-    ql[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rql, off, 0, 0));
-  }
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int idx = tid + 256 * i;
-    *reinterpret_cast<u32x4*>(sP + (idx >> 3) * TN_PP + 8 * (idx & 7)) = pv[i];
-  }
-#pragma unroll
-  for (int i = 0; i < QL; ++i) {
-    const int idx = tid + 256 * i;
-    if (idx < MCH * QC) {
-      const int mi = idx / QC, j = 8 * (idx % QC);
-      *reinterpret_cast<u32x4*>(sQh + mi * PQ + j) = qh[i];
-      *reinterpret_cast<u32x4*>(sQl + mi * PQ + j) = ql[i];
-    }
-  }
-  __syncthreads();
-
-  f32x4 acc[JT];
-#pragma unroll
-  for (int t = 0; t < JT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int s = 0; s < MCH; s += 32) {
-    const u32x4 a = lds_read_tr16x(sP, TN_PP, s, 16 * wave, lane);
-#pragma unroll
-    for (int t = 0; t < JT; ++t) {
-      acc[t] = mfma16(a, lds_read_tr16x(sQh, PQ, s, 16 * t, lane), acc[t]);
-      acc[t] = mfma16(a, lds_read_tr16x(sQl, PQ, s, 16 * t, lane), acc[t]);
-    }
-  }
-  // acc[t][v] = C-tile[c = 16 * wave + 4 * (lane / 16) + v][j = 16 t + lane % 16]
-  const int g = lane >> 4, col = lane & 15;
-#pragma unroll
-  for (int t = 0; t < JT; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int c = c0 + 16 * wave + 4 * g + v, j = 16 * t + col;
-      if (c < C && j < r) part[((int64_t)chunk * C + c) * r + j] = acc[t][v];
-    }
+// Workgroup barrier without the release/acquire fences of __syncthreads:
+// with global stores in flight those fences make every wave wait for its
+// stores (vmcnt(0)) at each barrier.  Callers wait for the LDS traffic that
+// must be visible (RS_WAIT_VM includes lgkmcnt(0)); the signal fences keep
+// the compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// out[c * sc + j * sj] = s * sum_chunk part[chunk][c][j], chunks in order.
-__global__ __launch_bounds__(256) void k_rank_tn_reduce(
-    const float* __restrict__ part, int chunks, int C, int r, float s,
-    float* __restrict__ out, int64_t sc, int64_t sj) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)C * r;
-  if (idx >= total) return;
-  float acc = 0.0f;
-  for (int ch = 0; ch < chunks; ++ch) acc += part[(int64_t)ch * total + idx];
-  const int64_t c = idx / r, j = idx % r;
-  out[c * sc + j * sj] = s * acc;
+// s_waitcnt vmcnt(n) expcnt(7) lgkmcnt(0) (gfx9 encoding)
+#define RS_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
+
+template <int MODE, int JT>
+__device__ __forceinline__ void rs_stage_dma(rsrc_t rs, rsrc_t rr, char* dS,
+                                             char* dR, int64_t C, int nvalid,
+                                             int r, int stage, int wave,
+                                             int lane) {
+  using G = RsCfg<MODE, JT>;
+#pragma unroll
+  for (int u = 0; u < G::SUB; ++u) {
+    const int col0 = (stage * G::SUB + u) * 64;
+    rs_dma<G::RM>(rs, dS + u * G::RM * 128, C, nvalid, col0, (int)C, wave, lane);
+    if (G::ROWS) {
+      if (G::RP == 16)
+        rs_dma4<G::RP>(rr, dR + u * G::RP * 128, C, r, col0, (int)C, wave, lane);
+      else
+        rs_dma<G::RP>(rr, dR + u * G::RP * 128, C, r, col0, (int)C, wave, lane);
+    }
+  }
+}
+
+template <int MODE, int JT>
+__device__ __forceinline__ void rs_stage_compute(
+    const char* sS, const char* sR, const uint16_t* sUh, const uint16_t* sUl,
+    int wave, int lane, f32x4 (&accR)[RsCfg<MODE, JT>::TR][JT],
+    f32x4 (&accC)[RsCfg<MODE, JT>::SUB][JT]) {
+  using G = RsCfg<MODE, JT>;
+#pragma unroll
+  for (int u = 0; u < G::SUB; ++u) {
+    const char* tS = sS + u * G::RM * 128;
+    if (G::ROWS) {
+      const char* tR = sR + u * G::RP * 128;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 b[JT];
+#pragma unroll
+        for (int t = 0; t < JT; ++t)
+          b[t] = rs_read_row(tR, 16 * t + (lane & 15), 4 * s + (lane >> 4));
+#pragma unroll
+        for (int tr = 0; tr < G::TR; ++tr) {
+          const u32x4 a = rs_read_row(
+              tS, wave * (G::RM / 4) + 16 * tr + (lane & 15), 4 * s + (lane >> 4));
+#pragma unroll
+          for (int t = 0; t < JT; ++t) accR[tr][t] = mfma16(a, b[t], accR[tr][t]);
+        }
+      }
+    }
+    if (G::COLS) {
+#pragma unroll
+      for (int t = 0; t < JT; ++t) accC[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int s2 = 0; s2 < G::RM / 32; ++s2) {
+        const u32x4 a = rs_read_colT(tS, 32 * s2, 16 * wave, lane);
+#pragma unroll
+        for (int t = 0; t < JT; ++t) {
+          const int uo = (16 * t + (lane & 15)) * G::PU + 32 * s2 + 8 * (lane >> 4);
+          accC[u][t] = mfma16(a, *reinterpret_cast<const u32x4*>(sUh + uo), accC[u][t]);
+          accC[u][t] = mfma16(a, *reinterpret_cast<const u32x4*>(sUl + uo), accC[u][t]);
+        }
+      }
+    }
+  }
+}
+
+// Column sums of one stage: accC[u][t][v] = Q[c][j] with
+// c = 64 (SUB stage + u) + 16 wave + 4 (l / 16) + v, j = 16 t + l % 16.
+// Buffer stores: columns past C fall outside the range and are dropped, so
+// every wave issues the same stores.
+template <int MODE, int JT>
+__device__ __forceinline__ void rs_store_cols(
+    rsrc_t rc, int stage, int C, int wave, int lane,
+    const f32x4 (&accC)[RsCfg<MODE, JT>::SUB][JT]) {
+  using G = RsCfg<MODE, JT>;
+#pragma unroll
+  for (int u = 0; u < G::SUB; ++u) {
+    const int cb = (stage * G::SUB + u) * 64 + 16 * wave + 4 * (lane >> 4);
+#pragma unroll
+    for (int t = 0; t < JT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = cb + v;
+        const uint32_t off =
+            c < C ? (uint32_t)((c * G::RP + 16 * t + (lane & 15)) * 4) : G_OOB;
+        const float x = accC[u][t][v];   // element copy, then reinterpret
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rc, off, 0, 0);
+      }
+  }
+}
+
+template <int MODE, int JT>
+__global__ __launch_bounds__(256) void k_rank_stream(
+    const uint16_t* __restrict__ S, int M, int C,
+    const uint16_t* __restrict__ R, int r, const uint16_t* __restrict__ Uh,
+    const uint16_t* __restrict__ Ul, int ldu, int cpb,
+    float* __restrict__ prow, float* __restrict__ pcol) {
+  using G = RsCfg<MODE, JT>;
+  // distinct buffers, so the compiler can tell the tile being filled from
+  // the tiles being read
+  __shared__ __attribute__((aligned(16))) char sS0[G::S_BYTES];
+  __shared__ __attribute__((aligned(16))) char sS1[G::S_BYTES];
+  __shared__ __attribute__((aligned(16))) char sS2[G::NBUF > 2 ? G::S_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char sR0[G::R_BYTES];
+  __shared__ __attribute__((aligned(16))) char sR1[G::R_BYTES];
+  __shared__ __attribute__((aligned(16))) char sR2[G::NBUF > 2 ? G::R_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) uint16_t sUh[G::U_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sUl[G::U_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = blockIdx.y * G::RM;
+  const int nvalid = min(G::RM, M - m0);
+  const int nst = (C + 64 * G::SUB - 1) / (64 * G::SUB);
+  const int sb = blockIdx.x * cpb, se = min(nst, sb + cpb);
+  const rsrc_t rs = make_rsrc(S + (int64_t)m0 * C, (uint32_t)((int64_t)nvalid * C * 2));
+  const rsrc_t rr = make_rsrc(R, G::ROWS ? (uint32_t)((int64_t)r * C * 2) : 0u);
+  const rsrc_t rc = make_rsrc(G::COLS ? pcol + (int64_t)blockIdx.y * C * G::RP : nullptr,
+                              G::COLS ? (uint32_t)((int64_t)C * G::RP * 4) : 0u);
+
+  f32x4 accR[G::TR][JT];
+#pragma unroll
+  for (int tr = 0; tr < G::TR; ++tr)
+#pragma unroll
+    for (int t = 0; t < JT; ++t) accR[tr][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accC[G::SUB][JT];
+
+  // U block of this workgroup's rows: [rpad][RM] of the transposed [r][ldu]
+  constexpr int MC = G::RM / 8, UCH = G::RP * MC;
+  constexpr int UL = G::COLS ? UCH / 256 : 0;
+  static_assert(!G::COLS || UCH % 256 == 0, "U staging");
+  u32x4 uh[UL > 0 ? UL : 1], ul[UL > 0 ? UL : 1];
+  if constexpr (G::COLS) {
+    const rsrc_t ruh = make_rsrc(Uh, (uint32_t)((int64_t)r * ldu * 2));
+    const rsrc_t rul = make_rsrc(Ul, (uint32_t)((int64_t)r * ldu * 2));
+#pragma unroll
+    for (int k = 0; k < UL; ++k) {
+      const int i = 256 * k + tid, j = i / MC, m = m0 + 8 * (i % MC);
+      const uint32_t off = (j < r && m < ldu)
+                               ? (uint32_t)(((int64_t)j * ldu + m) * 2) : G_OOB;
+      uh[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ruh, off, 0, 0));
+      ul[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rul, off, 0, 0));
+    }
+  }
+  rs_stage_dma<MODE, JT>(rs, rr, sS0, sR0, C, nvalid, r, sb, wave, lane);
+  const bool two = G::NBUF == 3 && sb + 1 < se;
+  if (two)
+    rs_stage_dma<MODE, JT>(rs, rr, sS1, sR1, C, nvalid, r, sb + 1, wave, lane);
+  if constexpr (G::COLS) {
+#pragma unroll
+    for (int k = 0; k < UL; ++k) {
+      const int i = 256 * k + tid, j = i / MC, mc = i % MC;
+      *reinterpret_cast<u32x4*>(sUh + j * G::PU + 8 * mc) = uh[k];
+      *reinterpret_cast<u32x4*>(sUl + j * G::PU + 8 * mc) = ul[k];
+    }
+  }
+  if (two) RS_WAIT_VM(G::DMA);
+  else RS_WAIT_VM(0);
+  wg_barrier();
+
+  // One stage: store the previous stage's column sums, compute on buffer
+  // `cur`, start the stage NBUF - 1 ahead into buffer `far`, then wait until
+  // the next stage has landed (with three buffers the newest one stays in
+  // flight; its loads are the last ones issued, and loads complete in order).
+#define RS_BODY(I, CS, CR, FS, FR)                                            \
+  do {                                                                        \
+    if (G::COLS && (I) > sb)                                                  \
+      rs_store_cols<MODE, JT>(rc, (I) - 1, C, wave, lane, accC);              \
+    rs_stage_compute<MODE, JT>(CS, CR, sUh, sUl, wave, lane, accR, accC);     \
+    if ((I) + G::NBUF - 1 < se) {                                             \
+      rs_stage_dma<MODE, JT>(rs, rr, FS, FR, C, nvalid, r, (I) + G::NBUF - 1, \
+                             wave, lane);                                     \
+      if (G::NBUF == 3) RS_WAIT_VM(G::DMA);                                   \
+      else RS_WAIT_VM(0);                                                     \
+    } else {                                                                  \
+      RS_WAIT_VM(0);                                                          \
+    }                                                                         \
+    wg_barrier();                                                          \
+  } while (0)
+
+  if constexpr (G::NBUF == 3) {
+    for (int st = sb; st < se; st += 3) {
+      RS_BODY(st, sS0, sR0, sS2, sR2);
+      if (st + 1 < se) RS_BODY(st + 1, sS1, sR1, sS0, sR0);
+      if (st + 2 < se) RS_BODY(st + 2, sS2, sR2, sS1, sR1);
+    }
+  } else {
+    for (int st = sb; st < se; st += 2) {
+      RS_BODY(st, sS0, sR0, sS1, sR1);
+      if (st + 1 < se) RS_BODY(st + 1, sS1, sR1, sS0, sR0);
+    }
+  }
+#undef RS_BODY
+  if (G::COLS) rs_store_cols<MODE, JT>(rc, se - 1, C, wave, lane, accC);
+  if (G::ROWS) {
+    // accR[tr][t][v] = P[m = wave RM/4 + 16 tr + 4 (l / 16) + v][j = 16 t + l % 16]
+    float* dst = prow + ((int64_t)blockIdx.x * M + m0) * G::RP;
+#pragma unroll
+    for (int tr = 0; tr < G::TR; ++tr)
+#pragma unroll
+      for (int t = 0; t < JT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = wave * (G::RM / 4) + 16 * tr + 4 * (lane >> 4) + v;
+          if (m < nvalid) dst[(int64_t)m * G::RP + 16 * t + (lane & 15)] = accR[tr][t][v];
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_rank_finish: up to four small jobs in one launch, one thread per output
+// element, blocks [0, nbR) rows job, then cols, pad1, pad2.
+//  rows: v[m][j] = sum_b src[b bstride + m ld + j] (b in order; 0 for
+//        j >= jvalid and for M <= m < Mp) -> out[m][jvalid] = v,
+//        hi/lo[m][rpad] and hiT/loT[jvalid][Mp] = bf16 hi/lo of scale v;
+//  cols: out[c sc + j sj] = sum_b src[(b C + c) rpad + j]  (j < r);
+//  pad:  dst[row dw + col] = col < valid ? src[row rs + col cs] : 0.
+// ---------------------------------------------------------------------------
+struct FinishRows {
+  const float* src;
+  int64_t bstride;
+  int ld, nb, M, Mp, jvalid, rpad;
+  float scale;
+  float* out;
+  uint16_t *hi, *lo, *hiT, *loT;
+};
+struct FinishCols {
+  const float* src;
+  int nb, C, r, rpad;
+  float* out;
+  int64_t sc, sj;
+};
+struct FinishPad {
+  const uint16_t* src;
+  uint16_t* dst;
+  int rows, dw, valid;
+  int64_t rs, cs;
+};
+struct FinishArgs {
+  FinishRows R;
+  FinishCols Cc;
+  FinishPad P1, P2;
+  int nbR, nbC, nbP1, nbP2;
+};
+
+__device__ __forceinline__ void finish_pad(const FinishPad& p, int64_t idx) {
+  if (idx >= (int64_t)p.rows * p.dw) return;
+  const int64_t row = idx / p.dw, col = idx % p.dw;
+  p.dst[idx] = col < p.valid ? p.src[row * p.rs + col * p.cs] : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
+  int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (b < a.nbR) {
+    const FinishRows& p = a.R;
+    const int64_t idx = (int64_t)b * 256 + tid;
+    if (idx >= (int64_t)p.Mp * p.rpad) return;
+    const int m = (int)(idx / p.rpad), j = (int)(idx % p.rpad);
+    float v = 0.0f;
+    if (m < p.M && j < p.jvalid)
+      for (int k = 0; k < p.nb; ++k)
+        v += p.src[k * p.bstride + (int64_t)m * p.ld + j];
+    uint16_t h, l;
+    split_bf16(p.scale * v, h, l);
+    if (m < p.M) {
+      if (p.out != nullptr && j < p.jvalid) p.out[(int64_t)m * p.jvalid + j] = v;
+      if (p.hi != nullptr) {
+        p.hi[(int64_t)m * p.rpad + j] = h;
+        p.lo[(int64_t)m * p.rpad + j] = l;
+      }
+    }
+    if (p.hiT != nullptr && j < p.jvalid) {
+      p.hiT[(int64_t)j * p.Mp + m] = h;
+      p.loT[(int64_t)j * p.Mp + m] = l;
+    }
+    return;
+  }
+  b -= a.nbR;
+  if (b < a.nbC) {
+    const FinishCols& p = a.Cc;
+    const int64_t idx = (int64_t)b * 256 + tid;
+    if (idx >= (int64_t)p.C * p.r) return;
+    const int64_t c = idx / p.r, j = idx % p.r;
+    float v = 0.0f;
+    for (int k = 0; k < p.nb; ++k)
+      v += p.src[((int64_t)k * p.C + c) * p.rpad + j];
+    p.out[c * p.sc + j * p.sj] = v;
+    return;
+  }
+  b -= a.nbC;
+  if (b < a.nbP1) {
+    finish_pad(a.P1, (int64_t)b * 256 + tid);
+    return;
+  }
+  b -= a.nbP1;
+  if (b < a.nbP2) finish_pad(a.P2, (int64_t)b * 256 + tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1228,6 +1446,14 @@ bool valid_tensor(const nf4_tensor* w) {
          aligned16(w->packed);
 }
 
+// Rank-tile dispatch: JT = number of 16-wide tiles of r, rounded up to a
+// power of two (1, 2, 4, 8, 16 covers r <= 256); rpad = 16 JT.
+int rank_tiles(int r) {
+  int jt = 1;
+  while (jt * 16 < r) jt *= 2;
+  return jt;
+}
+
 bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
   if (!valid_tensor(w) || M <= 0) return false;
   if (r < 1 || r > QN_MAX_RANK) return false;
@@ -1239,6 +1465,8 @@ bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
   // "out of range"): every operand read through one stays below 2 GiB
   const int64_t lim = 1LL << 31;
   if (M * K * 2 >= lim || M * N * 2 >= lim || N * K / 2 >= lim) return false;
+  // fp32 rank-r partial rows [N or K][rpad] addressed through a resource
+  if (std::max(N, K) * 4 * 16 * rank_tiles(r) >= lim) return false;
   return true;
 }
 
@@ -1303,13 +1531,6 @@ void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                                  out_bf16);
 }
 
-// Rank-tile dispatch: JT = number of 16-wide tiles of r, rounded up to a
-// power of two (1, 2, 4, 8, 16 covers r <= 256); rpad = 16 JT.
-int rank_tiles(int r) {
-  int jt = 1;
-  while (jt * 16 < r) jt *= 2;
-  return jt;
-}
 
 #define QN_RANK_DISPATCH(r, CALL)                \
   switch (rank_tiles(r)) {                       \
@@ -1320,22 +1541,52 @@ int rank_tiles(int r) {
     default: { constexpr int JT = 16; CALL; break; } \
   }
 
-void launch_rank_nt(hipStream_t st, const uint16_t* P, int64_t ldp,
-                    const uint16_t* R, int64_t ldr, int M, int C, int r,
-                    float* out, float scale, uint16_t* hi, uint16_t* lo) {
-  const dim3 grid((unsigned)cdiv(M, 16));
-  QN_RANK_DISPATCH(r, QN_LAUNCH("k_rank_nt", k_rank_nt<JT>, grid, dim3(256),
-                                st, P, ldp, R, ldr, M, C, r, out, scale, hi,
-                                lo));
+// Rank-stream geometry: RM rows per workgroup, stages of 64 SUB columns,
+// and enough column blocks for one long-lived workgroup per CU (each keeps
+// two stages in flight).
+struct StreamPlan {
+  int rm, sub, mb, nb, cpb;
+};
+
+StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt) {
+  StreamPlan P;
+  P.rm = rs_rm(mode, jt);
+  P.sub = rs_sub(mode, jt);
+  P.mb = (int)cdiv(M, P.rm);
+  const int64_t nst = cdiv(C, 64 * P.sub);
+  const int64_t want = std::max<int64_t>(1, cdiv(256, P.mb));
+  const int64_t nb = std::min(nst, want);
+  P.cpb = (int)cdiv(nst, nb);
+  P.nb = (int)cdiv(nst, P.cpb);
+  return P;
 }
 
-void launch_rank_tn(hipStream_t st, const uint16_t* P, int64_t ldp,
-                    const uint16_t* Qh, const uint16_t* Ql, int M, int C,
-                    int r, int chunks, float* part) {
-  const dim3 grid((unsigned)cdiv(C, 64), (unsigned)chunks);
-  QN_RANK_DISPATCH(r, QN_LAUNCH("k_rank_tn_partial", k_rank_tn_partial<JT>,
-                                grid, dim3(256), st, P, ldp, Qh, Ql, M, C, r,
-                                part));
+template <int MODE>
+void launch_rank_stream(hipStream_t st, const char* kname, const StreamPlan& P,
+                        const uint16_t* S, int M, int C, const uint16_t* R,
+                        int r, const uint16_t* Uh, const uint16_t* Ul, int ldu,
+                        float* prow, float* pcol) {
+  const dim3 grid((unsigned)P.nb, (unsigned)P.mb);
+  QN_RANK_DISPATCH(r, QN_LAUNCH(kname, (k_rank_stream<MODE, JT>), grid,
+                                dim3(256), st, S, M, C, R, r, Uh, Ul, ldu,
+                                P.cpb, prow, pcol));
+}
+
+FinishArgs finish_args() {
+  FinishArgs a;
+  std::memset(&a, 0, sizeof(a));
+  return a;
+}
+
+void launch_finish(hipStream_t st, FinishArgs& a) {
+  a.nbR = a.R.src != nullptr ? (int)cdiv((int64_t)a.R.Mp * a.R.rpad, 256) : 0;
+  a.nbC = a.Cc.src != nullptr ? (int)cdiv((int64_t)a.Cc.C * a.Cc.r, 256) : 0;
+  a.nbP1 = a.P1.src != nullptr ? (int)cdiv((int64_t)a.P1.rows * a.P1.dw, 256) : 0;
+  a.nbP2 = a.P2.src != nullptr ? (int)cdiv((int64_t)a.P2.rows * a.P2.dw, 256) : 0;
+  const int nblk = a.nbR + a.nbC + a.nbP1 + a.nbP2;
+  if (nblk > 0)
+    QN_LAUNCH("k_rank_finish", k_rank_finish, dim3((unsigned)nblk), dim3(256),
+              st, a);
 }
 
 // Skinny path plan: K slices of ks columns (multiple of 256, <= 2048),
@@ -1382,6 +1633,7 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
     L.total = align256(size_t(P.slices) * 16 * P.rows_total * 4);
     return L;
   }
+  const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r));
   size_t off = 0;
   L.th = off;
   off += align256(size_t(M) * L.rpad * 2);
@@ -1389,6 +1641,8 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
   off += align256(size_t(M) * L.rpad * 2);
   L.bp = off;
   off += align256(size_t(N) * L.rpad * 2);
+  L.prow = off;
+  off += align256(size_t(P.nb) * M * L.rpad * 4);
   L.total = off;
   return L;
 }
@@ -1396,25 +1650,33 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
 BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K,
                                   int32_t r) {
   BwdWorkspace L{};
-  L.rpad = 16 * rank_tiles(r);
-  L.chunks = cdiv(M, tn_chunk_rows(rank_tiles(r)));
+  const int jt = rank_tiles(r);
+  L.rpad = 16 * jt;
+  L.mp = cdiv(M, 8) * 8;
+  const StreamPlan Pg = stream_plan(RS_ROWS | RS_COLS, M, N, jt);
+  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
+  const size_t pcol = std::max(size_t(Pg.mb) * N, size_t(Pa.mb) * K);
   size_t off = 0;
   L.bt = off;
   off += align256(size_t(r) * N * 2);
+  L.uth = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.utl = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.atp = off;
+  off += align256(size_t(K) * L.rpad * 2);
   L.gh = off;
   off += align256(size_t(M) * L.rpad * 2);
   L.gl = off;
   off += align256(size_t(M) * L.rpad * 2);
-  L.th = off;
-  off += align256(size_t(M) * L.rpad * 2);
-  L.tl = off;
-  off += align256(size_t(M) * L.rpad * 2);
-  L.atp = off;
-  off += align256(size_t(K) * L.rpad * 2);
-  L.part_db = off;
-  off += align256(size_t(L.chunks) * N * r * 4);
-  L.part_da = off;
-  off += align256(size_t(L.chunks) * K * r * 4);
+  L.ugh = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.ugl = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.prow = off;
+  off += align256(size_t(Pg.nb) * M * L.rpad * 4);
+  L.pcol = off;
+  off += align256(pcol * L.rpad * 4);
   L.total = off;
   return L;
 }
@@ -1530,10 +1792,18 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   uint16_t* Th = ws_at<uint16_t>(ws, L.th);
   uint16_t* Tl = ws_at<uint16_t>(ws, L.tl);
   uint16_t* Bp = ws_at<uint16_t>(ws, L.bp);
-  // T = X A^T (fp32, saved) and the hi/lo parts of s T
-  launch_rank_nt(st, x, K, A, K, Mi, Ki, (int)r, t_save, s, Th, Tl);
-  QN_LAUNCH("k_gather_pad", k_gather_pad, dim3((unsigned)cdiv(N * L.rpad, 256)),
-            dim3(256), st, B, Ni, (int)r, L.rpad, (int64_t)r, (int64_t)1, Bp);
+  float* prow = ws_at<float>(ws, L.prow);
+  const int jt = rank_tiles(r);
+  // T = X A^T: partials over column blocks of X
+  const StreamPlan P = stream_plan(RS_ROWS, M, K, jt);
+  launch_rank_stream<RS_ROWS>(st, "k_rank_stream_t", P, x, Mi, Ki, A, (int)r,
+                              nullptr, nullptr, 0, prow, nullptr);
+  // T (fp32, saved), hi/lo parts of s T, B zero-padded to [N][rpad]
+  FinishArgs fa = finish_args();
+  fa.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, P.nb, Mi, Mi, (int)r,
+                    L.rpad, s, t_save, Th, Tl, nullptr, nullptr};
+  fa.P1 = FinishPad{B, Bp, Ni, L.rpad, (int)r, (int64_t)r, (int64_t)1};
+  launch_finish(st, fa);
   launch_gemm<false>(st, x, w, Th, Tl, Bp, Mi, L.rpad, y,
                      (int)(y_dtype == QN_BF16));
   return check_launch();
@@ -1557,40 +1827,48 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
   if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
     return QN_EWORKSPACE;
   uint16_t* Bt = ws_at<uint16_t>(ws, L.bt);
+  uint16_t* UTh = ws_at<uint16_t>(ws, L.uth);
+  uint16_t* UTl = ws_at<uint16_t>(ws, L.utl);
+  uint16_t* Atp = ws_at<uint16_t>(ws, L.atp);
   uint16_t* Gh = ws_at<uint16_t>(ws, L.gh);
   uint16_t* Gl = ws_at<uint16_t>(ws, L.gl);
-  uint16_t* Th = ws_at<uint16_t>(ws, L.th);
-  uint16_t* Tl = ws_at<uint16_t>(ws, L.tl);
-  uint16_t* Atp = ws_at<uint16_t>(ws, L.atp);
-  float* part_db = ws_at<float>(ws, L.part_db);
-  float* part_da = ws_at<float>(ws, L.part_da);
+  uint16_t* UGh = ws_at<uint16_t>(ws, L.ugh);
+  uint16_t* UGl = ws_at<uint16_t>(ws, L.ugl);
+  float* prow = ws_at<float>(ws, L.prow);
+  float* pcol = ws_at<float>(ws, L.pcol);
   const float s = alpha / (float)r;
-  const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K, Mp = (int)L.mp;
+  const int jt = rank_tiles(r);
   hipStream_t st = (hipStream_t)stream;
 
-  QN_LAUNCH("k_transpose_b", k_transpose_b, dim3((unsigned)cdiv(N * r, 256)),
-            dim3(256), st, B, Ni, (int)r, Bt);
-  // hi/lo parts of s G, G = dY B
-  launch_rank_nt(st, dy, N, Bt, N, Mi, Ni, (int)r, nullptr, s, Gh, Gl);
-  // hi/lo parts of s T
-  QN_LAUNCH("k_split_scale", k_split_scale, dim3((unsigned)cdiv(M * L.rpad, 256)),
-            dim3(256), st, t_saved, Mi, (int)r, L.rpad, s, Th, Tl);
-  // A^T padded to [K][rpad] for the dX adapter term
-  QN_LAUNCH("k_gather_pad", k_gather_pad, dim3((unsigned)cdiv(K * L.rpad, 256)),
-            dim3(256), st, A, Ki, (int)r, L.rpad, (int64_t)1, K, Atp);
-  // dB = dY^T (s T)
-  launch_rank_tn(st, dy, N, Th, Tl, Mi, Ni, (int)r, (int)L.chunks, part_db);
-  QN_LAUNCH("k_rank_tn_reduce", k_rank_tn_reduce,
-            dim3((unsigned)cdiv(N * r, 256)), dim3(256), st, part_db,
-            (int)L.chunks, Ni, (int)r, 1.0f, dB, (int64_t)r, (int64_t)1);
+  // s T transposed (hi/lo), A^T padded to [K][rpad], B^T
+  FinishArgs f0 = finish_args();
+  f0.R = FinishRows{t_saved, 0, (int)r, 1, Mi, Mp, (int)r, L.rpad, s,
+                    nullptr, nullptr, nullptr, UTh, UTl};
+  f0.P1 = FinishPad{A, Atp, Ki, L.rpad, (int)r, (int64_t)1, K};
+  f0.P2 = FinishPad{B, Bt, (int)r, Ni, Ni, (int)1, (int64_t)r};
+  launch_finish(st, f0);
+  // one pass over dY: G = dY B (column-block partials), dB = dY^T (s T)
+  // (row-block partials)
+  const StreamPlan Pg = stream_plan(RS_ROWS | RS_COLS, M, N, jt);
+  launch_rank_stream<RS_ROWS | RS_COLS>(st, "k_rank_stream_dy", Pg, dy, Mi, Ni,
+                                        Bt, (int)r, UTh, UTl, Mp, prow, pcol);
+  // hi/lo parts of s G (row-major and transposed), dB
+  FinishArgs f1 = finish_args();
+  f1.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, Pg.nb, Mi, Mp, (int)r,
+                    L.rpad, s, nullptr, Gh, Gl, UGh, UGl};
+  f1.Cc = FinishCols{pcol, Pg.mb, Ni, (int)r, L.rpad, dB, (int64_t)r, 1};
+  launch_finish(st, f1);
   // dX = dY W' + (s G) A
   launch_gemm<true>(st, dy, w, Gh, Gl, Atp, Mi, L.rpad, dx,
                     (int)(dx_dtype == QN_BF16));
-  // dA = (s G)^T X  (out[k][j] -> dA[j][k])
-  launch_rank_tn(st, x, K, Gh, Gl, Mi, Ki, (int)r, (int)L.chunks, part_da);
-  QN_LAUNCH("k_rank_tn_reduce", k_rank_tn_reduce,
-            dim3((unsigned)cdiv(K * r, 256)), dim3(256), st, part_da,
-            (int)L.chunks, Ki, (int)r, 1.0f, dA, (int64_t)1, K);
+  // dA = (s G)^T X: row-block partials of out[k][j] -> dA[j][k]
+  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
+  launch_rank_stream<RS_COLS>(st, "k_rank_stream_da", Pa, x, Mi, Ki, nullptr,
+                              (int)r, UGh, UGl, Mp, nullptr, pcol);
+  FinishArgs f2 = finish_args();
+  f2.Cc = FinishCols{pcol, Pa.mb, Ki, (int)r, L.rpad, dA, (int64_t)1, K};
+  launch_finish(st, f2);
   return check_launch();
 }
 

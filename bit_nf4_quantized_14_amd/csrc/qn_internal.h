@@ -19,6 +19,7 @@ constexpr int64_t QN_SKINNY_M = 16;
 struct FwdWorkspace {
   size_t th, tl;    // bf16 [M, rpad]  hi/lo parts of s*T      (GEMM path)
   size_t bp;        // bf16 [N, rpad]  B zero-padded           (GEMM path)
+  size_t prow;      // fp32 [nb, M, rpad] column-block partials of T
   size_t part;      // fp32 [slices, 16, rows] K-slice partials (skinny path)
   int32_t slices, ks;
   size_t total;
@@ -27,13 +28,14 @@ struct FwdWorkspace {
 
 struct BwdWorkspace {
   size_t bt;        // bf16 [r, N]     B transposed
-  size_t gh, gl;    // bf16 [M, rpad]  hi/lo parts of s*G, G = dY B
-  size_t th, tl;    // bf16 [M, rpad]  hi/lo parts of s*T
+  size_t uth, utl;  // bf16 [r, Mp]    hi/lo parts of s*T, transposed
   size_t atp;       // bf16 [K, rpad]  A transposed, zero-padded
-  size_t part_db;   // fp32 [chunks, N, r] split-M partials of dY^T (s T)
-  size_t part_da;   // fp32 [chunks, K, r] split-M partials of (s G)^T X
+  size_t gh, gl;    // bf16 [M, rpad]  hi/lo parts of s*G, G = dY B
+  size_t ugh, ugl;  // bf16 [r, Mp]    hi/lo parts of s*G, transposed
+  size_t prow;      // fp32 [nb, M, rpad] column-block partials of G
+  size_t pcol;      // fp32 [mb, max(N, K), rpad] row-block partials of dB, dA
   size_t total;
-  int64_t chunks;   // number of M chunks
+  int64_t mp;       // M rounded up to a multiple of 8
   int32_t rpad;
 };
 
