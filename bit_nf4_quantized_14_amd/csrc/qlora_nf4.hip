@@ -383,29 +383,31 @@ __device__ __forceinline__ void store_out(void* out, int out_bf16,
 //   forward  (BWD = false): Y[M,N]  = X[M,K]  W'^T  + (s T) B^T
 //   backward (BWD = true) : dX[M,K] = dY[M,N] W'    + (s G) A
 //
-// Output tile BM x BN, reduction step 64, 256 threads = 4 waves in a 2 x 2
-// arrangement, each wave owning (BM/2) x (BN/2) of the output as
-// (BM/64) x (BN/64) tiles of v_mfma_f32_32x32x16_bf16 with fp32
-// accumulators.
+// Output tile BM x BN, reduction step 64.  The 256 x 256 tile runs 8 waves
+// (2 x 4, two waves per SIMD, 128 x 64 of the output each), the 128 x 128
+// tile 4 waves (2 x 2, 64 x 64 each), as tiles of v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators.  With two waves on a SIMD, one wave's LDS writes,
+// buffer loads and dequantization issue while the other's MFMAs run; a
+// single wave has to issue all of them between its own MFMAs.
 //
 // Per reduction step:
-//  * the A tile (X or dY rows, bf16) goes global -> LDS directly
-//    (buffer_load ... lds, 1 KB per wave instruction), 128-byte rows with
-//    the 16-byte chunk index XOR-swizzled by (row / 2) & 7: the 16 lanes
-//    of one ds_read_b128 phase (16 rows) cover all 64 LDS banks;
-//  * the weight tile arrives as packed nibbles + 8-bit block codes + group
-//    scales in registers and each thread dequantizes BN/4 weights of one
-//    64-weight block (per-block v_perm LUT) into LDS, row-major.  The
-//    forward reads W' rows as MFMA B operands with ds_read_b128 (rows padded
-//    to 144 bytes); the backward reads W' columns with ds_read_b64_tr_b16
-//    from unpadded rows whose 16-byte chunks are XOR-swizzled (wswz).
+//  * the A tile (X or dY rows, bf16) is loaded into registers (16 bytes per
+//    thread per chunk) and written to LDS after the step's MFMAs: 128-byte
+//    rows with the 16-byte chunk index XOR-swizzled by (row / 2) & 7, so the
+//    16 lanes of one ds_read_b128 phase (16 rows) cover all 64 LDS banks;
+//  * the weight tile arrives as packed nibbles (16 bytes = 32 weights per
+//    thread) + the 8-bit block code + the group scale in registers; each
+//    thread builds its block's 16-entry bf16 LUT (v_perm) and dequantizes
+//    into LDS.  Forward: W' [BN rows n][64 k], 128-byte rows, swizzled like
+//    A, read as MFMA B operands with ds_read_b128.  Backward: W' [64 rows
+//    n][BN k], chunks XOR-swizzled by bwd_swz, read column-wise with
+//    ds_read_b64_tr_b16.
 // LDS is double-buffered.  While the MFMAs consume step i, the A tile of
 // step i+1 streams into the other buffer and the weight tile of step i+1
 // (loaded one step earlier) is dequantized into it; the dequantization is
 // woven between the MFMAs in fenced groups (one MFMA, then up to six VALU
-// ops), so it runs while the matrix core is busy.  Global loads go
-// through buffer resources whose range check returns zeros, which covers
-// ragged M, N and K tiles without branches.
+// ops).  Global loads go through buffer resources whose range check returns
+// zeros, which covers ragged M, N and K tiles without branches.
 // The adapter term is 2r extra reduction steps with the A side s*T (or s*G)
 // split into bf16 hi + lo parts, so the fp32 intermediate keeps ~16
 // mantissa bits.
@@ -422,44 +424,39 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            (int)bytes, G_RSRC_FLAGS);
 }
 
-// Backward weight tile: thread -> (weight row within the step, block of EPT
-// output columns).
-__device__ __forceinline__ int bwd_wrow(int tid) { return tid >> 2; }
-__device__ __forceinline__ int bwd_wblk(int tid) { return tid & 3; }
-
-// XOR applied to the 16-byte chunk index c of row n of the 64 x 256 backward
-// weight tile.  With it, the 16 lanes of a ds_write_b128 phase (4 rows x 4
-// column blocks of 64) and the 32 lanes of a ds_read_b64_tr_b16 phase
-// (4 rows x 4 chunks) each cover all 64 LDS banks.
-__device__ __forceinline__ int wswz(int n, int c) {
-  const int r = n & 3, h = (c >> 4) & 1;
-  return ((r >> 1) << 3) | ((r & 1) << 2) | (h << 1) | (r >> 1);
-}
-
 template <int BM, int BN, bool BWD>
 struct GemmCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;        // per-wave tile
-  static constexpr int TM = WM / 32, TN = WN / 32;      // MFMA tiles per wave
-  static constexpr int A_BYTES = BM * 128;              // swizzled, unpadded
-  static constexpr int A_LOADS = BM / 32;               // 1 KB loads per wave
-  static constexpr int EPT = BN / 4;                    // weights per thread
-  static constexpr int WDW = EPT / 8;                   // packed dwords
-  static constexpr int TPR = 64 / EPT;                  // forward threads/row
-  // W tile in LDS: forward [BN rows n][64 k], backward [64 rows n][BN k]
-  // backward 256-wide tile: unpadded rows, 16-byte chunks XOR-swizzled
-  static constexpr bool WSWZ = BWD && BN == 256;
-  static constexpr int PW = BWD ? (WSWZ ? BN : BN + 16) : G_BK + 8;
-  static constexpr int W_ROWS = BWD ? G_BK : BN;
-  static constexpr int W_BYTES = W_ROWS * PW * 2;
-  static constexpr int LDS_BYTES = 2 * A_BYTES + 2 * W_BYTES;
-  static constexpr int MFMAS = 4 * TM * TN;             // per step per wave
-  static constexpr int DS_READS = 4 * (TM + (BWD ? 2 : 1) * TN);
+  static constexpr int WAVES_M = 2, WAVES_N = BN == 256 ? 4 : 2;
+  static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // per-wave tile
+  static constexpr int TM = WM / 32, TN = WN / 32;             // MFMA tiles
+  static constexpr int A_BYTES = BM * 128;                     // swizzled
+  static constexpr int A_CHUNKS = BM * 8 / NT;                 // 16 B per thread
+  static constexpr int EPT = 64 * BN / NT;                     // weights/thread
+  static constexpr int WDW = EPT / 8;                          // packed dwords
+  // threads per weight row: forward rows are 64 weights, backward rows BN
+  static constexpr int TPR = BWD ? BN / EPT : 64 / EPT;
+  static constexpr int PW = BWD ? BN : G_BK;                   // row pitch
+  static constexpr int W_BYTES = 64 * BN * 2;
+  static constexpr int MFMAS = 4 * TM * TN;                    // per step
+  static_assert(EPT == 32 && WDW == 4, "one 16-byte load per thread");
+  static_assert(A_CHUNKS * NT == BM * 8, "A tile loads");
+  static_assert(NT == (BN == 256 ? 512 : 256), "k_gemm launch bounds");
 };
 
-// Packed weight bytes of one step for one thread, plus its block code and
-// group scale (raw; c' = q * d is formed when the tile is dequantized).
+// XOR for the 16-byte chunk index c of row r of the backward weight tile
+// [64][BN]: the 16 lanes of a ds_write_b128 phase and the 32 lanes of a
+// ds_read_b64_tr_b16 phase each cover all 64 LDS banks.
+template <int BN>
+__device__ __forceinline__ int bwd_swz(int r, int c) {
+  return BN == 256 ? 4 * (r & 3) + 2 * (r & 1) + ((c >> 4) & 1) : 5 * (r & 3);
+}
+
+// Packed weight bytes of one step for one thread (32 weights), plus its
+// block code and group scale (raw; c' = q * d is formed when the tile is
+// dequantized).
 struct WRegs {
-  u32x4 w0, w1;
+  u32x4 w;
   uint32_t q;
   float d;
 };
@@ -474,11 +471,10 @@ struct WDst {
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ WDst gemm_wdst(uint16_t* sW, int tid) {
   using C = GemmCfg<BM, BN, BWD>;
-  if (!BWD) return {sW + (tid / C::TPR) * C::PW + (tid % C::TPR) * C::EPT, 0};
-  const int n = bwd_wrow(tid), b = bwd_wblk(tid);
-  if (!C::WSWZ) return {sW + n * C::PW + b * C::EPT, 0};
-  const int g = wswz(n, 8 * b);
-  return {sW + n * C::PW + 8 * ((8 * b) ^ (g & 8)), g & 7};
+  const int row = tid / C::TPR, c0 = (tid % C::TPR) * (C::EPT / 8);
+  const int x = BWD ? bwd_swz<BN>(row, c0) : ((row >> 1) & 7);
+  // c0 is a multiple of 4 and d < 4: (c0 + d) ^ x = (c0 ^ (x & ~3)) + (d ^ (x & 3))
+  return {sW + row * C::PW + 8 * (c0 ^ (x & ~3)), x & 3};
 }
 
 template <int BM, int BN, bool BWD>
@@ -491,19 +487,15 @@ __device__ __forceinline__ void gemm_load_w(WRegs& R, rsrc_t rp, rsrc_t rq,
     n = c0 + tid / C::TPR;           // output column = weight row
     k = red0 + (tid % C::TPR) * C::EPT;
   } else {
-    n = red0 + bwd_wrow(tid);        // reduction index = weight row
-    k = c0 + bwd_wblk(tid) * C::EPT;
+    n = red0 + tid / C::TPR;         // reduction index = weight row
+    k = c0 + (tid % C::TPR) * C::EPT;
   }
   const bool ok = n < N && k < K;
   const int64_t e = (int64_t)n * K + k;
   const uint32_t op = ok ? (uint32_t)(e >> 1) : G_OOB;
   const uint32_t ob = ok ? (uint32_t)(e >> 6) : G_OOB;
   const uint32_t og = ok ? (uint32_t)((e >> 14) << 2) : G_OOB;
-  R.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op, 0, 0));
-  if (C::WDW == 8)
-    R.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op + 16, 0, 0));
-  else
-    R.w1 = u32x4{0u, 0u, 0u, 0u};
+  R.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op, 0, 0));
   R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, ob, 0, 0);
   R.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, og, 0, 0));
 }
@@ -511,35 +503,49 @@ __device__ __forceinline__ void gemm_load_w(WRegs& R, rsrc_t rp, rsrc_t rq,
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_dequant_w(const WRegs& R, uint16_t* sW,
                                                const Codebook& cb, int tid) {
-  using C = GemmCfg<BM, BN, BWD>;
   const WDst dst = gemm_wdst<BM, BN, BWD>(sW, tid);
   const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
-  const uint32_t wd[8] = {R.w0.x, R.w0.y, R.w0.z, R.w0.w,
-                          R.w1.x, R.w1.y, R.w1.z, R.w1.w};
+  const uint32_t wd[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
 #pragma unroll
-  for (int d = 0; d < C::WDW; ++d)
+  for (int d = 0; d < 4; ++d)
     *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = decode8(wd[d], t);
 }
 
-// A tile of one step straight into LDS: wave w issues 1 KB chunks
-// q = w, w+4, ...; chunk q holds rows 8q..8q+7, and lane l of the
-// instruction fills row 8q + l/8, slot l%8, with global 16-byte chunk
-// (l%8) ^ (row & 7).
+// A tile of one step: 16-byte global loads into registers (thread t takes
+// chunks q = t + NT i; chunk q is row q / 8, 16-byte column q % 8, so eight
+// consecutive lanes read one 128-byte row segment), written to LDS after the
+// step's MFMAs at the row's swizzled slot (q % 8) ^ ((row / 2) & 7).
+// (A buffer_load ... lds per 1 KB costs the issuing SIMD far more than a
+// load plus a ds_write_b128.)
 template <int BM, int BN, bool BWD>
-__device__ __forceinline__ void gemm_load_a(rsrc_t ra, char* sA, int M,
-                                            int KRED, int m0, int red0,
-                                            int wave, int lane) {
+struct ARegs {
+  u32x4 v[GemmCfg<BM, BN, BWD>::A_CHUNKS];
+};
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_load_a(ARegs<BM, BN, BWD>& R, rsrc_t ra,
+                                            int M, int KRED, int m0, int red0,
+                                            int tid) {
   using C = GemmCfg<BM, BN, BWD>;
 #pragma unroll
-  for (int i = 0; i < C::A_LOADS; ++i) {
-    const int q = wave + 4 * i;
-    const int row = 8 * q + (lane >> 3);
-    const int col = red0 + 8 * ((lane & 7) ^ ((row >> 1) & 7));
+  for (int i = 0; i < C::A_CHUNKS; ++i) {
+    const int q = tid + C::NT * i, row = q >> 3;
+    const int col = red0 + 8 * (q & 7);
     const bool ok = m0 + row < M && col < KRED;
     const uint32_t off =
         ok ? (uint32_t)(((int64_t)(m0 + row) * KRED + col) * 2) : G_OOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + q * 1024),
-                                             16, off, 0, 0, 0);
+    R.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+  }
+}
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_store_a(const ARegs<BM, BN, BWD>& R,
+                                             char* sA, int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+#pragma unroll
+  for (int i = 0; i < C::A_CHUNKS; ++i) {
+    const int q = tid + C::NT * i, row = q >> 3;
+    *reinterpret_cast<u32x4*>(sA + row * 128 + (((q & 7) ^ ((row >> 1) & 7)) << 4)) = R.v[i];
   }
 }
 
@@ -548,17 +554,18 @@ __device__ __forceinline__ void gemm_load_a(rsrc_t ra, char* sA, int M,
 // ds_read_b64_tr_b16 serves 4 rows: in every group of 16 lanes, lane
 // q = 4j + p addresses row j, columns 4p..4p+3 of the group's 16 columns,
 // and lane q receives column q of the 4 rows.
-template <bool SWZ>
-__device__ __forceinline__ u32x4 lds_read_bT(const uint16_t* sW, int pitch,
-                                             int row0, int col0, int lane) {
+template <int BN>
+__device__ __forceinline__ u32x4 lds_read_bT(const uint16_t* sW, int row0,
+                                             int col0, int lane) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const int grp = lane >> 4, q = lane & 15;
   const int row = row0 + 8 * (grp >> 1) + (q >> 2);
-  int col = col0 + 16 * (grp & 1) + 4 * (q & 3);
-  if (SWZ) col = (((col >> 3) ^ wswz(row, col >> 3)) << 3) | (col & 7);
-  const uint16_t* p0 = sW + row * pitch + col;
-  const uint16_t* p1 = p0 + 4 * pitch;
+  const int col = col0 + 16 * (grp & 1) + 4 * (q & 3);
+  // rows row and row + 4 have the same swizzle (it depends on row & 3)
+  const int pc = (((col >> 3) ^ bwd_swz<BN>(row, col >> 3)) << 3) | (col & 7);
+  const uint16_t* p0 = sW + row * BN + pc;
+  const uint16_t* p1 = p0 + 4 * BN;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_s16x4*)(const_cast<uint16_t*>(p0)));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -571,8 +578,14 @@ __device__ __forceinline__ u32x4 lds_read_bT(const uint16_t* sW, int pitch,
   return r;
 }
 
-// Fragments of one k16 slice: A rows (ds_read_b128 from the swizzled tile)
-// and B columns (ds_read_b128 forward, ds_read_b64_tr_b16 backward).
+// 16 bytes of row r, logical chunk c of a 128-byte-row tile swizzled by
+// (r / 2) & 7 (the A tile, and the forward weight tile).
+__device__ __forceinline__ u32x4 lds_read_row128(const void* t, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(t) + r * 128 +
+                                         ((c ^ ((r >> 1) & 7)) << 4));
+}
+
+// Fragments of one k16 slice: A rows and B columns.
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_frags(const char* sA, const uint16_t* sW,
                                            int wm, int wn, int lane, int kk,
@@ -581,19 +594,14 @@ __device__ __forceinline__ void gemm_frags(const char* sA, const uint16_t* sW,
   using C = GemmCfg<BM, BN, BWD>;
   const int chunk = 2 * kk + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int r = wm * C::WM + i * 32 + (lane & 31);
-    a[i] = *reinterpret_cast<const u32x4*>(sA + r * 128 +
-                                           ((chunk ^ ((r >> 1) & 7)) << 4));
-  }
+  for (int i = 0; i < C::TM; ++i)
+    a[i] = lds_read_row128(sA, wm * C::WM + i * 32 + (lane & 31), chunk);
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) {
     if (!BWD)
-      b[j] = *reinterpret_cast<const u32x4*>(
-          sW + (wn * C::WN + j * 32 + (lane & 31)) * C::PW + kk * 16 +
-          (lane >> 5) * 8);
+      b[j] = lds_read_row128(sW, wn * C::WN + j * 32 + (lane & 31), chunk);
     else
-      b[j] = lds_read_bT<C::WSWZ>(sW, C::PW, kk * 16, wn * C::WN + j * 32, lane);
+      b[j] = lds_read_bT<BN>(sW, kk * 16, wn * C::WN + j * 32, lane);
   }
 }
 
@@ -602,7 +610,7 @@ constexpr int G_VALU_PER_MFMA = 6;
 
 // The four k16 slices of one step with the dequantization of the next weight
 // tile woven in: one decode8 (28 VALU ops and a 16-byte LDS write) after
-// every MPD MFMAs, each group fenced and ordered MFMA / 4 VALU so the VALU
+// every MPD MFMAs, each group fenced and ordered MFMA / VALU so the VALU
 // work issues in the shadow of the MFMAs instead of after them.
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_mma_deq(
@@ -616,8 +624,7 @@ __device__ __forceinline__ void gemm_mma_deq(
   static_assert(C::WDW % 4 == 0 && MPK % DPK == 0, "decode split");
   const WDst dst = gemm_wdst<BM, BN, BWD>(sWn, tid);
   const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
-  const uint32_t wd[8] = {R.w0.x, R.w0.y, R.w0.z, R.w0.w,
-                          R.w1.x, R.w1.y, R.w1.z, R.w1.w};
+  const uint32_t wd[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
   u32x4 a[2][C::TM], b[2][C::TN];
   gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, 0, a[0], b[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -636,11 +643,8 @@ __device__ __forceinline__ void gemm_mma_deq(
 #pragma unroll
         for (int h = 0; h < MPD; ++h) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, G_VALU_PER_MFMA, 0);   // VALU
-          if (kk < 3 && h < (C::TM + C::TN) / DPK)
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, G_VALU_PER_MFMA, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);     // DS write
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -670,16 +674,18 @@ __device__ __forceinline__ void gemm_step(
     const Codebook& cb,
     f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
   WRegs Wn;
-  gemm_load_a<BM, BN, BWD>(ra, sAn, M, KRED, m0, (st + 1) * G_BK, wave, lane);
+  ARegs<BM, BN, BWD> An;
+  gemm_load_a<BM, BN, BWD>(An, ra, M, KRED, m0, (st + 1) * G_BK, tid);
   gemm_load_w<BM, BN, BWD>(Wn, rp, rq, rd, N, K, c0, (st + 2) * G_BK, tid);
   gemm_mma_deq<BM, BN, BWD>(sAc, sWc, sWn, Wc, cb, wm, wn, tid, lane, acc);
-  __builtin_amdgcn_s_waitcnt(0);   // all counters: loads landed in LDS/regs
+  gemm_store_a<BM, BN, BWD>(An, sAn, tid);
+  __builtin_amdgcn_s_waitcnt(0);   // all counters: loads and LDS writes done
   __syncthreads();
   Wc = Wn;
 }
 
 template <int BM, int BN, bool BWD>
-__global__ __launch_bounds__(256, 1) void k_gemm(
+__global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
     const uint16_t* __restrict__ Aop, const uint8_t* __restrict__ packed,
     const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
     const uint16_t* __restrict__ La_hi, const uint16_t* __restrict__ La_lo,
@@ -696,7 +702,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(
   const int KRED = BWD ? N : K;        // reduction length
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   int tm, tn;
   gemm_tile_of((M + BM - 1) / BM, (NOUT + BN - 1) / BN, tm, tn);
   const int m0 = tm * BM, c0 = tn * BN;
@@ -720,7 +726,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(
   // pairs of steps without branches.
   const int nsteps = (KRED + G_BK - 1) / G_BK;
   WRegs Wc;
-  gemm_load_a<BM, BN, BWD>(ra, sA0, M, KRED, m0, 0, wave, lane);
+  {
+    ARegs<BM, BN, BWD> A0;
+    gemm_load_a<BM, BN, BWD>(A0, ra, M, KRED, m0, 0, tid);
+    gemm_store_a<BM, BN, BWD>(A0, sA0, tid);
+  }
   gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, 0, tid);
   gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);
   gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, G_BK, tid);
@@ -1513,7 +1523,7 @@ void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
   const int nout = BWD ? K : N;
   const unsigned tiles = (unsigned)(cdiv(M, BM) * cdiv(nout, BN));
   QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD>),
-            dim3(tiles), dim3(256), st, Aop, w->packed, w->qabs, w->gscale,
+            dim3(tiles), dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs, w->gscale,
             La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16, codebook());
 }
 
