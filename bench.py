@@ -156,49 +156,60 @@ def timed_graph(fn, reps, warmup=2):
     return sec
 
 
-def bench_dequant_quant(reps):
-    """7B-class layer: dequant and quantize GB/s over all 7 projections."""
+def bench_dequant_quant(reps, copies=3):
+    """7B-class layer: dequant and quantize GB/s over all 7 projections.
+
+    The dequant pass reads 104 MB of NF4 data, which the 256 MB MALL could
+    keep between passes; the timed region cycles through `copies`
+    independently quantized copies of the layer (3 x 104 MB > 256 MB), so
+    each pass reads its input from HBM."""
     import torch
     from bit_nf4_quantized_14_amd import capi
     from bit_nf4_quantized_14_amd import workloads as wl
     wk = wl.workload("dequant7b")
-    tens, outs, ws32 = [], [], []
+    sets, outs, ws32 = [[] for _ in range(copies)], [], []
     params = 0
     for p in range(len(wk.projections)):
         w = torch.from_numpy(wl.weight(wk, p)).to("cuda")
-        tens.append(capi.nf4_quantize(w))
+        for c in range(copies):
+            sets[c].append(capi.nf4_quantize(w))
         ws32.append(w)
         outs.append(torch.empty((w.shape[0], w.shape[1]), dtype=torch.bfloat16,
                                 device="cuda"))
         params += w.numel()
+    tens = sets[0]
     npk = sum(t.packed.numel() + t.qabs.numel() + 4 * t.gscale.numel() for t in tens)
     deq_bytes = npk + 2 * params
     q_bytes = 4 * params + npk
 
-    def deq():
-        for t, o in zip(tens, outs):
-            capi.nf4_dequantize(t, o)
+    def deq():                      # `copies` passes, one per weight copy
+        for c in range(copies):
+            for t, o in zip(sets[c], outs):
+                capi.nf4_dequantize(t, o)
 
     def quant():
         for w, t in zip(ws32, tens):
             capi.nf4_quantize(w, t)
 
     res = {}
-    for name, fn, kname, nbytes in (("dequant7b", deq, "k_dequant", deq_bytes),
-                                    ("quantize7b", quant, "k_quantize", q_bytes)):
-        sec = timed_graph(fn, reps)
-        kt, _ = kernel_times_ms(capi, kname, fn, len(tens), reps)
+    for name, fn, kname, nbytes, passes in (
+            ("dequant7b", deq, "k_dequant", deq_bytes, copies),
+            ("quantize7b", quant, "k_quantize", q_bytes, 1)):
+        sec = timed_graph(fn, reps) / passes
+        kt, _ = kernel_times_ms(capi, kname, fn, len(tens) * passes, reps)
         ksum = kt * len(tens) * 1e-3
         res[name] = {"params": params, "bytes_per_pass": nbytes,
                      "ms_per_pass": sec * 1e3,
                      "GB/s": nbytes / sec / 1e9,
-                     "timing": "graph replay of the 7-projection pass",
+                     "timing": "graph replay of the 7-projection pass" +
+                               (f", cycling over {passes} weight copies (> MALL)"
+                                if passes > 1 else ""),
                      "kernel": kname, "kernel_ms_per_pass": ksum * 1e3,
                      "kernel_GB/s": nbytes / ksum / 1e9,
                      "frac_hbm_peak": nbytes / ksum / 1e9 / HBM_PEAK_GBS}
         log(f"{name}: {res[name]['GB/s']:.0f} GB/s graph, "
             f"{res[name]['kernel_GB/s']:.0f} GB/s kernel")
-    del tens, outs, ws32
+    del sets, tens, outs, ws32
     torch.cuda.empty_cache()
     return res
 
@@ -442,7 +453,10 @@ def main():
             comps.update(bench_70b(max(3, args.steps // 4)))
         out["components"] = comps
         if "dequant7b" in comps:
-            out["dequant_GBps"] = comps["dequant7b"]["kernel_GB/s"]
+            # whole-pass throughput (graph replay over weight copies that do
+            # not fit the MALL); the per-launch event figure is reported in
+            # components and includes event overhead per launch
+            out["dequant_GBps"] = comps["dequant7b"]["GB/s"]
     if not args.quick and not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample_tokens)

@@ -1249,11 +1249,14 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
 // v_mfma_f32_16x16x32_bf16 step (t = 0..7 takes weights 8t..8t+7 of the
 // block); the matching A operand is X[m][64 g + 8 t ...] from LDS.  The
 // next chunk's weight bytes are loaded before the current chunk is decoded.
-// Partial sums go to part[slice][m][row] (fp32), combined by k_skinny_reduce.
+// A persistent workgroup takes a contiguous run of work items ordered
+// slice-major, so its X slice stays in LDS across the row blocks of one
+// slice.  Partial sums go to part[slice][m][row] (fp32, m < M), combined by
+// k_skinny_reduce.
 // ---------------------------------------------------------------------------
 constexpr int SK_WAVES = 8;
 constexpr int SK_ROWS = 16 * SK_WAVES;       // rows per workgroup
-constexpr int SK_KS_MAX = 2048;              // longest K slice
+constexpr int SK_KS_MAX = 4096;              // longest K slice
 
 struct SkRegs {
   u32x4 w0, w1;
@@ -1281,8 +1284,14 @@ __global__ __launch_bounds__(512) void k_skinny_partial(
   const rsrc_t ra = make_rsrc(A, (uint32_t)((int64_t)r * K * 2));
   const rsrc_t rx = make_rsrc(X, (uint32_t)((int64_t)M * K * 2));
 
-  // work items: (block of SK_ROWS rows, K slice), handed out round-robin
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  // work items (block of SK_ROWS rows, K slice), item = slice * wg_rows +
+  // row block; this workgroup takes items [ib, ie)
+  const int ipw = (nitems + gridDim.x - 1) / gridDim.x;
+  const int ib = blockIdx.x * ipw, ie = min(nitems, ib + ipw);
+  for (int c = tid; c < KS / 8; c += 512)
+    *reinterpret_cast<u32x4*>(sX + M * XP + 8 * c) = u32x4{0u, 0u, 0u, 0u};
+  int staged = -1;                               // slice held in sX
+  for (int item = ib; item < ie; ++item) {
     const int rb = item % wg_rows, slice = item / wg_rows;
     const int k0 = slice * KS;
     const int klen = min(KS, K - k0);
@@ -1291,30 +1300,32 @@ __global__ __launch_bounds__(512) void k_skinny_partial(
 
     // X slice -> LDS (M rows, columns >= klen zero), each 8-element group
     // permuted into the order decode8p produces; loads issued before use.
-    for (int c = tid; c < KS / 8; c += 512)
-      *reinterpret_cast<u32x4*>(sX + M * XP + 8 * c) = u32x4{0u, 0u, 0u, 0u};
-    {
+    if (slice != staged) {
+      if (staged >= 0) __syncthreads();          // sX still being read
+      staged = slice;
       const int groups = M * (KS / 8);
-      constexpr int XL = 16 * (SK_KS_MAX / 8) / 512;
-      u32x4 xv[XL];
+      // batches of 4 loads per thread, all issued before their LDS writes
+      for (int i0 = 0; i0 < groups; i0 += 4 * 512) {
+        u32x4 xv[4];
 #pragma unroll
-      for (int i = 0; i < XL; ++i) {
-        const int idx = tid + 512 * i;
-        const int m = idx / (KS / 8), c = 8 * (idx % (KS / 8));
-        const bool ok = idx < groups && c < klen;
-        xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            rx, ok ? (uint32_t)(((int64_t)m * K + k0 + c) * 2) : G_OOB, 0, 0));
-      }
-#pragma unroll
-      for (int i = 0; i < XL; ++i) {
-        const int idx = tid + 512 * i;
-        if (idx < groups) {
+        for (int i = 0; i < 4; ++i) {
+          const int idx = i0 + tid + 512 * i;
           const int m = idx / (KS / 8), c = 8 * (idx % (KS / 8));
-          *reinterpret_cast<u32x4*>(sX + m * XP + c) = permute8(xv[i]);
+          const bool ok = idx < groups && c < klen;
+          xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+              rx, ok ? (uint32_t)(((int64_t)m * K + k0 + c) * 2) : G_OOB, 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = i0 + tid + 512 * i;
+          if (idx < groups) {
+            const int m = idx / (KS / 8), c = 8 * (idx % (KS / 8));
+            *reinterpret_cast<u32x4*>(sX + m * XP + c) = permute8(xv[i]);
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (row0 < rows_total) {
@@ -1371,10 +1382,9 @@ __global__ __launch_bounds__(512) void k_skinny_partial(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
-        if (m < M) part[((int64_t)slice * 16 + m) * rows_total + row] = acc[v];
+        if (m < M) part[((int64_t)slice * M + m) * rows_total + row] = acc[v];
       }
     }
-    __syncthreads();      // sX is refilled by the next item
   }
 }
 
@@ -1397,8 +1407,8 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
     for (; sl + 4 <= slices; sl += 4)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        t[u] += part[((int64_t)(sl + u) * 16 + m) * rows_total + Np16 + j];
-    for (; sl < slices; ++sl) t[0] += part[((int64_t)sl * 16 + m) * rows_total + Np16 + j];
+        t[u] += part[((int64_t)(sl + u) * M + m) * rows_total + Np16 + j];
+    for (; sl < slices; ++sl) t[0] += part[((int64_t)sl * M + m) * rows_total + Np16 + j];
     const float v = (t[0] + t[1]) + (t[2] + t[3]);
     sT[idx] = v;
     if (blockIdx.x == 0) t_save[idx] = v;
@@ -1415,8 +1425,8 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
     for (; sl + 4 <= slices; sl += 4)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        y[u] += part[((int64_t)(sl + u) * 16 + m) * rows_total + n];
-    for (; sl < slices; ++sl) y[0] += part[((int64_t)sl * 16 + m) * rows_total + n];
+        y[u] += part[((int64_t)(sl + u) * M + m) * rows_total + n];
+    for (; sl < slices; ++sl) y[0] += part[((int64_t)sl * M + m) * rows_total + n];
     float lora = 0.f;
     for (int j = 0; j < r; ++j)
       lora += sT[m * r + j] * bf16_to_f32(B[(int64_t)n * r + j]);
@@ -1606,15 +1616,19 @@ struct SkinnyPlan {
 };
 
 constexpr int SK_WGS_PER_CU = 2;     // resident skinny workgroups per CU
+constexpr int64_t SK_LDS_PER_WG = 64 * 1024;   // X tile budget (bytes)
 
-SkinnyPlan skinny_plan(int64_t N, int64_t K, int r) {
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
   SkinnyPlan P;
   P.rows_total = (int)(((N + 15) & ~15LL) + 16 * rank_tiles(r));
   P.wg_rows = (int)cdiv(P.rows_total, SK_ROWS);
   const int64_t kchunks = cdiv(K, 256);
-  // slices of at most 1024 columns, and enough work items to keep several
-  // resident workgroups per CU busy
-  int64_t slices = std::max<int64_t>(cdiv(K, 1024), cdiv(256 * SK_WGS_PER_CU * 2, P.wg_rows));
+  // longest slice whose X tile ((M + 1) rows, zero row included) leaves room
+  // for two workgroups per CU, and enough slices for ~2 items per workgroup
+  int64_t ks_max = (SK_LDS_PER_WG / (2 * (M + 1)) - 8) / 256 * 256;
+  ks_max = std::max<int64_t>(256, std::min<int64_t>(ks_max, SK_KS_MAX));
+  int64_t slices = std::max<int64_t>(cdiv(K, ks_max),
+                                     cdiv(256 * SK_WGS_PER_CU * 2, P.wg_rows));
   slices = std::min<int64_t>(slices, kchunks);
   const int64_t ks = cdiv(kchunks, slices) * 256;
   P.ks = (int)ks;
@@ -1636,11 +1650,11 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
   FwdWorkspace L{};
   L.rpad = 16 * rank_tiles(r);
   if (M <= qn::QN_SKINNY_M) {
-    const SkinnyPlan P = skinny_plan(N, K, r);
+    const SkinnyPlan P = skinny_plan(M, N, K, r);
     L.slices = P.slices;
     L.ks = P.ks;
     L.part = 0;
-    L.total = align256(size_t(P.slices) * 16 * P.rows_total * 4);
+    L.total = align256(size_t(P.slices) * M * P.rows_total * 4);
     return L;
   }
   const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r));
@@ -1785,7 +1799,7 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
   hipStream_t st = (hipStream_t)stream;
   if (M <= qn::QN_SKINNY_M) {
-    const SkinnyPlan P = skinny_plan(N, K, r);
+    const SkinnyPlan P = skinny_plan(M, N, K, r);
     float* part = ws_at<float>(ws, L.part);
     const int nitems = P.wg_rows * P.slices;
     const size_t shm = size_t(M + 1) * (P.ks + 8) * 2;
