@@ -182,7 +182,11 @@ def bench_dequant_quant(reps, copies=3):
     deq_bytes = npk + 2 * params
     q_bytes = 4 * params + npk
 
-    def deq():                      # `copies` passes, one per weight copy
+    def deq():                      # `copies` passes, one launch per copy
+        for c in range(copies):
+            capi.nf4_dequantize_batch(sets[c], outs)
+
+    def deq_each():                 # the same, one call per projection
         for c in range(copies):
             for t, o in zip(sets[c], outs):
                 capi.nf4_dequantize(t, o)
@@ -192,23 +196,29 @@ def bench_dequant_quant(reps, copies=3):
             capi.nf4_quantize(w, t)
 
     res = {}
-    for name, fn, kname, nbytes, passes in (
-            ("dequant7b", deq, "k_dequant", deq_bytes, copies),
-            ("quantize7b", quant, "k_quantize", q_bytes, 1)):
+    for name, fn, kname, nbytes, passes, launches in (
+            ("dequant7b", deq, "k_dequant", deq_bytes, copies, 1),
+            ("quantize7b", quant, "k_quantize", q_bytes, 1, len(tens))):
         sec = timed_graph(fn, reps) / passes
-        kt, _ = kernel_times_ms(capi, kname, fn, len(tens) * passes, reps)
-        ksum = kt * len(tens) * 1e-3
+        kt, _ = kernel_times_ms(capi, kname, fn, launches * passes, reps)
+        ksum = kt * launches * 1e-3
         res[name] = {"params": params, "bytes_per_pass": nbytes,
                      "ms_per_pass": sec * 1e3,
                      "GB/s": nbytes / sec / 1e9,
-                     "timing": "graph replay of the 7-projection pass" +
-                               (f", cycling over {passes} weight copies (> MALL)"
-                                if passes > 1 else ""),
+                     "timing": "graph replay of the 7-projection pass",
                      "kernel": kname, "kernel_ms_per_pass": ksum * 1e3,
                      "kernel_GB/s": nbytes / ksum / 1e9,
                      "frac_hbm_peak": nbytes / ksum / 1e9 / HBM_PEAK_GBS}
         log(f"{name}: {res[name]['GB/s']:.0f} GB/s graph, "
             f"{res[name]['kernel_GB/s']:.0f} GB/s kernel")
+    # the same pass as seven separate calls (one launch per projection)
+    sec = timed_graph(deq_each, reps) / copies
+    res["dequant7b"]["per_call_GB/s"] = deq_bytes / sec / 1e9
+    res["dequant7b"]["timing"] = ("graph replay of the 7-projection pass as one "
+                                  "nf4_dequantize_batch launch, cycling over "
+                                  f"{copies} weight copies (> MALL); per_call_GB/s: "
+                                  "the same pass as 7 nf4_dequantize calls")
+    log(f"dequant7b as 7 calls: {res['dequant7b']['per_call_GB/s']:.0f} GB/s graph")
     del sets, tens, outs, ws32
     torch.cuda.empty_cache()
     return res

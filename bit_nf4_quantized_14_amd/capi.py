@@ -25,8 +25,10 @@ QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 256
 
 # Every symbol the header declares (tests check the library exports them).
 EXPORTS = ("nf4_codebook", "nf4_quantize", "nf4_dequantize",
+           "nf4_dequantize_batch",
            "qlora_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
            "qn_strerror", "qn_profile_kernel")
+QN_DEQUANT_BATCH_MAX = 16
 
 
 class _NF4Struct(ctypes.Structure):
@@ -56,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.nf4_quantize.restype = ctypes.c_int
     L.nf4_dequantize.argtypes = [sp, vp, vp]
     L.nf4_dequantize.restype = ctypes.c_int
+    L.nf4_dequantize_batch.argtypes = [sp, ctypes.POINTER(vp), i32, vp]
+    L.nf4_dequantize_batch.restype = ctypes.c_int
     L.qlora_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.qlora_workspace_bytes.restype = ctypes.c_size_t
     L.qlora_linear_fwd.argtypes = [vp, i64, sp, vp, vp, i32, f32, vp, i32, vp,
@@ -161,6 +165,21 @@ def nf4_dequantize(w: NF4Tensor, out=None, stream=None):
     _check("nf4_dequantize", lib().nf4_dequantize(ctypes.byref(st), _ptr(out),
                                                   _stream(stream)))
     return out
+
+
+def nf4_dequantize_batch(ws, outs=None, stream=None):
+    """Dequantize several NF4 tensors in one launch; returns the bf16
+    outputs (allocated when `outs` is None)."""
+    import torch
+    ws = list(ws)
+    if outs is None:
+        outs = [torch.empty((w.rows, w.cols), dtype=torch.bfloat16,
+                            device=w.packed.device) for w in ws]
+    structs = (_NF4Struct * len(ws))(*[w.as_struct() for w in ws])
+    ptrs = (ctypes.c_void_p * len(ws))(*[_ptr(o) for o in outs])
+    _check("nf4_dequantize_batch", lib().nf4_dequantize_batch(
+        structs, ptrs, len(ws), _stream(stream)))
+    return outs
 
 
 def qlora_workspace_bytes(M: int, N: int, K: int, r: int, which: int) -> int:

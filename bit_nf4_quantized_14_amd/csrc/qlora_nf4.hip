@@ -288,32 +288,54 @@ struct DqRegs {
   float d;
 };
 
-__global__ __launch_bounds__(DQ_THREADS) void k_dequant(
-    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
-    const float* __restrict__ gscale, int64_t nspans,
-    uint16_t* __restrict__ out, Codebook cb) {
+// One launch dequantizes up to DQ_BATCH_MAX tensors: their whole spans are
+// numbered consecutively (tensor i owns global spans [span0_i, span0_{i+1})).
+constexpr int DQ_BATCH_MAX = QN_DEQUANT_BATCH_MAX;
+struct DqTensor {
+  const uint8_t* packed;
+  const uint8_t* qabs;
+  const float* gscale;
+  uint16_t* out;
+  int64_t span0;
+};
+struct DqBatch {
+  DqTensor t[DQ_BATCH_MAX];
+  int64_t nspans;       // total whole spans
+  int count;
+};
+
+__global__ __launch_bounds__(DQ_THREADS) void k_dequant(DqBatch b, Codebook cb) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave0 = ((int64_t)blockIdx.x * DQ_THREADS + threadIdx.x) >> 6;
+  const int64_t wave0 = __builtin_amdgcn_readfirstlane(
+      (int)(((int64_t)blockIdx.x * DQ_THREADS + threadIdx.x) >> 6));
   const int64_t nwaves = ((int64_t)gridDim.x * DQ_THREADS) >> 6;
+  // tensor owning global span s (wave-uniform scan over <= 16 entries)
+  auto owner = [&](int64_t s) {
+    int i = 0;
+    while (i + 1 < b.count && s >= b.t[i + 1].span0) ++i;
+    return i;
+  };
   auto load = [&](DqRegs& R, int64_t span) {
-    const bool ok = span < nspans;
-    const int64_t sp = ok ? span : 0;
-    const uint32_t* pw = reinterpret_cast<const uint32_t*>(packed) + sp * (DQ_SPAN / 8);
-    const uint8_t* qb = qabs + sp * (DQ_SPAN / 64);
+    const bool ok = span < b.nspans;
+    const int ti = ok ? owner(span) : 0;
+    const int64_t sp = ok ? span - b.t[ti].span0 : 0;
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(b.t[ti].packed) + sp * (DQ_SPAN / 8);
+    const uint8_t* qb = b.t[ti].qabs + sp * (DQ_SPAN / 64);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       R.p[j] = pw[lane + 64 * j];
       R.q[j] = qb[(lane >> 3) + 8 * j];
     }
-    R.d = ok ? gscale[(sp * (DQ_SPAN / 64)) >> 8] : 0.0f;
+    R.d = ok ? b.t[ti].gscale[(sp * (DQ_SPAN / 64)) >> 8] : 0.0f;
   };
   DqRegs cur;
   int64_t span = wave0;
   load(cur, span);
-  for (; span < nspans; span += nwaves) {
+  for (; span < b.nspans; span += nwaves) {
     DqRegs nxt;
     load(nxt, span + nwaves);
-    u32x4* o = reinterpret_cast<u32x4*>(out + span * DQ_SPAN);
+    const int ti = owner(span);
+    u32x4* o = reinterpret_cast<u32x4*>(b.t[ti].out + (span - b.t[ti].span0) * DQ_SPAN);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const Lut t = make_lut(cb, static_cast<float>(cur.q[j]) * cur.d);
@@ -325,7 +347,6 @@ __global__ __launch_bounds__(DQ_THREADS) void k_dequant(
   }
 }
 
-// Weights [e0, numel), e0 a multiple of 2048: one thread per weight.
 __global__ __launch_bounds__(DQ_THREADS) void k_dequant_tail(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
     const float* __restrict__ gscale, int64_t e0, int64_t numel,
@@ -1751,25 +1772,42 @@ int nf4_quantize(const float* w, const nf4_tensor* out, int32_t* status_dev,
   return check_launch();
 }
 
-int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream) {
-  if (!valid_tensor(w) || w_bf16 == nullptr || !aligned16(w_bf16))
+int nf4_dequantize_batch(const nf4_tensor* w, uint16_t* const* w_bf16,
+                         int32_t count, void* stream) {
+  if (w == nullptr || w_bf16 == nullptr || count < 1 || count > DQ_BATCH_MAX)
     return QN_EINVAL;
-  const int64_t numel = w->rows * w->cols;
-  const int64_t nspans = numel / DQ_SPAN;
-  hipStream_t st = (hipStream_t)stream;
-  if (nspans > 0) {
-    // up to 64 waves per CU; larger tensors walk several spans per wave
-    const int64_t grid = std::min<int64_t>(cdiv(nspans, DQ_THREADS / 64), QN_DQ_GRID_CAP);
-    QN_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(DQ_THREADS),
-              st, w->packed, w->qabs, w->gscale, nspans, w_bf16, codebook());
+  DqBatch b;
+  std::memset(&b, 0, sizeof(b));
+  int64_t spans = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!valid_tensor(&w[i]) || w_bf16[i] == nullptr || !aligned16(w_bf16[i]))
+      return QN_EINVAL;
+    b.t[i] = DqTensor{w[i].packed, w[i].qabs, w[i].gscale, w_bf16[i], spans};
+    spans += w[i].rows * w[i].cols / DQ_SPAN;
   }
-  const int64_t e0 = nspans * DQ_SPAN;
-  if (e0 < numel)
-    QN_LAUNCH("k_dequant_tail", k_dequant_tail,
-              dim3((unsigned)cdiv(numel - e0, DQ_THREADS)), dim3(DQ_THREADS),
-              st, w->packed, w->qabs, w->gscale, e0, numel, w_bf16,
-              codebook());
+  b.nspans = spans;
+  b.count = count;
+  hipStream_t st = (hipStream_t)stream;
+  if (spans > 0) {
+    // up to 64 waves per CU; larger passes walk several spans per wave
+    const int64_t grid = std::min<int64_t>(cdiv(spans, DQ_THREADS / 64), QN_DQ_GRID_CAP);
+    QN_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(DQ_THREADS),
+              st, b, codebook());
+  }
+  for (int i = 0; i < count; ++i) {
+    const int64_t numel = w[i].rows * w[i].cols;
+    const int64_t e0 = numel / DQ_SPAN * DQ_SPAN;
+    if (e0 < numel)
+      QN_LAUNCH("k_dequant_tail", k_dequant_tail,
+                dim3((unsigned)cdiv(numel - e0, DQ_THREADS)), dim3(DQ_THREADS),
+                st, w[i].packed, w[i].qabs, w[i].gscale, e0, numel, w_bf16[i],
+                codebook());
+  }
   return check_launch();
+}
+
+int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream) {
+  return nf4_dequantize_batch(w, &w_bf16, 1, stream);
 }
 
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,

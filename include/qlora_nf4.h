@@ -135,6 +135,23 @@ int nf4_quantize(const float* w, const nf4_tensor* out, int32_t* status_dev,
 int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream);
 
 /*
+ * nf4_dequantize_batch -- the same for several weights in one launch.
+ *
+ * Same operation as nf4_dequantize (pages and formula above), for all the
+ * projections of a layer at once: their whole 2048-weight spans form one
+ * work list, so the pass runs as one kernel instead of count kernels.
+ * w      : host array of count tensors (device buffers, as nf4_dequantize).
+ * w_bf16 : host array of count device pointers, each rows*cols uint16,
+ *          16-byte aligned.  The outputs must not overlap.
+ * count  : 1 .. QN_DEQUANT_BATCH_MAX.
+ * Errors: QN_EINVAL (count out of range, or any tensor / output invalid as
+ *         for nf4_dequantize; nothing is launched then), QN_EHIP.
+ */
+#define QN_DEQUANT_BATCH_MAX 16
+int nf4_dequantize_batch(const nf4_tensor* w, uint16_t* const* w_bf16,
+                         int32_t count, void* stream);
+
+/*
  * qlora_workspace_bytes -- device workspace a fused call needs (host).
  * which: QN_FWD or QN_BWD.  Returns 0 for invalid arguments.
  */

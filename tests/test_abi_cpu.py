@@ -72,6 +72,21 @@ def test_quantize_dequantize_validation():
     assert L.nf4_dequantize(ctypes.byref(st), None, None) == capi.QN_EINVAL
 
 
+def test_dequantize_batch_validation():
+    L = capi.lib()
+    st = (capi._NF4Struct * 2)(_fake_tensor(4, 64), _fake_tensor(4, 64))
+    outs = (ctypes.c_void_p * 2)(0x4000, 0x8000)
+    assert L.nf4_dequantize_batch(st, outs, 0, None) == capi.QN_EINVAL
+    assert L.nf4_dequantize_batch(st, outs, capi.QN_DEQUANT_BATCH_MAX + 1,
+                                  None) == capi.QN_EINVAL
+    assert L.nf4_dequantize_batch(None, outs, 2, None) == capi.QN_EINVAL
+    assert L.nf4_dequantize_batch(st, None, 2, None) == capi.QN_EINVAL
+    bad = (ctypes.c_void_p * 2)(0x4000, 0x8001)             # misaligned output
+    assert L.nf4_dequantize_batch(st, bad, 2, None) == capi.QN_EINVAL
+    st_bad = (capi._NF4Struct * 2)(_fake_tensor(4, 64), _fake_tensor(0, 64))
+    assert L.nf4_dequantize_batch(st_bad, outs, 2, None) == capi.QN_EINVAL
+
+
 def test_linear_validation():
     L = capi.lib()
     p = 0x10000
