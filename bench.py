@@ -284,22 +284,39 @@ def bench_70b(reps, do_train=True):
     return res
 
 
+# source files that define each kernel (plus the shared device header)
+KERNEL_SOURCES = (("k_gemm", "gemm.hip"), ("k_rank", "rank.hip"),
+                  ("k_dequant", "codec.hip"), ("k_quantize", "codec.hip"),
+                  ("k_skinny", "skinny.hip"))
+
+
+def kernel_source_sha(kernel_key: str):
+    """sha256[:16] of the sources a kernel is built from, or None."""
+    import hashlib
+    csrc = os.path.join(ROOT, "bit_nf4_quantized_14_amd", "csrc")
+    for prefix, fname in KERNEL_SOURCES:
+        if kernel_key.startswith(prefix):
+            h = hashlib.sha256()
+            for f in ("qn_device.h", fname):
+                with open(os.path.join(csrc, f), "rb") as fh:
+                    h.update(fh.read())
+            return h.hexdigest()[:16]
+    return None
+
+
 def measured_traffic(kernel_key: str):
     """HBM bytes per launch of `kernel_key` from the committed rocprofv3
     counter summary (profiles/hbm_traffic.json, FETCH_SIZE/WRITE_SIZE scaled
-    by a plain copy of known size), or None when the kernel source has
+    by a plain copy of known size), or None when the kernel's sources have
     changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    src = os.path.join(ROOT, "bit_nf4_quantized_14_amd", "csrc", "qlora_nf4.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    except (OSError, ValueError):
+        k = rec["kernels"][kernel_key]
+    except (OSError, ValueError, KeyError):
         return None
-    if rec.get("source_sha256_16") != sha or kernel_key not in rec.get("kernels", {}):
+    if k.get("source_sha256_16") != kernel_source_sha(kernel_key):
         return None
-    k = rec["kernels"][kernel_key]
     return k["read_bytes"] + k["write_bytes"]
 
 

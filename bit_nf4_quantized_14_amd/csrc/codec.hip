@@ -1,0 +1,255 @@
+// NF4 codec kernels of the QLoRA NF4 library: quantization with double
+// quantization (K1) and dequantization to bf16 (K2), and their C entry
+// points.  What is computed follows "Qlora Expert" (Core Concept: NF4 at
+// N(0,1) quantiles, double quantization of the block constants),
+// "QLoRA Implementation Details (2025 Edition)" (Step 1 NF4 Math: 64-value
+// blocks) and the "QLORA ... paper summary" (Notes: load 4-bit, dequantize
+// to BF16).
+#include "qn_host.h"
+
+namespace {
+
+using namespace qn;
+
+// ---------------------------------------------------------------------------
+// K1: quantization + double quantization.  One workgroup per group of 256
+// blocks (16384 weights); each thread owns 8 consecutive weights in each of
+// 8 passes (8 lanes per 64-weight block).
+// ---------------------------------------------------------------------------
+constexpr int QZ_THREADS = 256;
+constexpr int QZ_PASSES = 8;  // 8 * 256 * 8 = 16384 weights
+
+__global__ __launch_bounds__(QZ_THREADS) void k_quantize(
+    const float* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
+    uint8_t* __restrict__ qabs, float* __restrict__ gscale,
+    int32_t* __restrict__ status, Codebook cb) {
+  __shared__ float s_c[256];
+  __shared__ float s_wmax[QZ_THREADS / 64];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int64_t gbase = g * (int64_t)(QN_BLOCK * QN_GROUP);
+  const int64_t nb_total = (numel + QN_BLOCK - 1) / QN_BLOCK;
+
+  float v[QZ_PASSES][8];
+  float cmine[QZ_PASSES];
+  bool finite = true;
+#pragma unroll
+  for (int it = 0; it < QZ_PASSES; ++it) {
+    const int64_t e0 = gbase + it * (QZ_THREADS * 8) + tid * 8;
+    if (e0 + 8 <= numel) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(w + e0);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(w + e0 + 4);
+      v[it][0] = a.x; v[it][1] = a.y; v[it][2] = a.z; v[it][3] = a.w;
+      v[it][4] = b.x; v[it][5] = b.y; v[it][6] = b.z; v[it][7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[it][i] = (e0 + i < numel) ? w[e0 + i] : 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      finite = finite && __builtin_isfinite(v[it][i]);
+      m = fmaxf(m, fabsf(v[it][i]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    cmine[it] = m;
+    if ((tid & 7) == 0) s_c[it * (QZ_THREADS / 8) + (tid >> 3)] = m;
+  }
+  if (!finite && status != nullptr) *status = QN_ENONFINITE;
+  __syncthreads();
+
+  // group absmax
+  const float cb_t = s_c[tid];
+  float gm = cb_t;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+  if ((tid & 63) == 0) s_wmax[tid >> 6] = gm;
+  __syncthreads();
+  float smax = s_wmax[0];
+#pragma unroll
+  for (int i = 1; i < QZ_THREADS / 64; ++i) smax = fmaxf(smax, s_wmax[i]);
+  const float d = (smax == 0.0f) ? 0.0f : smax / 255.0f;
+  const int64_t b_this = g * QN_GROUP + tid;
+  if (b_this < nb_total) {
+    float qv = 0.0f;
+    if (smax != 0.0f) qv = fminf(rintf(cb_t / d), 255.0f);
+    qabs[b_this] = static_cast<uint8_t>(qv);
+  }
+  if (tid == 0) gscale[g] = d;
+
+  // NF4 codes against the un-quantized block constant
+  const int64_t nbytes = (numel + 1) / 2;
+#pragma unroll
+  for (int it = 0; it < QZ_PASSES; ++it) {
+    const int64_t e0 = gbase + it * (QZ_THREADS * 8) + tid * 8;
+    if (e0 >= numel) break;
+    const float c = cmine[it];
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float n = (c == 0.0f) ? 0.0f : v[it][i] / c;
+      uint32_t code = 0;
+#pragma unroll
+      for (int j = 0; j < 15; ++j) code += (n > cb.T[j]) ? 1u : 0u;
+      word |= code << (4 * i);
+    }
+    const int64_t byte0 = e0 >> 1;
+    if (byte0 + 4 <= nbytes) {
+      *reinterpret_cast<uint32_t*>(packed + byte0) = word;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (byte0 + i < nbytes) packed[byte0 + i] = (word >> (8 * i)) & 0xFFu;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: dequantization stream.  A wave handles spans of 2048 weights (1 KB of
+// packed codes -> 4 KB of bf16, 32 blocks, inside one double-quant group).
+// Lane l takes packed dword l + 64 j (j = 0..3) of the span, so every load
+// instruction reads 256 contiguous bytes and every store instruction writes
+// 1 KB contiguous (non-temporal); each dword (8 weights) lies in one block
+// and gets that block's 16-entry LUT.  Spans are dealt round-robin to the
+// waves; the next span's loads are issued before the current one is
+// decoded.  Weights past the last whole span are done by k_dequant_tail.
+// ---------------------------------------------------------------------------
+constexpr int DQ_THREADS = 256;
+constexpr int DQ_SPAN = 2048;                 // weights per span
+#ifndef QN_DQ_GRID_CAP
+#define QN_DQ_GRID_CAP 16384
+#endif
+
+struct DqRegs {
+  uint32_t p[4];
+  uint32_t q[4];
+  float d;
+};
+
+// One launch dequantizes up to DQ_BATCH_MAX tensors: their whole spans are
+// numbered consecutively (tensor i owns global spans [span0_i, span0_{i+1})).
+constexpr int DQ_BATCH_MAX = QN_DEQUANT_BATCH_MAX;
+struct DqTensor {
+  const uint8_t* packed;
+  const uint8_t* qabs;
+  const float* gscale;
+  uint16_t* out;
+  int64_t span0;
+};
+struct DqBatch {
+  DqTensor t[DQ_BATCH_MAX];
+  int64_t nspans;       // total whole spans
+  int count;
+};
+
+__global__ __launch_bounds__(DQ_THREADS) void k_dequant(DqBatch b, Codebook cb) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = __builtin_amdgcn_readfirstlane(
+      (int)(((int64_t)blockIdx.x * DQ_THREADS + threadIdx.x) >> 6));
+  const int64_t nwaves = ((int64_t)gridDim.x * DQ_THREADS) >> 6;
+  // tensor owning global span s (wave-uniform scan over <= 16 entries)
+  auto owner = [&](int64_t s) {
+    int i = 0;
+    while (i + 1 < b.count && s >= b.t[i + 1].span0) ++i;
+    return i;
+  };
+  auto load = [&](DqRegs& R, int64_t span) {
+    const bool ok = span < b.nspans;
+    const int ti = ok ? owner(span) : 0;
+    const int64_t sp = ok ? span - b.t[ti].span0 : 0;
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(b.t[ti].packed) + sp * (DQ_SPAN / 8);
+    const uint8_t* qb = b.t[ti].qabs + sp * (DQ_SPAN / 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      R.p[j] = pw[lane + 64 * j];
+      R.q[j] = qb[(lane >> 3) + 8 * j];
+    }
+    R.d = ok ? b.t[ti].gscale[(sp * (DQ_SPAN / 64)) >> 8] : 0.0f;
+  };
+  DqRegs cur;
+  int64_t span = wave0;
+  load(cur, span);
+  for (; span < b.nspans; span += nwaves) {
+    DqRegs nxt;
+    load(nxt, span + nwaves);
+    const int ti = owner(span);
+    u32x4* o = reinterpret_cast<u32x4*>(b.t[ti].out + (span - b.t[ti].span0) * DQ_SPAN);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const Lut t = make_lut(cb, static_cast<float>(cur.q[j]) * cur.d);
+      // streaming store: the output is not re-read here, and keeping it out
+      // of L2 avoids a large write-back when the kernel retires
+      __builtin_nontemporal_store(decode8(cur.p[j], t), &o[lane + 64 * j]);
+    }
+    cur = nxt;
+  }
+}
+
+__global__ __launch_bounds__(DQ_THREADS) void k_dequant_tail(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
+    const float* __restrict__ gscale, int64_t e0, int64_t numel,
+    uint16_t* __restrict__ out, Codebook cb) {
+  const int64_t e = e0 + (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x;
+  if (e >= numel) return;
+  const uint32_t byte = packed[e >> 1];
+  const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xFu);
+  out[e] = decode1(cb, code, block_cprime(qabs, gscale, e >> 6));
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4_quantize(const float* w, const nf4_tensor* out, int32_t* status_dev,
+                 void* stream) {
+  if (w == nullptr || !valid_tensor(out) || !aligned16(w)) return QN_EINVAL;
+  const int64_t numel = out->rows * out->cols;
+  const int64_t nb = cdiv(numel, QN_BLOCK);
+  const int64_t ng = cdiv(nb, QN_GROUP);
+  if (ng > 0x7FFFFFFFLL) return QN_EINVAL;
+  QN_LAUNCH("k_quantize", k_quantize, dim3((unsigned)ng), dim3(QZ_THREADS),
+            (hipStream_t)stream, w, numel, out->packed, out->qabs,
+            out->gscale, status_dev, qn::codebook());
+  return check_launch();
+}
+
+int nf4_dequantize_batch(const nf4_tensor* w, uint16_t* const* w_bf16,
+                         int32_t count, void* stream) {
+  if (w == nullptr || w_bf16 == nullptr || count < 1 || count > DQ_BATCH_MAX)
+    return QN_EINVAL;
+  DqBatch b;
+  std::memset(&b, 0, sizeof(b));
+  int64_t spans = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!valid_tensor(&w[i]) || w_bf16[i] == nullptr || !aligned16(w_bf16[i]))
+      return QN_EINVAL;
+    b.t[i] = DqTensor{w[i].packed, w[i].qabs, w[i].gscale, w_bf16[i], spans};
+    spans += w[i].rows * w[i].cols / DQ_SPAN;
+  }
+  b.nspans = spans;
+  b.count = count;
+  hipStream_t st = (hipStream_t)stream;
+  if (spans > 0) {
+    // up to 64 waves per CU; larger passes walk several spans per wave
+    const int64_t grid = std::min<int64_t>(cdiv(spans, DQ_THREADS / 64), QN_DQ_GRID_CAP);
+    QN_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(DQ_THREADS),
+              st, b, qn::codebook());
+  }
+  for (int i = 0; i < count; ++i) {
+    const int64_t numel = w[i].rows * w[i].cols;
+    const int64_t e0 = numel / DQ_SPAN * DQ_SPAN;
+    if (e0 < numel)
+      QN_LAUNCH("k_dequant_tail", k_dequant_tail,
+                dim3((unsigned)cdiv(numel - e0, DQ_THREADS)), dim3(DQ_THREADS),
+                st, w[i].packed, w[i].qabs, w[i].gscale, e0, numel, w_bf16[i],
+                qn::codebook());
+  }
+  return check_launch();
+}
+
+int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream) {
+  return nf4_dequantize_batch(w, &w_bf16, 1, stream);
+}
+
+}  // extern "C"

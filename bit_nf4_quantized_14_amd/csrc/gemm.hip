@@ -1,0 +1,456 @@
+// Fused dequant + MFMA GEMM of the QLoRA NF4 library (the forward and
+// backward base products).  "QLoRA Guide" (Forward pass diagram: dequantize
+// W to bf16, multiply, add the adapter path) and the "QLORA ... paper
+// summary" (Notes: dequantize to BF16, then matmul; gradients for the
+// adapters only, through the dequantized weight for dX).
+#include "qn_host.h"
+
+namespace {
+
+using namespace qn;
+
+// ---------------------------------------------------------------------------
+// K3/K4: fused dequant + MFMA GEMM, one template for both directions.
+//
+//   forward  (BWD = false): Y[M,N]  = X[M,K]  W'^T  + (s T) B^T
+//   backward (BWD = true) : dX[M,K] = dY[M,N] W'    + (s G) A
+//
+// Output tile BM x BN, reduction step 64.  The 256 x 256 tile runs 8 waves
+// (2 x 4, two waves per SIMD, 128 x 64 of the output each), the 128 x 128
+// tile 4 waves (2 x 2, 64 x 64 each), as tiles of v_mfma_f32_32x32x16_bf16
+// with fp32 accumulators.  With two waves on a SIMD, one wave's LDS writes,
+// buffer loads and dequantization issue while the other's MFMAs run; a
+// single wave has to issue all of them between its own MFMAs.
+//
+// Per reduction step:
+//  * the A tile (X or dY rows, bf16) is loaded into registers (16 bytes per
+//    thread per chunk) and written to LDS after the step's MFMAs: 128-byte
+//    rows with the 16-byte chunk index XOR-swizzled by (row / 2) & 7, so the
+//    16 lanes of one ds_read_b128 phase (16 rows) cover all 64 LDS banks;
+//  * the weight tile arrives as packed nibbles (16 bytes = 32 weights per
+//    thread) + the 8-bit block code + the group scale in registers; each
+//    thread builds its block's 16-entry bf16 LUT (v_perm) and dequantizes
+//    into LDS.  Forward: W' [BN rows n][64 k], 128-byte rows, swizzled like
+//    A, read as MFMA B operands with ds_read_b128.  Backward: W' [64 rows
+//    n][BN k], chunks XOR-swizzled by bwd_swz, read column-wise with
+//    ds_read_b64_tr_b16.
+// LDS is double-buffered.  While the MFMAs consume step i, the A tile of
+// step i+1 streams into the other buffer and the weight tile of step i+1
+// (loaded one step earlier) is dequantized into it; the dequantization is
+// woven between the MFMAs in fenced groups (one MFMA, then up to six VALU
+// ops).  Global loads go through buffer resources whose range check returns
+// zeros, which covers ragged M, N and K tiles without branches.
+// The adapter term is 2r extra reduction steps with the A side s*T (or s*G)
+// split into bf16 hi + lo parts, so the fp32 intermediate keeps ~16
+// mantissa bits.
+// ---------------------------------------------------------------------------
+constexpr int G_BK = 64;
+
+template <int BM, int BN, bool BWD>
+struct GemmCfg {
+  static constexpr int WAVES_M = 2, WAVES_N = BN == 256 ? 4 : 2;
+  static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;  // per-wave tile
+  static constexpr int TM = WM / 32, TN = WN / 32;             // MFMA tiles
+  static constexpr int A_BYTES = BM * 128;                     // swizzled
+  static constexpr int A_CHUNKS = BM * 8 / NT;                 // 16 B per thread
+  static constexpr int EPT = 64 * BN / NT;                     // weights/thread
+  static constexpr int WDW = EPT / 8;                          // packed dwords
+  // threads per weight row: forward rows are 64 weights, backward rows BN
+  static constexpr int TPR = BWD ? BN / EPT : 64 / EPT;
+  static constexpr int PW = BWD ? BN : G_BK;                   // row pitch
+  static constexpr int W_BYTES = 64 * BN * 2;
+  static constexpr int MFMAS = 4 * TM * TN;                    // per step
+  static_assert(EPT == 32 && WDW == 4, "one 16-byte load per thread");
+  static_assert(A_CHUNKS * NT == BM * 8, "A tile loads");
+  static_assert(NT == (BN == 256 ? 512 : 256), "k_gemm launch bounds");
+};
+
+// XOR for the 16-byte chunk index c of row r of the backward weight tile
+// [64][BN]: the 16 lanes of a ds_write_b128 phase and the 32 lanes of a
+// ds_read_b64_tr_b16 phase each cover all 64 LDS banks.
+template <int BN>
+__device__ __forceinline__ int bwd_swz(int r, int c) {
+  return BN == 256 ? 4 * (r & 3) + 2 * (r & 1) + ((c >> 4) & 1) : 5 * (r & 3);
+}
+
+// Packed weight bytes of one step for one thread (32 weights), plus its
+// block code and group scale (raw; c' = q * d is formed when the tile is
+// dequantized).
+struct WRegs {
+  u32x4 w;
+  uint32_t q;
+  float d;
+};
+
+// Where a thread's dequantized weights go: its 16-byte chunk d (8 weights)
+// is stored at base + 8 * (d ^ x).
+struct WDst {
+  uint16_t* base;
+  int x;
+};
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ WDst gemm_wdst(uint16_t* sW, int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+  const int row = tid / C::TPR, c0 = (tid % C::TPR) * (C::EPT / 8);
+  const int x = BWD ? bwd_swz<BN>(row, c0) : ((row >> 1) & 7);
+  // c0 is a multiple of 4 and d < 4: (c0 + d) ^ x = (c0 ^ (x & ~3)) + (d ^ (x & 3))
+  return {sW + row * C::PW + 8 * (c0 ^ (x & ~3)), x & 3};
+}
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_load_w(WRegs& R, rsrc_t rp, rsrc_t rq,
+                                            rsrc_t rd, int N, int K, int c0,
+                                            int red0, int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+  int n, k;
+  if (!BWD) {
+    n = c0 + tid / C::TPR;           // output column = weight row
+    k = red0 + (tid % C::TPR) * C::EPT;
+  } else {
+    n = red0 + tid / C::TPR;         // reduction index = weight row
+    k = c0 + (tid % C::TPR) * C::EPT;
+  }
+  const bool ok = n < N && k < K;
+  const int64_t e = (int64_t)n * K + k;
+  const uint32_t op = ok ? (uint32_t)(e >> 1) : G_OOB;
+  const uint32_t ob = ok ? (uint32_t)(e >> 6) : G_OOB;
+  const uint32_t og = ok ? (uint32_t)((e >> 14) << 2) : G_OOB;
+  R.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op, 0, 0));
+  R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, ob, 0, 0);
+  R.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, og, 0, 0));
+}
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_dequant_w(const WRegs& R, uint16_t* sW,
+                                               const Codebook& cb, int tid) {
+  const WDst dst = gemm_wdst<BM, BN, BWD>(sW, tid);
+  const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
+  const uint32_t wd[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = decode8(wd[d], t);
+}
+
+// A tile of one step: 16-byte global loads into registers (thread t takes
+// chunks q = t + NT i; chunk q is row q / 8, 16-byte column q % 8, so eight
+// consecutive lanes read one 128-byte row segment), written to LDS after the
+// step's MFMAs at the row's swizzled slot (q % 8) ^ ((row / 2) & 7).
+// (A buffer_load ... lds per 1 KB costs the issuing SIMD far more than a
+// load plus a ds_write_b128.)
+template <int BM, int BN, bool BWD>
+struct ARegs {
+  u32x4 v[GemmCfg<BM, BN, BWD>::A_CHUNKS];
+};
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_load_a(ARegs<BM, BN, BWD>& R, rsrc_t ra,
+                                            int M, int KRED, int m0, int red0,
+                                            int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+#pragma unroll
+  for (int i = 0; i < C::A_CHUNKS; ++i) {
+    const int q = tid + C::NT * i, row = q >> 3;
+    const int col = red0 + 8 * (q & 7);
+    const bool ok = m0 + row < M && col < KRED;
+    const uint32_t off =
+        ok ? (uint32_t)(((int64_t)(m0 + row) * KRED + col) * 2) : G_OOB;
+    R.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+  }
+}
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_store_a(const ARegs<BM, BN, BWD>& R,
+                                             char* sA, int tid) {
+  using C = GemmCfg<BM, BN, BWD>;
+#pragma unroll
+  for (int i = 0; i < C::A_CHUNKS; ++i) {
+    const int q = tid + C::NT * i, row = q >> 3;
+    *reinterpret_cast<u32x4*>(sA + row * 128 + (((q & 7) ^ ((row >> 1) & 7)) << 4)) = R.v[i];
+  }
+}
+
+// Transposed B operand for the backward: lane l needs 8 consecutive
+// reduction rows (8 * (l / 32) ...) of output column (col0 + l % 32).  Each
+// ds_read_b64_tr_b16 serves 4 rows: in every group of 16 lanes, lane
+// q = 4j + p addresses row j, columns 4p..4p+3 of the group's 16 columns,
+// and lane q receives column q of the 4 rows.
+template <int BN>
+__device__ __forceinline__ u32x4 lds_read_bT(const uint16_t* sW, int row0,
+                                             int col0, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const int grp = lane >> 4, q = lane & 15;
+  const int row = row0 + 8 * (grp >> 1) + (q >> 2);
+  const int col = col0 + 16 * (grp & 1) + 4 * (q & 3);
+  // rows row and row + 4 have the same swizzle (it depends on row & 3)
+  const int pc = (((col >> 3) ^ bwd_swz<BN>(row, col >> 3)) << 3) | (col & 7);
+  const uint16_t* p0 = sW + row * BN + pc;
+  const uint16_t* p1 = p0 + 4 * BN;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const_cast<uint16_t*>(p0)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(const_cast<uint16_t*>(p1)));
+  u32x4 r;
+  r.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  r.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  r.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  r.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return r;
+}
+
+// 16 bytes of row r, logical chunk c of a 128-byte-row tile swizzled by
+// (r / 2) & 7 (the A tile, and the forward weight tile).
+__device__ __forceinline__ u32x4 lds_read_row128(const void* t, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(t) + r * 128 +
+                                         ((c ^ ((r >> 1) & 7)) << 4));
+}
+
+// Fragments of one k16 slice: A rows and B columns.
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_frags(const char* sA, const uint16_t* sW,
+                                           int wm, int wn, int lane, int kk,
+                                           u32x4 (&a)[GemmCfg<BM, BN, BWD>::TM],
+                                           u32x4 (&b)[GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
+  const int chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+    a[i] = lds_read_row128(sA, wm * C::WM + i * 32 + (lane & 31), chunk);
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    if (!BWD)
+      b[j] = lds_read_row128(sW, wn * C::WN + j * 32 + (lane & 31), chunk);
+    else
+      b[j] = lds_read_bT<BN>(sW, kk * 16, wn * C::WN + j * 32, lane);
+  }
+}
+
+// VALU instructions placed after each MFMA by the interleaving below.
+constexpr int G_VALU_PER_MFMA = 6;
+
+// The four k16 slices of one step with the dequantization of the next weight
+// tile woven in: one decode8 (28 VALU ops and a 16-byte LDS write) after
+// every MPD MFMAs, each group fenced and ordered MFMA / VALU so the VALU
+// work issues in the shadow of the MFMAs instead of after them.
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_mma_deq(
+    const char* sA, const uint16_t* sW, uint16_t* sWn, const WRegs& R,
+    const Codebook& cb, int wm, int wn, int tid, int lane,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
+  constexpr int MPK = C::TM * C::TN;     // MFMAs per k16 slice
+  constexpr int DPK = C::WDW / 4;        // decode8 per k16 slice
+  constexpr int MPD = MPK / DPK;         // MFMAs per decode8
+  static_assert(C::WDW % 4 == 0 && MPK % DPK == 0, "decode split");
+  const WDst dst = gemm_wdst<BM, BN, BWD>(sWn, tid);
+  const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
+  const uint32_t wd[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+  u32x4 a[2][C::TM], b[2][C::TN];
+  gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, 0, a[0], b[0]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kk < 3)
+      gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, kk + 1, a[(kk + 1) & 1],
+                              b[(kk + 1) & 1]);
+#pragma unroll
+    for (int g = 0; g < MPK; ++g) {
+      const int i = g / C::TN, j = g % C::TN;
+      acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
+      if (g % MPD == MPD - 1) {
+        const int d = kk * DPK + g / MPD;
+        *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = decode8(wd[d], t);
+#pragma unroll
+        for (int h = 0; h < MPD; ++h) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, G_VALU_PER_MFMA, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// Maps the linear workgroup index to an output tile so that each XCD (the
+// hardware deals workgroups round-robin over 8 XCDs) works on a contiguous
+// run of tiles, and runs walk the N direction first: a run shares A rows in
+// that XCD's L2.
+__device__ __forceinline__ void gemm_tile_of(int tiles_m, int tiles_n,
+                                             int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  tm = pid / tiles_n;
+  tn = pid % tiles_n;
+}
+
+// One reduction step: MFMAs on (sAc, sWc) while the next A tile streams into
+// sAn and the weight tile held in Wc is dequantized into sWn.
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_step(
+    int st, char* sAc, uint16_t* sWc, char* sAn, uint16_t* sWn, WRegs& Wc,
+    rsrc_t ra, rsrc_t rp, rsrc_t rq, rsrc_t rd, int M, int N, int K, int KRED,
+    int m0, int c0, int wave, int wm, int wn, int tid, int lane,
+    const Codebook& cb,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  WRegs Wn;
+  ARegs<BM, BN, BWD> An;
+  gemm_load_a<BM, BN, BWD>(An, ra, M, KRED, m0, (st + 1) * G_BK, tid);
+  gemm_load_w<BM, BN, BWD>(Wn, rp, rq, rd, N, K, c0, (st + 2) * G_BK, tid);
+  gemm_mma_deq<BM, BN, BWD>(sAc, sWc, sWn, Wc, cb, wm, wn, tid, lane, acc);
+  gemm_store_a<BM, BN, BWD>(An, sAn, tid);
+  __builtin_amdgcn_s_waitcnt(0);   // all counters: loads and LDS writes done
+  __syncthreads();
+  Wc = Wn;
+}
+
+template <int BM, int BN, bool BWD>
+__global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
+    const uint16_t* __restrict__ Aop, const uint8_t* __restrict__ packed,
+    const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
+    const uint16_t* __restrict__ La_hi, const uint16_t* __restrict__ La_lo,
+    const uint16_t* __restrict__ Lb, int M, int N, int K, int rpad,
+    void* __restrict__ out, int out_bf16, Codebook cb) {
+  using C = GemmCfg<BM, BN, BWD>;
+  // Four distinct LDS buffers so that the compiler can see that the tiles
+  // being filled never alias the tiles being read.
+  __shared__ __attribute__((aligned(16))) char sA0[C::A_BYTES];
+  __shared__ __attribute__((aligned(16))) char sA1[C::A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint16_t sW0[C::W_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t sW1[C::W_BYTES / 2];
+  const int NOUT = BWD ? K : N;        // output columns
+  const int KRED = BWD ? N : K;        // reduction length
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  int tm, tn;
+  gemm_tile_of((M + BM - 1) / BM, (NOUT + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, c0 = tn * BN;
+
+  const int64_t numel = (int64_t)N * K;
+  const rsrc_t ra = make_rsrc(Aop, (uint32_t)((int64_t)M * KRED * 2));
+  const rsrc_t rp = make_rsrc(packed, (uint32_t)((numel + 1) >> 1));
+  const rsrc_t rq = make_rsrc(qabs, (uint32_t)((numel + 63) >> 6));
+  const rsrc_t rd = make_rsrc(gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
+
+  f32x16 acc[C::TM][C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // Steps past the end read out of range: their tiles are zeros (a zero
+  // block constant dequantizes every code to zero), so the loop runs whole
+  // pairs of steps without branches.
+  const int nsteps = (KRED + G_BK - 1) / G_BK;
+  WRegs Wc;
+  {
+    ARegs<BM, BN, BWD> A0;
+    gemm_load_a<BM, BN, BWD>(A0, ra, M, KRED, m0, 0, tid);
+    gemm_store_a<BM, BN, BWD>(A0, sA0, tid);
+  }
+  gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, 0, tid);
+  gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);
+  gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, G_BK, tid);
+  __builtin_amdgcn_s_waitcnt(0);   // all counters: loads landed in LDS/regs
+  __syncthreads();
+  for (int st = 0; st < nsteps; st += 2) {
+    gemm_step<BM, BN, BWD>(st, sA0, sW0, sA1, sW1, Wc, ra, rp, rq, rd, M, N, K,
+                           KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
+    gemm_step<BM, BN, BWD>(st + 1, sA1, sW1, sA0, sW0, Wc, ra, rp, rq, rd, M, N,
+                           K, KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
+  }
+
+  // Adapter term, 2 * rpad more reduction steps straight from global memory
+  // (small, L2-resident arrays): A side the bf16 hi and lo parts of s*T
+  // (forward) or s*G (backward), [M][rpad]; B side [NOUT][rpad], B (forward)
+  // or A^T (backward), zero-padded to rpad columns.
+  {
+    const rsrc_t rh = make_rsrc(La_hi, (uint32_t)((int64_t)M * rpad * 2));
+    const rsrc_t rl = make_rsrc(La_lo, (uint32_t)((int64_t)M * rpad * 2));
+    const rsrc_t rb = make_rsrc(Lb, (uint32_t)((int64_t)NOUT * rpad * 2));
+    for (int j0 = 0; j0 < rpad; j0 += 16) {
+      const int jc = j0 + 8 * (lane >> 5);
+      u32x4 ah[C::TM], al[C::TM], b[C::TN];
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const uint32_t off =
+            (uint32_t)(((int64_t)(m0 + wm * C::WM + i * 32 + (lane & 31)) * rpad + jc) * 2);
+        ah[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+        al[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const uint32_t off =
+            (uint32_t)(((int64_t)(c0 + wn * C::WN + j * 32 + (lane & 31)) * rpad + jc) * 2);
+        b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+          acc[i][j] = mfma32(ah[i], b[j], acc[i][j]);
+          acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * C::WM + i * 32 + 8 * (v >> 2) +
+                        4 * (lane >> 5) + (v & 3);
+        const int col = c0 + wn * C::WN + j * 32 + (lane & 31);
+        if (row < M && col < NOUT)
+          store_out(out, out_bf16, (int64_t)row * NOUT + col, acc[i][j][v]);
+      }
+}
+
+}  // namespace
+
+namespace qn {
+
+// Fused GEMM launch: 256 x 256 tiles when they give at least ~one
+// workgroup per CU, otherwise 128 x 128.
+template <int BM, int BN, bool BWD>
+void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
+                   const uint16_t* La_hi, const uint16_t* La_lo,
+                   const uint16_t* Lb, int M, int rpad, void* out,
+                   int out_bf16) {
+  const int N = (int)w->rows, K = (int)w->cols;
+  const int nout = BWD ? K : N;
+  const unsigned tiles = (unsigned)(cdiv(M, BM) * cdiv(nout, BN));
+  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD>),
+            dim3(tiles), dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs, w->gscale,
+            La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16, qn::codebook());
+}
+
+template <bool BWD>
+void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
+                 const uint16_t* La_hi, const uint16_t* La_lo,
+                 const uint16_t* Lb, int M, int rpad, void* out,
+                 int out_bf16) {
+  const int64_t nout = BWD ? w->cols : w->rows;
+  if (cdiv(M, 256) * cdiv(nout, 256) >= 192)
+    launch_gemm_t<256, 256, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
+                                 out_bf16);
+  else
+    launch_gemm_t<128, 128, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
+                                 out_bf16);
+}
+
+template void launch_gemm<false>(hipStream_t, const uint16_t*, const nf4_tensor*,
+                                 const uint16_t*, const uint16_t*,
+                                 const uint16_t*, int, int, void*, int);
+template void launch_gemm<true>(hipStream_t, const uint16_t*, const nf4_tensor*,
+                                const uint16_t*, const uint16_t*,
+                                const uint16_t*, int, int, void*, int);
+
+}  // namespace qn

@@ -1,0 +1,247 @@
+// C entry points of the fused QLoRA linear layer (forward, backward,
+// workspace sizes) and the library's shared host state: the codebook
+// kernel argument, argument validation, error strings and the profiling
+// hook.  "QLoRA Guide" (Forward pass diagram: W_bf16 x + B(A(x)); only A
+// and B get gradients), "QLoRA Implementation Details (2025 Edition)"
+// (Step 4: scale alpha / r).
+#include "qn_host.h"
+
+namespace qn {
+
+ProfileHook g_prof;
+
+const Codebook& codebook() {
+  static const Codebook cb = [] {
+    Codebook c;
+    derive_codebook(c.L, c.T);
+    return c;
+  }();
+  return cb;
+}
+
+bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
+  if (!valid_tensor(w) || M <= 0) return false;
+  if (r < 1 || r > QN_MAX_RANK) return false;
+  const int64_t N = w->rows, K = w->cols;
+  if (K % QN_BLOCK != 0 || N % 8 != 0) return false;
+  // 32-bit index arithmetic inside the GEMM kernels
+  if (M > (1LL << 30) || N > (1LL << 30) || K > (1LL << 30)) return false;
+  // buffer-resource ranges are 32-bit byte counts (offsets past 2^31 mean
+  // "out of range"): every operand read through one stays below 2 GiB
+  const int64_t lim = 1LL << 31;
+  if (M * K * 2 >= lim || M * N * 2 >= lim || N * K / 2 >= lim) return false;
+  // fp32 rank-r partial rows [N or K][rpad] addressed through a resource
+  if (std::max(N, K) * 4 * 16 * rank_tiles(r) >= lim) return false;
+  return true;
+}
+
+FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
+                                  int32_t r) {
+  FwdWorkspace L{};
+  L.rpad = 16 * rank_tiles(r);
+  if (M <= qn::QN_SKINNY_M) {
+    const SkinnyPlan P = skinny_plan(M, N, K, r);
+    L.slices = P.slices;
+    L.ks = P.ks;
+    L.part = 0;
+    L.total = align256(size_t(P.slices) * M * P.rows_total * 4);
+    return L;
+  }
+  const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r));
+  size_t off = 0;
+  L.th = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.tl = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.bp = off;
+  off += align256(size_t(N) * L.rpad * 2);
+  L.prow = off;
+  off += align256(size_t(P.nb) * M * L.rpad * 4);
+  L.total = off;
+  return L;
+}
+
+BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K,
+                                  int32_t r) {
+  BwdWorkspace L{};
+  const int jt = rank_tiles(r);
+  L.rpad = 16 * jt;
+  L.mp = cdiv(M, 8) * 8;
+  const StreamPlan Pg = stream_plan(RS_ROWS | RS_COLS, M, N, jt);
+  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
+  const size_t pcol = std::max(size_t(Pg.mb) * N, size_t(Pa.mb) * K);
+  size_t off = 0;
+  L.bt = off;
+  off += align256(size_t(r) * N * 2);
+  L.uth = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.utl = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.atp = off;
+  off += align256(size_t(K) * L.rpad * 2);
+  L.gh = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.gl = off;
+  off += align256(size_t(M) * L.rpad * 2);
+  L.ugh = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.ugl = off;
+  off += align256(size_t(r) * L.mp * 2);
+  L.prow = off;
+  off += align256(size_t(Pg.nb) * M * L.rpad * 4);
+  L.pcol = off;
+  off += align256(pcol * L.rpad * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace qn
+
+using namespace qn;
+
+extern "C" {
+
+int qn_profile_kernel(const char* name, void** ev_start, void** ev_stop,
+                      int32_t capacity) {
+  const int32_t recorded = g_prof.count;
+  if (name == nullptr) {
+    g_prof = ProfileHook();
+    return recorded;
+  }
+  if (ev_start == nullptr || ev_stop == nullptr || capacity < 0 ||
+      std::strlen(name) >= sizeof(g_prof.name))
+    return QN_EINVAL;
+  g_prof = ProfileHook();
+  std::strcpy(g_prof.name, name);
+  g_prof.ev_start = ev_start;
+  g_prof.ev_stop = ev_stop;
+  g_prof.capacity = capacity;
+  return recorded;
+}
+
+const char* qn_strerror(int code) {
+  switch (code) {
+    case QN_OK: return "success";
+    case QN_EINVAL: return "invalid argument";
+    case QN_EWORKSPACE: return "workspace too small";
+    case QN_EHIP: return "HIP launch error";
+    case QN_ENONFINITE: return "non-finite weight";
+    default: return "unknown error";
+  }
+}
+
+size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
+                             int32_t which) {
+  if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QN_MAX_RANK) return 0;
+  if (which == QN_FWD) return qn::fwd_workspace_layout(M, N, K, r).total;
+  if (which == QN_BWD) return qn::bwd_workspace_layout(M, N, K, r).total;
+  return 0;
+}
+
+int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
+                     const uint16_t* A, const uint16_t* B, int32_t r,
+                     float alpha, void* y, int32_t y_dtype, float* t_save,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (x == nullptr || A == nullptr || B == nullptr || y == nullptr ||
+      t_save == nullptr)
+    return QN_EINVAL;
+  if (!valid_linear(M, w, r)) return QN_EINVAL;
+  if (y_dtype != QN_F32 && y_dtype != QN_BF16) return QN_EINVAL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(y) || !aligned16(t_save))
+    return QN_EINVAL;
+  const int64_t N = w->rows, K = w->cols;
+  const qn::FwdWorkspace L = qn::fwd_workspace_layout(M, N, K, r);
+  if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
+    return QN_EWORKSPACE;
+  const float s = alpha / (float)r;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
+  hipStream_t st = (hipStream_t)stream;
+  if (M <= qn::QN_SKINNY_M) {
+    launch_skinny(st, x, Mi, w, A, B, (int)r, L.rpad, s, t_save, y,
+                  (int)(y_dtype == QN_BF16), ws_at<float>(ws, L.part));
+    return check_launch();
+  }
+  uint16_t* Th = ws_at<uint16_t>(ws, L.th);
+  uint16_t* Tl = ws_at<uint16_t>(ws, L.tl);
+  uint16_t* Bp = ws_at<uint16_t>(ws, L.bp);
+  float* prow = ws_at<float>(ws, L.prow);
+  const int jt = rank_tiles(r);
+  // T = X A^T: partials over column blocks of X
+  const StreamPlan P = stream_plan(RS_ROWS, M, K, jt);
+  launch_rank_stream<RS_ROWS>(st, "k_rank_stream_t", P, x, Mi, Ki, A, (int)r,
+                              nullptr, nullptr, 0, prow, nullptr);
+  // T (fp32, saved), hi/lo parts of s T, B zero-padded to [N][rpad]
+  FinishArgs fa = finish_args();
+  fa.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, P.nb, Mi, Mi, (int)r,
+                    L.rpad, s, t_save, Th, Tl, nullptr, nullptr};
+  fa.P1 = FinishPad{B, Bp, Ni, L.rpad, (int)r, (int64_t)r, (int64_t)1};
+  launch_finish(st, fa);
+  launch_gemm<false>(st, x, w, Th, Tl, Bp, Mi, L.rpad, y,
+                     (int)(y_dtype == QN_BF16));
+  return check_launch();
+}
+
+int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
+                     const nf4_tensor* w, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha,
+                     const float* t_saved, void* dx, int32_t dx_dtype,
+                     float* dA, float* dB, void* ws, size_t ws_bytes,
+                     void* stream) {
+  if (dy == nullptr || x == nullptr || A == nullptr || B == nullptr ||
+      t_saved == nullptr || dx == nullptr || dA == nullptr || dB == nullptr)
+    return QN_EINVAL;
+  if (!valid_linear(M, w, r)) return QN_EINVAL;
+  if (dx_dtype != QN_F32 && dx_dtype != QN_BF16) return QN_EINVAL;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(A) || !aligned16(dx))
+    return QN_EINVAL;
+  const int64_t N = w->rows, K = w->cols;
+  const qn::BwdWorkspace L = qn::bwd_workspace_layout(M, N, K, r);
+  if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
+    return QN_EWORKSPACE;
+  uint16_t* Bt = ws_at<uint16_t>(ws, L.bt);
+  uint16_t* UTh = ws_at<uint16_t>(ws, L.uth);
+  uint16_t* UTl = ws_at<uint16_t>(ws, L.utl);
+  uint16_t* Atp = ws_at<uint16_t>(ws, L.atp);
+  uint16_t* Gh = ws_at<uint16_t>(ws, L.gh);
+  uint16_t* Gl = ws_at<uint16_t>(ws, L.gl);
+  uint16_t* UGh = ws_at<uint16_t>(ws, L.ugh);
+  uint16_t* UGl = ws_at<uint16_t>(ws, L.ugl);
+  float* prow = ws_at<float>(ws, L.prow);
+  float* pcol = ws_at<float>(ws, L.pcol);
+  const float s = alpha / (float)r;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K, Mp = (int)L.mp;
+  const int jt = rank_tiles(r);
+  hipStream_t st = (hipStream_t)stream;
+
+  // s T transposed (hi/lo), A^T padded to [K][rpad], B^T
+  FinishArgs f0 = finish_args();
+  f0.R = FinishRows{t_saved, 0, (int)r, 1, Mi, Mp, (int)r, L.rpad, s,
+                    nullptr, nullptr, nullptr, UTh, UTl};
+  f0.P1 = FinishPad{A, Atp, Ki, L.rpad, (int)r, (int64_t)1, K};
+  f0.P2 = FinishPad{B, Bt, (int)r, Ni, Ni, (int)1, (int64_t)r};
+  launch_finish(st, f0);
+  // one pass over dY: G = dY B (column-block partials), dB = dY^T (s T)
+  // (row-block partials)
+  const StreamPlan Pg = stream_plan(RS_ROWS | RS_COLS, M, N, jt);
+  launch_rank_stream<RS_ROWS | RS_COLS>(st, "k_rank_stream_dy", Pg, dy, Mi, Ni,
+                                        Bt, (int)r, UTh, UTl, Mp, prow, pcol);
+  // hi/lo parts of s G (row-major and transposed), dB
+  FinishArgs f1 = finish_args();
+  f1.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, Pg.nb, Mi, Mp, (int)r,
+                    L.rpad, s, nullptr, Gh, Gl, UGh, UGl};
+  f1.Cc = FinishCols{pcol, Pg.mb, Ni, (int)r, L.rpad, dB, (int64_t)r, 1};
+  launch_finish(st, f1);
+  // dX = dY W' + (s G) A
+  launch_gemm<true>(st, dy, w, Gh, Gl, Atp, Mi, L.rpad, dx,
+                    (int)(dx_dtype == QN_BF16));
+  // dA = (s G)^T X: row-block partials of out[k][j] -> dA[j][k]
+  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
+  launch_rank_stream<RS_COLS>(st, "k_rank_stream_da", Pa, x, Mi, Ki, nullptr,
+                              (int)r, UGh, UGl, Mp, nullptr, pcol);
+  FinishArgs f2 = finish_args();
+  f2.Cc = FinishCols{pcol, Pa.mb, Ki, (int)r, L.rpad, dA, (int64_t)1, K};
+  launch_finish(st, f2);
+  return check_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// Device-side pieces shared by the kernels of the QLoRA NF4 library: vector
+// types, the codebook kernel argument, bf16 helpers, the per-block bf16
+// lookup table and nibble decoders, MFMA wrappers and buffer resources.
+// Every function is inline; each translation unit keeps its kernels in an
+// anonymous namespace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Codebook passed by value as a kernel argument (lands in SGPRs).
+struct Codebook {
+  float L[16];
+  float T[15];
+};
+
+// ---------------------------------------------------------------------------
+// bf16 helpers
+// ---------------------------------------------------------------------------
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1,
+                                         uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// (mask & a) | (~mask & b), a single v_bfi_b32.
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a,
+                                        uint32_t b) {
+  return (mask & a) | (~mask & b);
+}
+
+// ---------------------------------------------------------------------------
+// NF4 decode: per-block 16-entry bf16 table, byte-sliced for v_perm_b32.
+//
+// For one block with constant c' = float(q) * d, entry j is
+// bf16_rne(L[j] * c') (both products fp32).  The 16 bf16 entries are kept as
+// four 8-byte tables: low bytes of entries 0-7 (ll) and 8-15 (lh), high
+// bytes of entries 0-7 (hl) and 8-15 (hh).  A code's low 3 bits select a
+// byte with v_perm_b32; its bit 3 chooses between the two halves.
+// ---------------------------------------------------------------------------
+struct Lut {
+  uint32_t ll0, ll1, lh0, lh1, hl0, hl1, hh0, hh1;
+};
+
+__device__ __forceinline__ float block_cprime(const uint8_t* __restrict__ qabs,
+                                              const float* __restrict__ gscale,
+                                              int64_t block) {
+  return static_cast<float>(qabs[block]) * gscale[block >> 8];
+}
+
+__device__ __forceinline__ Lut make_lut(const Codebook& cb, float cp) {
+  uint32_t P[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    P[k] = pack_bf16x2(cb.L[2 * k] * cp, cb.L[2 * k + 1] * cp);
+  Lut t;
+  // P[k] bytes: [lo e2k, hi e2k, lo e2k+1, hi e2k+1]
+  t.ll0 = perm(P[1], P[0], 0x06040200u);
+  t.hl0 = perm(P[1], P[0], 0x07050301u);
+  t.ll1 = perm(P[3], P[2], 0x06040200u);
+  t.hl1 = perm(P[3], P[2], 0x07050301u);
+  t.lh0 = perm(P[5], P[4], 0x06040200u);
+  t.hh0 = perm(P[5], P[4], 0x07050301u);
+  t.lh1 = perm(P[7], P[6], 0x06040200u);
+  t.hh1 = perm(P[7], P[6], 0x07050301u);
+  return t;
+}
+
+// 8 codes (one packed dword, element i in bits 4i..4i+3) -> 8 bf16 in
+// natural order (out[i] holds elements 2i, 2i+1, low half first).
+__device__ __forceinline__ u32x4 decode8(uint32_t p, const Lut& t) {
+  const uint32_t se = p & 0x07070707u;          // codes 0,2,4,6 (low 3 bits)
+  const uint32_t so = (p >> 4) & 0x07070707u;   // codes 1,3,5,7
+  // 0xFF per byte where bit 3 of the code is set (v_perm sign replication)
+  const uint32_t me = perm(p << 4, p << 12, 0x0B090A08u);
+  const uint32_t mo = perm(p, p << 8, 0x0B090A08u);
+  const uint32_t le = bfi(me, perm(t.lh1, t.lh0, se), perm(t.ll1, t.ll0, se));
+  const uint32_t he = bfi(me, perm(t.hh1, t.hh0, se), perm(t.hl1, t.hl0, se));
+  const uint32_t lo = bfi(mo, perm(t.lh1, t.lh0, so), perm(t.ll1, t.ll0, so));
+  const uint32_t ho = bfi(mo, perm(t.hh1, t.hh0, so), perm(t.hl1, t.hl0, so));
+  // low bytes of elements 0..3 and 4..7, then high bytes
+  const uint32_t l03 = perm(lo, le, 0x05010400u);
+  const uint32_t l47 = perm(lo, le, 0x07030602u);
+  const uint32_t h03 = perm(ho, he, 0x05010400u);
+  const uint32_t h47 = perm(ho, he, 0x07030602u);
+  u32x4 r;
+  r.x = perm(h03, l03, 0x05010400u);
+  r.y = perm(h03, l03, 0x07030602u);
+  r.z = perm(h47, l47, 0x05010400u);
+  r.w = perm(h47, l47, 0x07030602u);
+  return r;
+}
+
+// Same lookup as decode8, with the 8 outputs in the order
+// (0,2) (4,6) (1,3) (5,7): four v_perm_b32 fewer.  Only usable where the
+// other MFMA operand is permuted the same way (permute8 below), because the
+// order of a dot product's terms is free.
+__device__ __forceinline__ u32x4 decode8p(uint32_t p, const Lut& t) {
+  const uint32_t se = p & 0x07070707u;
+  const uint32_t so = (p >> 4) & 0x07070707u;
+  const uint32_t me = perm(p << 4, p << 12, 0x0B090A08u);
+  const uint32_t mo = perm(p, p << 8, 0x0B090A08u);
+  const uint32_t le = bfi(me, perm(t.lh1, t.lh0, se), perm(t.ll1, t.ll0, se));
+  const uint32_t he = bfi(me, perm(t.hh1, t.hh0, se), perm(t.hl1, t.hl0, se));
+  const uint32_t lo = bfi(mo, perm(t.lh1, t.lh0, so), perm(t.ll1, t.ll0, so));
+  const uint32_t ho = bfi(mo, perm(t.hh1, t.hh0, so), perm(t.hl1, t.hl0, so));
+  u32x4 r;
+  r.x = perm(he, le, 0x05010400u);   // elements 0, 2
+  r.y = perm(he, le, 0x07030602u);   // elements 4, 6
+  r.z = perm(ho, lo, 0x05010400u);   // elements 1, 3
+  r.w = perm(ho, lo, 0x07030602u);   // elements 5, 7
+  return r;
+}
+
+// 8 consecutive bf16 (natural order) -> the order of decode8p.
+__device__ __forceinline__ u32x4 permute8(const u32x4& v) {
+  u32x4 r;
+  r.x = perm(v.y, v.x, 0x05040100u);
+  r.y = perm(v.w, v.z, 0x05040100u);
+  r.z = perm(v.y, v.x, 0x07060302u);
+  r.w = perm(v.w, v.z, 0x07060302u);
+  return r;
+}
+
+// One element, used for ragged tails.
+__device__ __forceinline__ uint16_t decode1(const Codebook& cb, uint32_t code,
+                                            float cp) {
+  return static_cast<uint16_t>(pack_bf16x2(cb.L[code] * cp, 0.0f) & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA helpers.  v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of A
+// and column (l % 32) of B, each with 8 consecutive reduction elements
+// starting at 8 * (l / 32).  Accumulator register v of lane l holds
+// C[8 * (v / 4) + 4 * (l / 32) + (v % 4)][l % 32].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b,
+                                         const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+      0);
+}
+
+// v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16) of A and column
+// (l % 16) of B with 8 reduction elements from 8 * (l / 16); accumulator v
+// of lane l holds C[4 * (l / 16) + v][l % 16].
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b,
+                                        const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+      0);
+}
+
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi,
+                                           uint16_t& lo) {
+  const uint32_t h = pack_bf16x2(x, 0.0f) & 0xFFFFu;
+  const float rest = x - bf16_to_f32(h);
+  hi = static_cast<uint16_t>(h);
+  lo = static_cast<uint16_t>(pack_bf16x2(rest, 0.0f) & 0xFFFFu);
+}
+
+__device__ __forceinline__ void store_out(void* out, int out_bf16,
+                                          int64_t idx, float v) {
+  if (out_bf16)
+    reinterpret_cast<uint16_t*>(out)[idx] =
+        static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+  else
+    reinterpret_cast<float*>(out)[idx] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources: global loads and stores go through a resource whose
+// range check returns zeros (drops stores) past the end, which covers ragged
+// tiles without branches.
+// ---------------------------------------------------------------------------
+constexpr uint32_t G_OOB = 0x80000000u;   // buffer offset past every range
+constexpr int G_RSRC_FLAGS = 0x00020000;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, G_RSRC_FLAGS);
+}
+
+}  // namespace qn
