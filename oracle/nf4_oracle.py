@@ -23,7 +23,7 @@ Sources (the pages, cited by title and section):
   every pass loads 4-bit weights, dequantizes to BF16, multiplies, and
   computes gradients for the adapters only.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * Level construction: the pages fix only "16 levels at N(0,1) quantiles"
   containing an exact zero and +-1.  Read: 8 positive levels at the

@@ -31,7 +31,8 @@ DELTA = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0)
 # --------------------------------------------------------------------------
 
 def test_levels_shape_order_and_anchor_values():
-    # "Qlora Expert", Core Concept: 16 levels; spec: sorted, with -1, 0, +1
+    # "Qlora Expert", Core Concept: 16 levels at N(0,1) quantiles, normalised
+    # to [-1, 1] with an exact 0: sorted, containing -1, 0 and +1
     assert L.dtype == np.float32 and L.shape == (FACTS["nf4_level_count"]["value"],)
     assert np.all(np.diff(L.astype(np.float64)) > 0)
     assert L[0] == -1.0 and L[7] == 0.0 and L[15] == 1.0
@@ -141,7 +142,8 @@ def test_absmax_brute_force():
 
 
 def test_roundtrip_without_dq_within_half_gap_times_absmax():
-    # spec: quantize->dequantize error <= half the level gap x absmax
+    # nearest-level rounding: the round-trip error is at most half the gap
+    # between neighbouring levels, times the block absmax
     w = _small_weight()
     c = oracle.block_absmax(w)
     codes = oracle.nf4_codes(w, c)
