@@ -19,8 +19,10 @@ from .nf4_oracle import (  # noqa: F401
     bf16_bits_to_f64,
     block_absmax,
     bf16_rne_bits,
+    bf16_rne_from_f64,
     double_quantize,
     forward_f64,
+    merge_f64,
     nf4_codes,
     nf4_dequantize,
     nf4_levels,

@@ -113,6 +113,25 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def bf16_rne_from_f64(v) -> np.ndarray:
+    """float64 -> bf16 bit pattern, rounded once to the nearest bf16 value,
+    ties to even (no intermediate fp32 rounding).  Finite inputs only.
+
+    A bf16 value has 8 significant bits: with |v| = f * 2**e, f in [0.5, 1)
+    (frexp, exact), the representable neighbours are integer multiples of
+    2**(e - 8) (of 2**-133 below the normal range), so the rounding is
+    rint(|v| / 2**(e - 8)) -- an exact power-of-two scaling followed by
+    NumPy's round-half-to-even.
+    """
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    _, e = np.frexp(np.abs(a))
+    ulp_exp = np.maximum(e.astype(np.int64) - 8, -133)
+    q = np.rint(np.ldexp(np.abs(a), -ulp_exp))          # exact scaling
+    mag = np.ldexp(q, ulp_exp).astype(np.float32)        # exact in bf16
+    out = np.where(np.signbit(a), -mag, mag).astype(np.float32)
+    return (out.view(np.uint32) >> 16).astype(np.uint16)
+
+
 # ---------------------------------------------------------------------------
 # NF4 block quantization
 # ---------------------------------------------------------------------------
@@ -314,3 +333,25 @@ def qlora_backward(dy_bits, x_bits, w_bits, a_bits, b_bits, alpha: float,
     return backward_f64(bf16_bits_to_f64(dy_bits), bf16_bits_to_f64(x_bits),
                         bf16_bits_to_f64(w_bits), bf16_bits_to_f64(a_bits),
                         bf16_bits_to_f64(b_bits), s, t)
+
+
+# ---------------------------------------------------------------------------
+# Dequantize-and-merge
+# ---------------------------------------------------------------------------
+
+def merge_f64(w_bits, a_bits, b_bits, s: float):
+    """Merged dense weight bf16(W' + s B A) and its exact value.
+
+    "Qlora Expert", When to Use and Common Pitfalls: the adapter can be
+    merged into a dense model only after dequantizing the base, which
+    materialises the full bf16 weight; "QLoRA Implementation Details (2025
+    Edition)", Step 7 (Merge & Save).  Reading: the merged weight is the
+    dequantized base W' [N,K] plus the scaled low-rank update s B A
+    (B [N,r], A [r,K]), computed exactly (float64 on the exact bf16 inputs)
+    and rounded once to bf16.  Returns (bits uint16 [N,K], value float64).
+    """
+    w = bf16_bits_to_f64(w_bits)
+    a = bf16_bits_to_f64(a_bits)
+    b = bf16_bits_to_f64(b_bits)
+    v = w + float(s) * (b @ a)
+    return bf16_rne_from_f64(v), v

@@ -118,3 +118,23 @@ def test_dq_without_rounding_cprime_is_caught(monkeypatch):
         return core.bf16_rne_bits(lv[codes] * cprime)
     _patch(monkeypatch, "nf4_dequantize", bad)
     _fails(pins.test_absmax_element_decodes_to_plus_minus_cprime)
+
+
+def test_merge_rounding_through_fp32_is_caught(monkeypatch):
+    import test_oracle_merge_pins as mpins
+
+    def bad(v):       # rounds twice: float64 -> fp32 -> bf16
+        return core.bf16_rne_bits(np.asarray(v, dtype=np.float64).astype(np.float32))
+    _patch(monkeypatch, "bf16_rne_from_f64", bad)
+    _fails(mpins.test_rne_from_f64_ties_and_near_ties)
+
+
+def test_merge_without_scale_is_caught(monkeypatch):
+    import test_oracle_merge_pins as mpins
+
+    def bad(w_bits, a_bits, b_bits, s):
+        w, a, b = (core.bf16_bits_to_f64(t) for t in (w_bits, a_bits, b_bits))
+        v = w + b @ a
+        return core.bf16_rne_from_f64(v), v
+    _patch(monkeypatch, "merge_f64", bad)
+    _fails(mpins.test_merge_rank_one_by_hand)
