@@ -211,6 +211,31 @@ def bench_dequant_quant(reps, copies=3):
                      "frac_hbm_peak": nbytes / ksum / 1e9 / HBM_PEAK_GBS}
         log(f"{name}: {res[name]['GB/s']:.0f} GB/s graph, "
             f"{res[name]['kernel_GB/s']:.0f} GB/s kernel")
+    # dequantize-and-merge of the same layer with an r = 16, alpha = 32
+    # adapter per projection (one nf4_merge call per projection)
+    mr, malpha = 16, 32.0
+    ads = [(torch.from_numpy(wl.lora_a(wk, p, r=mr)).view(torch.bfloat16).to("cuda"),
+            torch.from_numpy(wl.lora_b(wk, p, r=mr)).view(torch.bfloat16).to("cuda"))
+           for p in range(len(wk.projections))]
+    m_bytes = deq_bytes + sum(2 * mr * (t.rows + t.cols) for t in tens)
+
+    def merge():
+        for c in range(copies):
+            for t, (a, b), o in zip(sets[c], ads, outs):
+                capi.nf4_merge(t, a, b, mr, malpha, o)
+    sec = timed_graph(merge, reps) / copies
+    kt, _ = kernel_times_ms(capi, "k_merge", merge, len(tens) * copies, reps)
+    ksum = kt * len(tens) * 1e-3
+    res["merge7b"] = {"params": params, "r": mr, "alpha": malpha,
+                      "bytes_per_pass": m_bytes, "ms_per_pass": sec * 1e3,
+                      "GB/s": m_bytes / sec / 1e9,
+                      "timing": "graph replay of the 7-projection pass (7 nf4_merge calls), "
+                                f"cycling over {copies} weight copies (> MALL)",
+                      "kernel": "k_merge", "kernel_ms_per_pass": ksum * 1e3,
+                      "kernel_GB/s": m_bytes / ksum / 1e9,
+                      "frac_hbm_peak": m_bytes / sec / 1e9 / HBM_PEAK_GBS}
+    log(f"merge7b (r=16): {res['merge7b']['GB/s']:.0f} GB/s graph, "
+        f"{res['merge7b']['kernel_GB/s']:.0f} GB/s kernel")
     # the same pass as seven separate calls (one launch per projection)
     sec = timed_graph(deq_each, reps) / copies
     res["dequant7b"]["per_call_GB/s"] = deq_bytes / sec / 1e9
@@ -219,7 +244,7 @@ def bench_dequant_quant(reps, copies=3):
                                   f"{copies} weight copies (> MALL); per_call_GB/s: "
                                   "the same pass as 7 nf4_dequantize calls")
     log(f"dequant7b as 7 calls: {res['dequant7b']['per_call_GB/s']:.0f} GB/s graph")
-    del sets, tens, outs, ws32
+    del sets, tens, outs, ws32, ads
     torch.cuda.empty_cache()
     return res
 

@@ -25,7 +25,7 @@ QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 256
 
 # Every symbol the header declares (tests check the library exports them).
 EXPORTS = ("nf4_codebook", "nf4_quantize", "nf4_dequantize",
-           "nf4_dequantize_batch",
+           "nf4_dequantize_batch", "nf4_merge",
            "qlora_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
            "qn_strerror", "qn_profile_kernel")
 QN_DEQUANT_BATCH_MAX = 16
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.nf4_dequantize.restype = ctypes.c_int
     L.nf4_dequantize_batch.argtypes = [sp, ctypes.POINTER(vp), i32, vp]
     L.nf4_dequantize_batch.restype = ctypes.c_int
+    L.nf4_merge.argtypes = [sp, vp, vp, i32, f32, vp, vp]
+    L.nf4_merge.restype = ctypes.c_int
     L.qlora_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.qlora_workspace_bytes.restype = ctypes.c_size_t
     L.qlora_linear_fwd.argtypes = [vp, i64, sp, vp, vp, i32, f32, vp, i32, vp,
@@ -180,6 +182,20 @@ def nf4_dequantize_batch(ws, outs=None, stream=None):
     _check("nf4_dequantize_batch", lib().nf4_dequantize_batch(
         structs, ptrs, len(ws), _stream(stream)))
     return outs
+
+
+def nf4_merge(w: NF4Tensor, A, B, r: int, alpha: float, out=None,
+              stream=None):
+    """Dense bf16 [rows, cols] = bf16(W' + (alpha / r) B A)."""
+    import torch
+    if out is None:
+        out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16,
+                          device=w.packed.device)
+    st = w.as_struct()
+    _check("nf4_merge", lib().nf4_merge(ctypes.byref(st), _ptr(A), _ptr(B),
+                                        int(r), float(alpha), _ptr(out),
+                                        _stream(stream)))
+    return out
 
 
 def qlora_workspace_bytes(M: int, N: int, K: int, r: int, which: int) -> int:

@@ -152,6 +152,28 @@ int nf4_dequantize_batch(const nf4_tensor* w, uint16_t* const* w_bf16,
                          int32_t count, void* stream);
 
 /*
+ * nf4_merge -- dequantize-and-merge: the dense bf16 weight with the adapter
+ * folded in (device).
+ *
+ * "Qlora Expert", When to Use and Common Pitfalls: an adapter is merged into
+ * a dense model by dequantizing the base, which materialises the full bf16
+ * weight; "QLoRA Implementation Details (2025 Edition)", Step 7 (Merge &
+ * Save); s = alpha / r as in the linear layer (Step 4).
+ *   w_merged[n][k] = bf16_rne(W'[n][k] + s * sum_j B[n][j] A[j][k])
+ * with W' the dequantized base (formula at nf4_tensor); the sum and the
+ * addition are formed in fp32 (fused multiply-add), then rounded once.
+ * w        : NF4 weight [N = rows, K = cols], K % 64 == 0.
+ * A        : device, bf16 [r][K] row-major, 16-byte aligned.
+ * B        : device, bf16 [N][r] row-major.
+ * r, alpha : 1 <= r <= QN_MAX_RANK.
+ * w_merged : device, bf16 [N][K] row-major, 16-byte aligned, written whole.
+ * Errors: QN_EINVAL (null or misaligned pointer, r out of range,
+ *         K % 64 != 0, operands of 2 GiB or more), QN_EHIP.
+ */
+int nf4_merge(const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
+              int32_t r, float alpha, uint16_t* w_merged, void* stream);
+
+/*
  * qlora_workspace_bytes -- device workspace a fused call needs (host).
  * which: QN_FWD or QN_BWD.  Returns 0 for invalid arguments.
  */

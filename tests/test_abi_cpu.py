@@ -87,6 +87,24 @@ def test_dequantize_batch_validation():
     assert L.nf4_dequantize_batch(st_bad, outs, 2, None) == capi.QN_EINVAL
 
 
+def test_merge_validation():
+    L = capi.lib()
+    st = _fake_tensor(8, 128)
+    p = 0x10000
+
+    def merge(w=st, A=p, B=p, r=4, out=p):
+        return L.nf4_merge(ctypes.byref(w), A, B, r, 8.0, out, None)
+    assert merge(A=None) == capi.QN_EINVAL
+    assert merge(B=None) == capi.QN_EINVAL
+    assert merge(out=None) == capi.QN_EINVAL
+    assert merge(out=p + 2) == capi.QN_EINVAL
+    assert merge(A=p + 2) == capi.QN_EINVAL
+    assert merge(r=0) == capi.QN_EINVAL
+    assert merge(r=257) == capi.QN_EINVAL
+    assert merge(w=_fake_tensor(8, 100)) == capi.QN_EINVAL      # K % 64 != 0
+    assert merge(w=_fake_tensor(0, 128)) == capi.QN_EINVAL
+
+
 def test_linear_validation():
     L = capi.lib()
     p = 0x10000
