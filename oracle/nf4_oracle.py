@@ -164,15 +164,18 @@ def block_absmax(w: np.ndarray) -> np.ndarray:
     return c
 
 
-def nf4_codes(w: np.ndarray, absmax: np.ndarray) -> np.ndarray:
+def nf4_codes(w: np.ndarray, absmax: np.ndarray,
+              thresholds: np.ndarray | None = None) -> np.ndarray:
     """4-bit code per weight (uint8 in 0..15).
 
     n = fp32(w / c_b) by one IEEE fp32 division (n = 0 when c_b = 0); the
     code is the number of thresholds strictly below n, i.e. the index of the
-    nearest level with ties going to the lower code.
+    nearest level with ties going to the lower code.  ``thresholds`` defaults
+    to the NF4 midpoints; another sorted 16-level table's midpoints give the
+    same rule for that table.
     """
     flat = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
-    t = nf4_thresholds()
+    t = nf4_thresholds() if thresholds is None else thresholds
     codes = np.empty(flat.shape[0], dtype=np.uint8)
     chunk = 1 << 22
     for s in range(0, flat.shape[0], chunk):
@@ -189,15 +192,16 @@ def nf4_codes(w: np.ndarray, absmax: np.ndarray) -> np.ndarray:
     return codes
 
 
-def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+def pack_nibbles(codes: np.ndarray, pad: int = 7) -> np.ndarray:
     """Two codes per byte: element 2i in bits 0-3, element 2i+1 in bits 4-7.
 
     "QLoRA: The 4-bit Revolution", section 1: 4 bits per number.  The nibble
-    order is a reading; an odd tail is padded with code 7 (the zero level).
+    order is a reading; an odd tail is padded with ``pad``, the code a zero
+    weight takes (7, the NF4 zero level, by default).
     """
     c = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
     if c.shape[0] % 2:
-        c = np.concatenate([c, np.array([7], dtype=np.uint8)])
+        c = np.concatenate([c, np.array([pad], dtype=np.uint8)])
     return (c[0::2] | (c[1::2] << 4)).astype(np.uint8)
 
 

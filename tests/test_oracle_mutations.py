@@ -138,3 +138,70 @@ def test_merge_without_scale_is_caught(monkeypatch):
         return core.bf16_rne_from_f64(v), v
     _patch(monkeypatch, "merge_f64", bad)
     _fails(mpins.test_merge_rank_one_by_hand)
+
+
+# --- codec variants -------------------------------------------------------
+
+import oracle.codec_variants as cvm  # noqa: E402
+import test_oracle_variant_pins as vpins  # noqa: E402
+
+
+def test_fp4_table_without_subnormal_is_caught(monkeypatch):
+    # exponent field 0 read as a normal number: 0.5 becomes 1.0, 0 becomes 0.5
+    def bad():
+        vals = []
+        for b in range(16):
+            s = -1.0 if b & 8 else 1.0
+            e, m = (b >> 1) & 3, b & 1
+            vals.append(s * 2.0 ** (e - 1) * (1.0 + 0.5 * m))
+        vals = sorted(vals)
+        return (np.array(vals) / max(vals)).astype(np.float32)
+    monkeypatch.setattr(cvm, "fp4_levels", bad)
+    _fails(vpins.test_fp4_table_is_e2m1_over_its_max)
+
+
+def test_int4_scaled_by_eight_is_caught(monkeypatch):
+    monkeypatch.setattr(cvm, "int4_levels",
+                        lambda: ((np.arange(16) - 8) / 8.0).astype(np.float32))
+    _fails(vpins.test_int4_codes_are_the_absmax_integer_quantizer)
+
+
+def test_centered_mean_not_added_back_is_caught(monkeypatch):
+    real = cvm.block_constants
+
+    def bad(consts, gscale, gmean, nb, dq):
+        if dq == cvm.DQ_CENTERED:
+            return real(consts, gscale, np.zeros_like(gmean), nb, dq)
+        return real(consts, gscale, gmean, nb, dq)
+    monkeypatch.setattr(cvm, "block_constants", bad)
+    _fails(vpins.test_centered_dq_bounds_and_extremes)
+
+
+def test_centered_unsigned_step_is_caught(monkeypatch):
+    real = cvm.centered_quantize
+
+    def bad(absmax):
+        q, d, mu = real(absmax)
+        return q, (d * np.float32(127.0 / 255.0)).astype(np.float32), mu
+    monkeypatch.setattr(cvm, "centered_quantize", bad)
+    _fails(vpins.test_centered_dq_bounds_and_extremes)
+
+
+def test_centered_fused_decode_is_caught(monkeypatch):
+    def bad(consts, gscale, gmean, nb, dq):
+        blk = np.arange(nb)
+        v = (np.asarray(consts, np.int8).astype(np.float64) * gscale[blk // 256].astype(np.float64)
+             + gmean[blk // 256].astype(np.float64))
+        return v.astype(np.float32)
+    monkeypatch.setattr(cvm, "block_constants", bad)
+    _fails(vpins.test_centered_decode_rounds_twice)
+
+
+def test_left_to_right_group_sum_is_caught(monkeypatch):
+    def bad(x):
+        s = np.float32(0)
+        for v in np.asarray(x, np.float32):
+            s = np.float32(s + v)
+        return s
+    monkeypatch.setattr(cvm, "pairwise_sum_f32", bad)
+    _fails(vpins.test_pairwise_sum_pairs_adjacent_values)
