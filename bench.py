@@ -249,6 +249,58 @@ def bench_dequant_quant(reps, copies=3):
     return res
 
 
+def bench_variants(reps, copies=3):
+    """Codec variants over the 7B-class layer: for each 4-bit table (NF4,
+    FP4, INT4) and block-constant storage (8-bit DQ, fp32, centered 8-bit):
+    dequant GB/s (7 qn_dequantize calls per pass, cycling over `copies`
+    quantized copies so the pass reads HBM) and the quantization error of
+    the layer, sqrt(sum (w' - w)^2 / sum w^2), measured on the GPU."""
+    import torch
+    from bit_nf4_quantized_14_amd import capi
+    from bit_nf4_quantized_14_amd import workloads as wl
+    wk = wl.workload("dequant7b")
+    ws32 = [torch.from_numpy(wl.weight(wk, p)).to("cuda")
+            for p in range(len(wk.projections))]
+    outs = [torch.empty(w.shape, dtype=torch.bfloat16, device="cuda") for w in ws32]
+    params = sum(w.numel() for w in ws32)
+    names = {capi.QN_CODE_NF4: "nf4", capi.QN_CODE_FP4: "fp4", capi.QN_CODE_INT4: "int4"}
+    modes = {capi.QN_CONST_DQ8: "dq8", capi.QN_CONST_FP32: "fp32",
+             capi.QN_CONST_CENTERED: "dq8c"}
+    res = {}
+    for code, cname in names.items():
+        for mode, mname in modes.items():
+            sets = [[capi.qn_quantize(w, code, mode) for w in ws32] for _ in range(copies)]
+            tens = sets[0]
+            nbytes = 2 * params + sum(
+                t.packed.numel() + t.consts.numel() * t.consts.element_size()
+                + 4 * (t.gscale.numel() + t.gmean.numel()) for t in tens)
+
+            def deq():
+                for c in range(copies):
+                    for t, o in zip(sets[c], outs):
+                        capi.qn_dequantize(t, o)
+            sec = timed_graph(deq, reps) / copies
+            num = den = 0.0
+            for t, w, o in zip(tens, ws32, outs):
+                capi.qn_dequantize(t, o)
+                num += float(((o.float() - w) ** 2).sum(dtype=torch.float64))
+                den += float((w.double() ** 2).sum())
+            key = f"{cname}_{mname}"
+            res[key] = {"bytes_per_pass": nbytes, "bits_per_weight":
+                        8.0 * (nbytes - 2 * params) / params,
+                        "ms_per_pass": sec * 1e3, "GB/s": nbytes / sec / 1e9,
+                        "rel_rms_error": (num / den) ** 0.5}
+            log(f"variant {key}: {res[key]['GB/s']:.0f} GB/s, "
+                f"{res[key]['bits_per_weight']:.3f} bit/w, rel rms err "
+                f"{res[key]['rel_rms_error']:.5f}")
+            del sets, tens
+    del ws32, outs
+    torch.cuda.empty_cache()
+    return {"variants7b": {"params": params, "timing": "graph replay of 7 "
+                           "qn_dequantize calls per pass, cycling over "
+                           f"{copies} copies (> MALL)", "variants": res}}
+
+
 def bench_70b(reps, do_train=True):
     import torch
     from bit_nf4_quantized_14_amd import capi
@@ -386,7 +438,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-70b", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    ap.add_argument("--only", choices=("dequant", "skinny", "layer70b"),
+    ap.add_argument("--only", choices=("dequant", "variants", "skinny", "layer70b"),
                     help="run one component pass only (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy, the "
@@ -416,6 +468,8 @@ def main():
         reps = max(3, args.steps)
         if args.only == "dequant":
             res = bench_dequant_quant(reps)
+        elif args.only == "variants":
+            res = bench_variants(reps)
         elif args.only == "skinny":
             res = bench_70b(reps, do_train=False)
         else:
@@ -501,6 +555,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.quick:
         comps = bench_dequant_quant(max(5, args.steps // 2))
+        comps.update(bench_variants(max(3, args.steps // 4)))
         if not args.no_70b:
             comps.update(bench_70b(max(3, args.steps // 4)))
         out["components"] = comps

@@ -26,15 +26,25 @@ QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 256
 # Every symbol the header declares (tests check the library exports them).
 EXPORTS = ("nf4_codebook", "nf4_quantize", "nf4_dequantize",
            "nf4_dequantize_batch", "nf4_merge",
+           "qn_codebook", "qn_quantize", "qn_dequantize",
            "qlora_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
            "qn_strerror", "qn_profile_kernel")
 QN_DEQUANT_BATCH_MAX = 16
+QN_CODE_NF4, QN_CODE_FP4, QN_CODE_INT4 = 0, 1, 2
+QN_CONST_DQ8, QN_CONST_FP32, QN_CONST_CENTERED = 0, 1, 2
 
 
 class _NF4Struct(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("qabs", ctypes.c_void_p),
                 ("gscale", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64)]
+
+
+class _QStruct(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("consts", ctypes.c_void_p),
+                ("gscale", ctypes.c_void_p), ("gmean", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("code", ctypes.c_int32), ("consts_mode", ctypes.c_int32)]
 
 
 _lib = None
@@ -62,6 +72,13 @@ def lib() -> ctypes.CDLL:
     L.nf4_dequantize_batch.restype = ctypes.c_int
     L.nf4_merge.argtypes = [sp, vp, vp, i32, f32, vp, vp]
     L.nf4_merge.restype = ctypes.c_int
+    qp = ctypes.POINTER(_QStruct)
+    L.qn_codebook.argtypes = [i32, vp, vp]
+    L.qn_codebook.restype = ctypes.c_int
+    L.qn_quantize.argtypes = [vp, qp, vp, vp]
+    L.qn_quantize.restype = ctypes.c_int
+    L.qn_dequantize.argtypes = [qp, vp, vp]
+    L.qn_dequantize.restype = ctypes.c_int
     L.qlora_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.qlora_workspace_bytes.restype = ctypes.c_size_t
     L.qlora_linear_fwd.argtypes = [vp, i64, sp, vp, vp, i32, f32, vp, i32, vp,
@@ -195,6 +212,80 @@ def nf4_merge(w: NF4Tensor, A, B, r: int, alpha: float, out=None,
     _check("nf4_merge", lib().nf4_merge(ctypes.byref(st), _ptr(A), _ptr(B),
                                         int(r), float(alpha), _ptr(out),
                                         _stream(stream)))
+    return out
+
+
+@dataclass
+class QTensor:
+    """Device buffers of a codec-variant weight (see qn_qtensor in the
+    header): packed codes, per-block constants (uint8, float32 or int8 by
+    consts_mode), per-group scale and mean (empty where unused)."""
+    packed: "object"
+    consts: "object"
+    gscale: "object"
+    gmean: "object"
+    rows: int
+    cols: int
+    code: int
+    consts_mode: int
+
+    @property
+    def numel(self) -> int:
+        return self.rows * self.cols
+
+    @classmethod
+    def empty(cls, rows: int, cols: int, code: int, consts_mode: int,
+              device="cuda"):
+        import torch
+        npk, nb, ng = NF4Tensor.sizes(rows, cols)
+        cdt = {QN_CONST_DQ8: torch.uint8, QN_CONST_FP32: torch.float32,
+               QN_CONST_CENTERED: torch.int8}[consts_mode]
+        has_scale = consts_mode != QN_CONST_FP32
+        has_mean = consts_mode == QN_CONST_CENTERED
+        return cls(torch.empty(npk, dtype=torch.uint8, device=device),
+                   torch.empty(nb, dtype=cdt, device=device),
+                   torch.empty(ng if has_scale else 0, dtype=torch.float32, device=device),
+                   torch.empty(ng if has_mean else 0, dtype=torch.float32, device=device),
+                   rows, cols, code, consts_mode)
+
+    def as_struct(self) -> _QStruct:
+        def p(t):
+            return t.data_ptr() if t is not None and t.numel() > 0 else None
+        return _QStruct(self.packed.data_ptr(), p(self.consts), p(self.gscale),
+                        p(self.gmean), self.rows, self.cols, self.code,
+                        self.consts_mode)
+
+
+def qn_codebook(code: int):
+    """(levels float32[16], thresholds float32[15]) of a QN_CODE_* table."""
+    lv = np.zeros(16, dtype=np.float32)
+    th = np.zeros(15, dtype=np.float32)
+    _check("qn_codebook", lib().qn_codebook(int(code), lv.ctypes.data,
+                                            th.ctypes.data))
+    return lv, th
+
+
+def qn_quantize(w, code: int, consts_mode: int, out: QTensor | None = None,
+                status=None, stream=None):
+    """Quantize a device fp32 weight into a variant format; returns it."""
+    rows, cols = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, w.numel())
+    if out is None:
+        out = QTensor.empty(rows, cols, code, consts_mode, device=w.device)
+    st = out.as_struct()
+    _check("qn_quantize", lib().qn_quantize(_ptr(w), ctypes.byref(st),
+                                            _ptr(status), _stream(stream)))
+    return out
+
+
+def qn_dequantize(w: QTensor, out=None, stream=None):
+    """bf16 device tensor [rows, cols] of a variant-format weight."""
+    import torch
+    if out is None:
+        out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16,
+                          device=w.packed.device)
+    st = w.as_struct()
+    _check("qn_dequantize", lib().qn_dequantize(ctypes.byref(st), _ptr(out),
+                                                _stream(stream)))
     return out
 
 

@@ -61,9 +61,47 @@ void derive_codebook(float levels[16], float thresholds[15]) {
           static_cast<float>((double(lv[j]) + double(lv[j + 1])) / 2.0);
 }
 
+bool derive_variant_codebook(int code, float levels[16],
+                             float thresholds[15]) {
+  float lv[16];
+  if (code == QN_CODE_NF4) {
+    derive_codebook(lv, nullptr);
+  } else if (code == QN_CODE_FP4) {
+    // E2M1: sign, 2-bit exponent (bias 1), 1-bit mantissa; exponent 0 is
+    // subnormal (0.5 * mantissa).  Sorted: the 7 negative nonzero values,
+    // two zeros (both +0), the 7 positive values; divided by the top, 6.
+    double pos[8];
+    for (int b = 0; b < 8; ++b) {
+      const int e = b >> 1, m = b & 1;
+      pos[b] = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+    }
+    for (int i = 0; i < 7; ++i) lv[i] = static_cast<float>(-pos[7 - i] / 6.0);
+    lv[7] = 0.0f;
+    lv[8] = 0.0f;
+    for (int i = 1; i < 8; ++i) lv[8 + i] = static_cast<float>(pos[i] / 6.0);
+  } else if (code == QN_CODE_INT4) {
+    for (int j = 0; j < 16; ++j) lv[j] = static_cast<float>((j - 8) / 7.0);
+  } else {
+    return false;
+  }
+  if (levels)
+    for (int j = 0; j < 16; ++j) levels[j] = lv[j];
+  if (thresholds)
+    for (int j = 0; j < 15; ++j)
+      thresholds[j] =
+          static_cast<float>((double(lv[j]) + double(lv[j + 1])) / 2.0);
+  return true;
+}
+
 }  // namespace qn
 
 extern "C" int nf4_codebook(float levels[16], float thresholds[15]) {
   qn::derive_codebook(levels, thresholds);
   return QN_OK;
+}
+
+extern "C" int qn_codebook(int32_t code, float levels[16],
+                           float thresholds[15]) {
+  return qn::derive_variant_codebook(code, levels, thresholds) ? QN_OK
+                                                               : QN_EINVAL;
 }

@@ -11,6 +11,40 @@ namespace {
 
 using namespace qn;
 
+// Storage of the per-block constants (QN_CONST_*): 8-bit codes with one
+// fp32 scale per group (double quantization), the fp32 absmax itself, or
+// centered signed 8-bit codes with a scale and a mean per group.
+enum ConstMode { CM_DQ8 = QN_CONST_DQ8, CM_FP32 = QN_CONST_FP32,
+                 CM_CENTERED = QN_CONST_CENTERED };
+
+// Centered decode c' = fp32(fp32(q d) + mu): two roundings, never fused.
+__device__ __forceinline__ float centered_cprime(int32_t q, float d,
+                                                 float mu) {
+#pragma clang fp contract(off)
+  const float p = static_cast<float>(q) * d;
+  return p + mu;
+}
+
+// Decoded block constant from the raw per-block entry (zero-extended u8,
+// fp32 bits, or sign-extended i8) and the group's scale and mean.
+template <int CM>
+__device__ __forceinline__ float cprime_of(uint32_t raw, float d, float mu) {
+  if constexpr (CM == CM_DQ8) return static_cast<float>(raw) * d;
+  else if constexpr (CM == CM_FP32) return __uint_as_float(raw);
+  else return centered_cprime(static_cast<int32_t>(raw), d, mu);
+}
+
+template <int CM>
+__device__ __forceinline__ uint32_t const_raw(const void* consts, int64_t b) {
+  if constexpr (CM == CM_DQ8)
+    return static_cast<const uint8_t*>(consts)[b];
+  else if constexpr (CM == CM_FP32)
+    return static_cast<const uint32_t*>(consts)[b];
+  else
+    return static_cast<uint32_t>(
+        static_cast<int32_t>(static_cast<const int8_t*>(consts)[b]));
+}
+
 // ---------------------------------------------------------------------------
 // K1: quantization + double quantization.  One workgroup per group of 256
 // blocks (16384 weights); each thread owns 8 consecutive weights in each of
@@ -19,12 +53,14 @@ using namespace qn;
 constexpr int QZ_THREADS = 256;
 constexpr int QZ_PASSES = 8;  // 8 * 256 * 8 = 16384 weights
 
+template <int CM>
 __global__ __launch_bounds__(QZ_THREADS) void k_quantize(
     const float* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
-    uint8_t* __restrict__ qabs, float* __restrict__ gscale,
-    int32_t* __restrict__ status, Codebook cb) {
+    void* __restrict__ consts, float* __restrict__ gscale,
+    float* __restrict__ gmean, int32_t* __restrict__ status, Codebook cb) {
   __shared__ float s_c[256];
   __shared__ float s_wmax[QZ_THREADS / 64];
+  __shared__ float s_wsum[QZ_THREADS / 64];
   const int tid = threadIdx.x;
   const int64_t g = blockIdx.x;
   const int64_t gbase = g * (int64_t)(QN_BLOCK * QN_GROUP);
@@ -60,24 +96,64 @@ __global__ __launch_bounds__(QZ_THREADS) void k_quantize(
   if (!finite && status != nullptr) *status = QN_ENONFINITE;
   __syncthreads();
 
-  // group absmax
+  // block constant of block `tid` of this group (0 past the last block)
   const float cb_t = s_c[tid];
-  float gm = cb_t;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
-  if ((tid & 63) == 0) s_wmax[tid >> 6] = gm;
-  __syncthreads();
-  float smax = s_wmax[0];
-#pragma unroll
-  for (int i = 1; i < QZ_THREADS / 64; ++i) smax = fmaxf(smax, s_wmax[i]);
-  const float d = (smax == 0.0f) ? 0.0f : smax / 255.0f;
   const int64_t b_this = g * QN_GROUP + tid;
-  if (b_this < nb_total) {
-    float qv = 0.0f;
-    if (smax != 0.0f) qv = fminf(rintf(cb_t / d), 255.0f);
-    qabs[b_this] = static_cast<uint8_t>(qv);
+  if constexpr (CM == CM_DQ8) {
+    // group absmax -> d = max / 255, q = min(255, rint(c / d))
+    float gm = cb_t;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+    if ((tid & 63) == 0) s_wmax[tid >> 6] = gm;
+    __syncthreads();
+    float smax = s_wmax[0];
+#pragma unroll
+    for (int i = 1; i < QZ_THREADS / 64; ++i) smax = fmaxf(smax, s_wmax[i]);
+    const float d = (smax == 0.0f) ? 0.0f : smax / 255.0f;
+    if (b_this < nb_total) {
+      float qv = 0.0f;
+      if (smax != 0.0f) qv = fminf(rintf(cb_t / d), 255.0f);
+      static_cast<uint8_t*>(consts)[b_this] = static_cast<uint8_t>(qv);
+    }
+    if (tid == 0) gscale[g] = d;
+  } else if constexpr (CM == CM_FP32) {
+    if (b_this < nb_total) static_cast<float*>(consts)[b_this] = cb_t;
+  } else {
+    // pairwise sum over the 256 (zero-padded) constants: the xor butterfly
+    // with offsets 1, 2, ..., 32 adds adjacent pairs level by level inside
+    // a wave (a + b == b + a, so both partners hold the same sum); the four
+    // wave sums finish the last two levels
+    float sum = cb_t;
+#pragma unroll
+    for (int off = 1; off <= 32; off <<= 1) sum = sum + __shfl_xor(sum, off);
+    if ((tid & 63) == 0) s_wsum[tid >> 6] = sum;
+    __syncthreads();
+    const float total = (s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3]);
+    const int64_t left = nb_total - g * QN_GROUP;
+    const int nvalid = left < QN_GROUP ? static_cast<int>(left) : QN_GROUP;
+    const float mu = total / static_cast<float>(nvalid);
+    const bool valid = b_this < nb_total;
+    const float dev = cb_t - mu;
+    float am = valid ? fabsf(dev) : 0.0f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    if ((tid & 63) == 0) s_wmax[tid >> 6] = am;
+    __syncthreads();
+    float dmax = s_wmax[0];
+#pragma unroll
+    for (int i = 1; i < QZ_THREADS / 64; ++i) dmax = fmaxf(dmax, s_wmax[i]);
+    const float d = (dmax == 0.0f) ? 0.0f : dmax / 127.0f;
+    if (valid) {
+      float qv = 0.0f;
+      if (dmax != 0.0f) qv = fminf(fmaxf(rintf(dev / d), -127.0f), 127.0f);
+      static_cast<int8_t*>(consts)[b_this] =
+          static_cast<int8_t>(static_cast<int32_t>(qv));
+    }
+    if (tid == 0) {
+      gscale[g] = d;
+      gmean[g] = mu;
+    }
   }
-  if (tid == 0) gscale[g] = d;
 
   // NF4 codes against the un-quantized block constant
   const int64_t nbytes = (numel + 1) / 2;
@@ -125,6 +201,7 @@ struct DqRegs {
   uint32_t p[4];
   uint32_t q[4];
   float d;
+  float mu;
 };
 
 // One launch dequantizes up to DQ_BATCH_MAX tensors: their whole spans are
@@ -132,8 +209,9 @@ struct DqRegs {
 constexpr int DQ_BATCH_MAX = QN_DEQUANT_BATCH_MAX;
 struct DqTensor {
   const uint8_t* packed;
-  const uint8_t* qabs;
+  const void* consts;
   const float* gscale;
+  const float* gmean;
   uint16_t* out;
   int64_t span0;
 };
@@ -143,6 +221,7 @@ struct DqBatch {
   int count;
 };
 
+template <int CM>
 __global__ __launch_bounds__(DQ_THREADS) void k_dequant(DqBatch b, Codebook cb) {
   const int lane = threadIdx.x & 63;
   const int64_t wave0 = __builtin_amdgcn_readfirstlane(
@@ -159,13 +238,14 @@ __global__ __launch_bounds__(DQ_THREADS) void k_dequant(DqBatch b, Codebook cb) 
     const int ti = ok ? owner(span) : 0;
     const int64_t sp = ok ? span - b.t[ti].span0 : 0;
     const uint32_t* pw = reinterpret_cast<const uint32_t*>(b.t[ti].packed) + sp * (DQ_SPAN / 8);
-    const uint8_t* qb = b.t[ti].qabs + sp * (DQ_SPAN / 64);
+    const int64_t blk0 = sp * (DQ_SPAN / 64);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       R.p[j] = pw[lane + 64 * j];
-      R.q[j] = qb[(lane >> 3) + 8 * j];
+      R.q[j] = const_raw<CM>(b.t[ti].consts, blk0 + (lane >> 3) + 8 * j);
     }
-    R.d = ok ? b.t[ti].gscale[(sp * (DQ_SPAN / 64)) >> 8] : 0.0f;
+    R.d = (CM != CM_FP32 && ok) ? b.t[ti].gscale[blk0 >> 8] : 0.0f;
+    R.mu = (CM == CM_CENTERED && ok) ? b.t[ti].gmean[blk0 >> 8] : 0.0f;
   };
   DqRegs cur;
   int64_t span = wave0;
@@ -177,7 +257,7 @@ __global__ __launch_bounds__(DQ_THREADS) void k_dequant(DqBatch b, Codebook cb) 
     u32x4* o = reinterpret_cast<u32x4*>(b.t[ti].out + (span - b.t[ti].span0) * DQ_SPAN);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const Lut t = make_lut(cb, static_cast<float>(cur.q[j]) * cur.d);
+      const Lut t = make_lut(cb, cprime_of<CM>(cur.q[j], cur.d, cur.mu));
       // streaming store: the output is not re-read here, and keeping it out
       // of L2 avoids a large write-back when the kernel retires
       __builtin_nontemporal_store(decode8(cur.p[j], t), &o[lane + 64 * j]);
@@ -186,15 +266,85 @@ __global__ __launch_bounds__(DQ_THREADS) void k_dequant(DqBatch b, Codebook cb) 
   }
 }
 
+template <int CM>
 __global__ __launch_bounds__(DQ_THREADS) void k_dequant_tail(
-    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
-    const float* __restrict__ gscale, int64_t e0, int64_t numel,
-    uint16_t* __restrict__ out, Codebook cb) {
+    DqTensor t, int64_t e0, int64_t numel, Codebook cb) {
   const int64_t e = e0 + (int64_t)blockIdx.x * DQ_THREADS + threadIdx.x;
   if (e >= numel) return;
-  const uint32_t byte = packed[e >> 1];
+  const uint32_t byte = t.packed[e >> 1];
   const uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xFu);
-  out[e] = decode1(cb, code, block_cprime(qabs, gscale, e >> 6));
+  const int64_t blk = e >> 6;
+  const float d = CM != CM_FP32 ? t.gscale[blk >> 8] : 0.0f;
+  const float mu = CM == CM_CENTERED ? t.gmean[blk >> 8] : 0.0f;
+  t.out[e] = decode1(cb, code, cprime_of<CM>(const_raw<CM>(t.consts, blk), d, mu));
+}
+
+// Host side: launch quantization / dequantization for one constant mode.
+template <int CM>
+int launch_quantize(const float* w, int64_t numel, uint8_t* packed,
+                    void* consts, float* gscale, float* gmean,
+                    int32_t* status, const Codebook& cb, hipStream_t st) {
+  const int64_t nb = cdiv(numel, QN_BLOCK);
+  const int64_t ng = cdiv(nb, QN_GROUP);
+  if (ng > 0x7FFFFFFFLL) return QN_EINVAL;
+  QN_LAUNCH("k_quantize", k_quantize<CM>, dim3((unsigned)ng), dim3(QZ_THREADS),
+            st, w, numel, packed, consts, gscale, gmean, status, cb);
+  return check_launch();
+}
+
+template <int CM>
+int launch_dequant(const DqTensor* t, const int64_t* numel, int count,
+                   const Codebook& cb, hipStream_t st) {
+  DqBatch b;
+  std::memset(&b, 0, sizeof(b));
+  int64_t spans = 0;
+  for (int i = 0; i < count; ++i) {
+    b.t[i] = t[i];
+    b.t[i].span0 = spans;
+    spans += numel[i] / DQ_SPAN;
+  }
+  b.nspans = spans;
+  b.count = count;
+  if (spans > 0) {
+    // up to 64 waves per CU; larger passes walk several spans per wave
+    const int64_t grid = std::min<int64_t>(cdiv(spans, DQ_THREADS / 64), QN_DQ_GRID_CAP);
+    QN_LAUNCH("k_dequant", k_dequant<CM>, dim3((unsigned)grid), dim3(DQ_THREADS),
+              st, b, cb);
+  }
+  for (int i = 0; i < count; ++i) {
+    const int64_t e0 = numel[i] / DQ_SPAN * DQ_SPAN;
+    if (e0 < numel[i])
+      QN_LAUNCH("k_dequant_tail", k_dequant_tail<CM>,
+                dim3((unsigned)cdiv(numel[i] - e0, DQ_THREADS)), dim3(DQ_THREADS),
+                st, t[i], e0, numel[i], cb);
+  }
+  return check_launch();
+}
+
+// Codebook kernel arguments of the QN_CODE_* tables (host-derived once).
+const Codebook* variant_codebook(int code) {
+  struct Tabs {
+    Codebook c[3];
+  };
+  static const Tabs tabs = [] {
+    Tabs t;
+    for (int i = 0; i < 3; ++i) derive_variant_codebook(i, t.c[i].L, t.c[i].T);
+    return t;
+  }();
+  return (code >= 0 && code < 3) ? &tabs.c[code] : nullptr;
+}
+
+bool valid_qtensor(const qn_qtensor* t) {
+  if (t == nullptr || t->packed == nullptr || t->consts == nullptr ||
+      t->rows <= 0 || t->cols <= 0 || !aligned16(t->packed))
+    return false;
+  if (t->code < QN_CODE_NF4 || t->code > QN_CODE_INT4) return false;
+  switch (t->consts_mode) {
+    case QN_CONST_DQ8: return t->gscale != nullptr;
+    case QN_CONST_FP32: return (reinterpret_cast<uintptr_t>(t->consts) & 3u) == 0;
+    case QN_CONST_CENTERED: return t->gscale != nullptr && t->gmean != nullptr;
+    default: return false;
+  }
 }
 
 }  // namespace
@@ -204,52 +354,63 @@ extern "C" {
 int nf4_quantize(const float* w, const nf4_tensor* out, int32_t* status_dev,
                  void* stream) {
   if (w == nullptr || !valid_tensor(out) || !aligned16(w)) return QN_EINVAL;
-  const int64_t numel = out->rows * out->cols;
-  const int64_t nb = cdiv(numel, QN_BLOCK);
-  const int64_t ng = cdiv(nb, QN_GROUP);
-  if (ng > 0x7FFFFFFFLL) return QN_EINVAL;
-  QN_LAUNCH("k_quantize", k_quantize, dim3((unsigned)ng), dim3(QZ_THREADS),
-            (hipStream_t)stream, w, numel, out->packed, out->qabs,
-            out->gscale, status_dev, qn::codebook());
-  return check_launch();
+  return launch_quantize<CM_DQ8>(w, out->rows * out->cols, out->packed,
+                                 out->qabs, out->gscale, nullptr, status_dev,
+                                 qn::codebook(), (hipStream_t)stream);
 }
 
 int nf4_dequantize_batch(const nf4_tensor* w, uint16_t* const* w_bf16,
                          int32_t count, void* stream) {
   if (w == nullptr || w_bf16 == nullptr || count < 1 || count > DQ_BATCH_MAX)
     return QN_EINVAL;
-  DqBatch b;
-  std::memset(&b, 0, sizeof(b));
-  int64_t spans = 0;
+  DqTensor t[DQ_BATCH_MAX];
+  int64_t numel[DQ_BATCH_MAX];
   for (int i = 0; i < count; ++i) {
     if (!valid_tensor(&w[i]) || w_bf16[i] == nullptr || !aligned16(w_bf16[i]))
       return QN_EINVAL;
-    b.t[i] = DqTensor{w[i].packed, w[i].qabs, w[i].gscale, w_bf16[i], spans};
-    spans += w[i].rows * w[i].cols / DQ_SPAN;
+    t[i] = DqTensor{w[i].packed, w[i].qabs, w[i].gscale, nullptr, w_bf16[i], 0};
+    numel[i] = w[i].rows * w[i].cols;
   }
-  b.nspans = spans;
-  b.count = count;
-  hipStream_t st = (hipStream_t)stream;
-  if (spans > 0) {
-    // up to 64 waves per CU; larger passes walk several spans per wave
-    const int64_t grid = std::min<int64_t>(cdiv(spans, DQ_THREADS / 64), QN_DQ_GRID_CAP);
-    QN_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(DQ_THREADS),
-              st, b, qn::codebook());
-  }
-  for (int i = 0; i < count; ++i) {
-    const int64_t numel = w[i].rows * w[i].cols;
-    const int64_t e0 = numel / DQ_SPAN * DQ_SPAN;
-    if (e0 < numel)
-      QN_LAUNCH("k_dequant_tail", k_dequant_tail,
-                dim3((unsigned)cdiv(numel - e0, DQ_THREADS)), dim3(DQ_THREADS),
-                st, w[i].packed, w[i].qabs, w[i].gscale, e0, numel, w_bf16[i],
-                qn::codebook());
-  }
-  return check_launch();
+  return launch_dequant<CM_DQ8>(t, numel, count, qn::codebook(),
+                                (hipStream_t)stream);
 }
 
 int nf4_dequantize(const nf4_tensor* w, uint16_t* w_bf16, void* stream) {
   return nf4_dequantize_batch(w, &w_bf16, 1, stream);
+}
+
+int qn_quantize(const float* w, const qn_qtensor* out, int32_t* status_dev,
+                void* stream) {
+  if (w == nullptr || !valid_qtensor(out) || !aligned16(w)) return QN_EINVAL;
+  const Codebook& cb = *variant_codebook(out->code);
+  const int64_t numel = out->rows * out->cols;
+  hipStream_t st = (hipStream_t)stream;
+  switch (out->consts_mode) {
+    case QN_CONST_DQ8:
+      return launch_quantize<CM_DQ8>(w, numel, out->packed, out->consts,
+                                     out->gscale, nullptr, status_dev, cb, st);
+    case QN_CONST_FP32:
+      return launch_quantize<CM_FP32>(w, numel, out->packed, out->consts,
+                                      nullptr, nullptr, status_dev, cb, st);
+    default:
+      return launch_quantize<CM_CENTERED>(w, numel, out->packed, out->consts,
+                                          out->gscale, out->gmean, status_dev,
+                                          cb, st);
+  }
+}
+
+int qn_dequantize(const qn_qtensor* w, uint16_t* w_bf16, void* stream) {
+  if (!valid_qtensor(w) || w_bf16 == nullptr || !aligned16(w_bf16))
+    return QN_EINVAL;
+  const Codebook& cb = *variant_codebook(w->code);
+  const int64_t numel = w->rows * w->cols;
+  const DqTensor t{w->packed, w->consts, w->gscale, w->gmean, w_bf16, 0};
+  hipStream_t st = (hipStream_t)stream;
+  switch (w->consts_mode) {
+    case QN_CONST_DQ8: return launch_dequant<CM_DQ8>(&t, &numel, 1, cb, st);
+    case QN_CONST_FP32: return launch_dequant<CM_FP32>(&t, &numel, 1, cb, st);
+    default: return launch_dequant<CM_CENTERED>(&t, &numel, 1, cb, st);
+  }
 }
 
 }  // extern "C"

@@ -11,6 +11,9 @@ namespace qn {
 // precision (codebook.cpp).
 void derive_codebook(float levels[16], float thresholds[15]);
 
+// Levels and thresholds of a QN_CODE_* table; false for an unknown table.
+bool derive_variant_codebook(int code, float levels[16], float thresholds[15]);
+
 // Workspace layouts of the fused calls (byte offsets, 256-byte aligned).
 // rpad = r rounded up to 16, 32, 64, 128 or 256 (the adapter MFMA width).
 // M <= QN_SKINNY_M takes the skinny (GEMV) forward.

@@ -174,6 +174,77 @@ int nf4_merge(const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
               int32_t r, float alpha, uint16_t* w_merged, void* stream);
 
 /*
+ * Codec variants -- other 4-bit tables and other storage of the block
+ * constants, for quantization-error comparisons.
+ *
+ * "Qlora Expert", Hyperparameter Guidance: quant type "fp4" exists beside
+ * "nf4", and double quantization can be switched off; Memory Math prices the
+ * constants at 0.5 bit per weight without it.  "QLoRA Guide", NF4 vs uniform
+ * INT4; "QLoRA Implementation Details", Step 1 NF4 Math (the signed 4-bit
+ * range [-8, 7]).  The pages define none of these, so each keeps NF4's
+ * block scheme (absmax per 64 weights, one IEEE division, the number of
+ * fp32 midpoint thresholds strictly below w/absmax, ties to the lower code,
+ * two codes per byte) and swaps only the sorted 16-level table:
+ *   QN_CODE_NF4  : the NF4 levels of nf4_codebook();
+ *   QN_CODE_FP4  : the 16 values of the 4-bit float E2M1 (+-{0, 0.5, 1, 1.5,
+ *                  2, 3, 4, 6}) divided by 6, both zeros as +0 (codes 7, 8);
+ *   QN_CODE_INT4 : the integers -8..7 divided by 7 (code 0 is never chosen).
+ * The stored code is the index into the sorted table.  Block constants:
+ *   QN_CONST_DQ8      : as nf4_tensor (unsigned 8-bit code, fp32 scale per
+ *                       group of 256): c' = fp32(q) * d;
+ *   QN_CONST_FP32     : the fp32 absmax itself, c' = c (4.5 bits/weight);
+ *   QN_CONST_CENTERED : per group of 256, mu = fp32 pairwise sum of the
+ *                       constants (adjacent pairs, level by level, padded
+ *                       with zeros to 256) / count; d = max|c - mu| / 127;
+ *                       q = clamp(rint_even((c - mu) / d), -127, 127) as
+ *                       int8 (d = q = 0 when every c equals mu);
+ *                       c' = fp32(fp32(q * d) + mu), no fused multiply-add.
+ * Dequantized value: bf16_rne(fp32(L[code] * c')).  QN_CODE_NF4 with
+ * QN_CONST_DQ8 is exactly nf4_quantize / nf4_dequantize.
+ */
+#define QN_CODE_NF4 0
+#define QN_CODE_FP4 1
+#define QN_CODE_INT4 2
+#define QN_CONST_DQ8 0
+#define QN_CONST_FP32 1
+#define QN_CONST_CENTERED 2
+
+/*
+ * A weight of rows x cols elements in one of the variant formats:
+ *   packed : device, ceil(numel/2) bytes, 16-byte aligned; layout as in
+ *            nf4_tensor; an odd tail nibble is the code of a zero weight.
+ *   consts : device, nb = ceil(numel/64) entries: uint8 (QN_CONST_DQ8),
+ *            float (QN_CONST_FP32, 4-byte aligned) or int8
+ *            (QN_CONST_CENTERED).
+ *   gscale : device, ng = ceil(nb/256) floats (DQ8, CENTERED; else unused).
+ *   gmean  : device, ng floats (CENTERED; else unused).
+ *   code   : QN_CODE_*;  consts_mode: QN_CONST_*.
+ */
+typedef struct {
+  uint8_t* packed;
+  void* consts;
+  float* gscale;
+  float* gmean;
+  int64_t rows, cols;
+  int32_t code;
+  int32_t consts_mode;
+} qn_qtensor;
+
+/* qn_codebook -- the 16 sorted levels and 15 fp32 midpoint thresholds of a
+ * QN_CODE_* table (host).  Errors: QN_EINVAL for an unknown table. */
+int qn_codebook(int32_t code, float levels[16], float thresholds[15]);
+
+/* qn_quantize -- quantize an fp32 weight w (device, numel floats, 16-byte
+ * aligned) into `out` (device).  Non-finite weights set *status_dev to
+ * QN_ENONFINITE as nf4_quantize does.  Errors: QN_EINVAL, QN_EHIP. */
+int qn_quantize(const float* w, const qn_qtensor* out, int32_t* status_dev,
+                void* stream);
+
+/* qn_dequantize -- bf16 copy of a variant-format weight (device, numel
+ * bf16, 16-byte aligned).  Errors: QN_EINVAL, QN_EHIP. */
+int qn_dequantize(const qn_qtensor* w, uint16_t* w_bf16, void* stream);
+
+/*
  * qlora_workspace_bytes -- device workspace a fused call needs (host).
  * which: QN_FWD or QN_BWD.  Returns 0 for invalid arguments.
  */

@@ -140,3 +140,43 @@ def test_workspace_sizes():
     a = capi.qlora_workspace_bytes(4096, 11008, 4096, 16, capi.QN_BWD)
     b = capi.qlora_workspace_bytes(4096, 11008, 4096, 64, capi.QN_BWD)
     assert 0 < a < b
+
+
+def test_variant_codebooks_equal_oracle():
+    from oracle import codec_variants as cv
+    for code in (capi.QN_CODE_NF4, capi.QN_CODE_FP4, capi.QN_CODE_INT4):
+        lv, th = capi.qn_codebook(code)
+        assert np.array_equal(lv.view(np.uint32), cv.levels(code).view(np.uint32))
+        assert np.array_equal(th.view(np.uint32), cv.thresholds(code).view(np.uint32))
+    with pytest.raises(capi.QNError):
+        capi.qn_codebook(3)
+
+
+def test_variant_validation():
+    L = capi.lib()
+    p = 0x10000
+
+    def q(packed=p, consts=p, gscale=p, gmean=p, rows=8, cols=128, code=0, mode=0):
+        return capi._QStruct(packed, consts, gscale, gmean, rows, cols, code, mode)
+
+    def quant(st, w=p):
+        return L.qn_quantize(w, ctypes.byref(st), None, None)
+
+    def deq(st, out=p):
+        return L.qn_dequantize(ctypes.byref(st), out, None)
+    for fn in (quant, deq):
+        assert fn(q(packed=None)) == capi.QN_EINVAL
+        assert fn(q(packed=p + 8)) == capi.QN_EINVAL
+        assert fn(q(consts=None)) == capi.QN_EINVAL
+        assert fn(q(rows=0)) == capi.QN_EINVAL
+        assert fn(q(code=3)) == capi.QN_EINVAL
+        assert fn(q(code=-1)) == capi.QN_EINVAL
+        assert fn(q(mode=3)) == capi.QN_EINVAL
+        assert fn(q(mode=capi.QN_CONST_DQ8, gscale=None)) == capi.QN_EINVAL
+        assert fn(q(mode=capi.QN_CONST_CENTERED, gmean=None)) == capi.QN_EINVAL
+        assert fn(q(mode=capi.QN_CONST_CENTERED, gscale=None)) == capi.QN_EINVAL
+        assert fn(q(mode=capi.QN_CONST_FP32, consts=p + 2)) == capi.QN_EINVAL
+    assert quant(q(), w=None) == capi.QN_EINVAL
+    assert quant(q(), w=p + 4) == capi.QN_EINVAL
+    assert deq(q(), out=None) == capi.QN_EINVAL
+    assert deq(q(), out=p + 2) == capi.QN_EINVAL
