@@ -8,7 +8,8 @@ the HIP library (no kernels, headers, tables or constant generators) and it
 imports nothing from ``bit_nf4_quantized_14_amd``.
 
 ``oracle.codec_variants`` holds the FP4 / INT4 tables and the other ways of
-storing the block constants (none, centered 8-bit).
+storing the block constants (none, centered 8-bit); ``oracle.adamw8`` the
+8-bit AdamW step on the adapters.
 
 Every function follows the passage of the source pages it cites; where the
 pages are silent or garbled, the reading taken is stated in the function's

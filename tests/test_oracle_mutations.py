@@ -205,3 +205,70 @@ def test_left_to_right_group_sum_is_caught(monkeypatch):
         return s
     monkeypatch.setattr(cvm, "pairwise_sum_f32", bad)
     _fails(vpins.test_pairwise_sum_pairs_adjacent_values)
+
+
+# --- 8-bit AdamW ----------------------------------------------------------
+
+import oracle.adamw8 as awm  # noqa: E402
+import test_oracle_adamw_pins as apins  # noqa: E402
+
+
+def test_missing_bias_correction_is_caught(monkeypatch):
+    real = awm.HParams.constants
+
+    def bad(self, step):
+        k = real(self, step)
+        k["bc1"] = np.float32(1.0)
+        k["bc2"] = np.float32(1.0)
+        return k
+    monkeypatch.setattr(awm.HParams, "constants", bad)
+    _fails(apins.test_adamw_f32_matches_torch_adamw)
+
+
+def test_weight_decay_through_the_gradient_is_caught(monkeypatch):
+    # Adam with L2 in the gradient (not decoupled)
+    real = awm.adamw_step_f32
+
+    def bad(p32, g, m, v, hp, step):
+        g = (np.asarray(g, np.float32) + np.float32(hp.weight_decay) * p32).astype(np.float32)
+        hp2 = awm.HParams(hp.lr, hp.beta1, hp.beta2, hp.eps, 0.0, hp.grad_scale)
+        return real(p32, g, m, v, hp2, step)
+    monkeypatch.setattr(awm, "adamw_step_f32", bad)
+    _fails(apins.test_adamw_f32_matches_torch_adamw)
+
+
+def test_e4m3_bias_eight_is_caught(monkeypatch):
+    def bad(code):
+        c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        e, m = (c >> 3) & 0xF, c & 7
+        mag = np.where(e == 0, m * 2.0 ** -10, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+        return sign * mag
+    monkeypatch.setattr(awm, "e4m3_value", bad)
+    _fails(apins.test_e4m3_decode_matches_torch)
+
+
+def test_e4m3_truncation_is_caught(monkeypatch):
+    real = awm.e4m3_encode
+
+    def bad(x):
+        x = np.asarray(x, np.float32)
+        # shave the magnitude so ties and upper halves round down
+        return real((x * np.float32(1 - 2 ** -5)).astype(np.float32))
+    monkeypatch.setattr(awm, "e4m3_encode", bad)
+    _fails(apins.test_e4m3_encode_matches_torch)
+
+
+def test_state_scale_by_127_is_caught(monkeypatch):
+    monkeypatch.setattr(awm, "E4M3_MAX", 127.0)
+    _fails(apins.test_state_block_maps_its_absmax_to_448)
+
+
+def test_eps_inside_the_sqrt_is_caught(monkeypatch):
+    def bad(p32, m, v, k):
+        den = np.sqrt((v * k["bc2"] + k["eps"]).astype(np.float32)).astype(np.float32)
+        u = ((m * k["bc1"]).astype(np.float32) / den).astype(np.float32)
+        return ((p32 * k["decay"]).astype(np.float32)
+                - (k["lr"] * u).astype(np.float32)).astype(np.float32)
+    monkeypatch.setattr(awm, "param_update_f32", bad)
+    _fails(apins.test_adamw_f32_matches_torch_adamw)
