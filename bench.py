@@ -301,6 +301,76 @@ def bench_variants(reps, copies=3):
                            f"{copies} copies (> MALL)", "variants": res}}
 
 
+def adapter_params_70b(r=16, layers=80):
+    """Parameters of r-rank adapters on all 7 linear projections of every
+    layer of a Llama-70B-class model (hidden 8192, GQA k/v 1024, MLP 28672)."""
+    shapes = ((8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192),
+              (28672, 8192), (28672, 8192), (8192, 28672))
+    return layers * sum(r * (n + k) for n, k in shapes)
+
+
+def bench_adamw(reps, chunk=1 << 24):
+    """8-bit AdamW over the adapters of a whole 70B-class model at r = 16
+    (one flat buffer): the resident step (state in HBM) as GB/s of its
+    algorithmic traffic, and the paged step (state in pinned host memory,
+    pages of `chunk` elements through a double-buffered device staging
+    area, copies on two streams of their own) as ms per step."""
+    import torch
+    from bit_nf4_quantized_14_amd import capi
+    n = adapter_params_70b()
+    gen = torch.Generator(device="cuda").manual_seed(1430)
+    p = (torch.randn(n, generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    g = torch.randn(n, generator=gen, device="cuda") * 1e-3
+    st = capi.AdamW8State.zeros(n)
+    hp = dict(lr=2e-4, weight_decay=0.0)
+    for t in range(1, 3):
+        capi.qn_adamw8_step(p, g, st, t, **hp)
+    nb = -(-n // capi.QN_ADAMW_BLOCK)
+    nbytes = n * (2 + 4 + 1 + 1 + 2 + 1 + 1) + nb * 4 * 4
+
+    def step():
+        capi.qn_adamw8_step(p, g, st, 3, **hp)
+    sec = timed_graph(step, reps)
+    kt, _ = kernel_times_ms(capi, "k_adamw8", step, 1, reps)
+    res = {"params": n, "bytes_per_step": nbytes, "ms_per_step": sec * 1e3,
+           "GB/s": nbytes / sec / 1e9, "kernel": "k_adamw8",
+           "kernel_ms": kt, "kernel_GB/s": nbytes / (kt * 1e-3) / 1e9,
+           "frac_hbm_peak": nbytes / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "workload": "r=16 adapters on the 7 projections of 80 layers of "
+                       "a 70B-class model, bf16 params, fp32 grads"}
+    log(f"adamw8 resident: {sec*1e3:.3f} ms/step, {res['GB/s']:.0f} GB/s "
+        f"(kernel {res['kernel_GB/s']:.0f} GB/s)")
+    # paged: the same state in pinned host memory
+    host = capi.AdamW8State(st.m_codes.cpu().pin_memory(), st.m_scale.cpu().pin_memory(),
+                            st.r_codes.cpu().pin_memory(), st.r_scale.cpu().pin_memory())
+    del st
+    staging = torch.empty(capi.qn_adamw8_staging_bytes(chunk), dtype=torch.uint8,
+                          device="cuda")
+    h2d, d2h = torch.cuda.Stream(), torch.cuda.Stream()
+    page_bytes = 2 * (2 * n + 8 * nb)     # state in and out
+
+    def paged(t):
+        capi.qn_adamw8_paged_step(p, g, host, staging, chunk, t,
+                                  h2d_stream=h2d, d2h_stream=d2h, **hp)
+    paged(3)
+    torch.cuda.synchronize()
+    prep = max(2, reps // 4)
+    t0 = time.perf_counter()
+    for i in range(prep):
+        paged(4 + i)
+    torch.cuda.synchronize()
+    psec = (time.perf_counter() - t0) / prep
+    res["paged"] = {"ms_per_step": psec * 1e3, "chunk": chunk,
+                    "host_device_bytes_per_step": page_bytes,
+                    "host_link_GB/s": page_bytes / psec / 1e9,
+                    "timing": "wall clock over eager steps (pinned host state)"}
+    log(f"adamw8 paged: {psec*1e3:.2f} ms/step, state traffic "
+        f"{page_bytes / psec / 1e9:.1f} GB/s over the host link")
+    del p, g, host, staging
+    torch.cuda.empty_cache()
+    return {"adamw8_70b_adapters": res}
+
+
 def bench_70b(reps, do_train=True):
     import torch
     from bit_nf4_quantized_14_amd import capi
@@ -438,7 +508,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-70b", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    ap.add_argument("--only", choices=("dequant", "variants", "skinny", "layer70b"),
+    ap.add_argument("--only", choices=("dequant", "variants", "adamw", "skinny",
+                                       "layer70b"),
                     help="run one component pass only (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy, the "
@@ -470,6 +541,8 @@ def main():
             res = bench_dequant_quant(reps)
         elif args.only == "variants":
             res = bench_variants(reps)
+        elif args.only == "adamw":
+            res = bench_adamw(reps)
         elif args.only == "skinny":
             res = bench_70b(reps, do_train=False)
         else:
@@ -556,6 +629,7 @@ def main():
     if not args.quick:
         comps = bench_dequant_quant(max(5, args.steps // 2))
         comps.update(bench_variants(max(3, args.steps // 4)))
+        comps.update(bench_adamw(max(5, args.steps // 2)))
         if not args.no_70b:
             comps.update(bench_70b(max(3, args.steps // 4)))
         out["components"] = comps

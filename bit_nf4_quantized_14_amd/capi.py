@@ -27,11 +27,13 @@ QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 256
 EXPORTS = ("nf4_codebook", "nf4_quantize", "nf4_dequantize",
            "nf4_dequantize_batch", "nf4_merge",
            "qn_codebook", "qn_quantize", "qn_dequantize",
+           "qn_adamw8_step", "qn_adamw8_staging_bytes", "qn_adamw8_paged_step",
            "qlora_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
            "qn_strerror", "qn_profile_kernel")
 QN_DEQUANT_BATCH_MAX = 16
 QN_CODE_NF4, QN_CODE_FP4, QN_CODE_INT4 = 0, 1, 2
 QN_CONST_DQ8, QN_CONST_FP32, QN_CONST_CENTERED = 0, 1, 2
+QN_ADAMW_BLOCK = 256
 
 
 class _NF4Struct(ctypes.Structure):
@@ -45,6 +47,18 @@ class _QStruct(ctypes.Structure):
                 ("gscale", ctypes.c_void_p), ("gmean", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("code", ctypes.c_int32), ("consts_mode", ctypes.c_int32)]
+
+
+class _AdamHP(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double),
+                ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("weight_decay", ctypes.c_double),
+                ("grad_scale", ctypes.c_double)]
+
+
+class _Adam8State(ctypes.Structure):
+    _fields_ = [("m_codes", ctypes.c_void_p), ("m_scale", ctypes.c_void_p),
+                ("r_codes", ctypes.c_void_p), ("r_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -79,6 +93,14 @@ def lib() -> ctypes.CDLL:
     L.qn_quantize.restype = ctypes.c_int
     L.qn_dequantize.argtypes = [qp, vp, vp]
     L.qn_dequantize.restype = ctypes.c_int
+    hpp, stp = ctypes.POINTER(_AdamHP), ctypes.POINTER(_Adam8State)
+    L.qn_adamw8_step.argtypes = [vp, vp, i64, stp, hpp, i64, vp]
+    L.qn_adamw8_step.restype = ctypes.c_int
+    L.qn_adamw8_staging_bytes.argtypes = [i64]
+    L.qn_adamw8_staging_bytes.restype = ctypes.c_size_t
+    L.qn_adamw8_paged_step.argtypes = [vp, vp, i64, stp, vp, ctypes.c_size_t,
+                                       i64, hpp, i64, vp, vp, vp]
+    L.qn_adamw8_paged_step.restype = ctypes.c_int
     L.qlora_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.qlora_workspace_bytes.restype = ctypes.c_size_t
     L.qlora_linear_fwd.argtypes = [vp, i64, sp, vp, vp, i32, f32, vp, i32, vp,
@@ -287,6 +309,69 @@ def qn_dequantize(w: QTensor, out=None, stream=None):
     _check("qn_dequantize", lib().qn_dequantize(ctypes.byref(st), _ptr(out),
                                                 _stream(stream)))
     return out
+
+
+@dataclass
+class AdamW8State:
+    """8-bit AdamW state of n parameters (see qn_adamw8_state in the header):
+    E4M3 codes of m and sqrt(v), one fp32 scale each per 256 elements.
+    Device tensors, or pinned host tensors for the paged step."""
+    m_codes: "object"
+    m_scale: "object"
+    r_codes: "object"
+    r_scale: "object"
+
+    @classmethod
+    def zeros(cls, n: int, device="cuda", pin_memory=False):
+        import torch
+        nb = -(-n // QN_ADAMW_BLOCK)
+        kw = dict(device=device) if not pin_memory else dict(pin_memory=True)
+        return cls(torch.zeros(n, dtype=torch.uint8, **kw),
+                   torch.zeros(nb, dtype=torch.float32, **kw),
+                   torch.zeros(n, dtype=torch.uint8, **kw),
+                   torch.zeros(nb, dtype=torch.float32, **kw))
+
+    def as_struct(self) -> _Adam8State:
+        return _Adam8State(self.m_codes.data_ptr(), self.m_scale.data_ptr(),
+                           self.r_codes.data_ptr(), self.r_scale.data_ptr())
+
+
+def _hparams(lr, beta1, beta2, eps, weight_decay, grad_scale) -> _AdamHP:
+    return _AdamHP(float(lr), float(beta1), float(beta2), float(eps),
+                   float(weight_decay), float(grad_scale))
+
+
+def qn_adamw8_step(p, g, state: AdamW8State, step: int, lr=2e-4, beta1=0.9,
+                   beta2=0.999, eps=1e-8, weight_decay=0.0, grad_scale=1.0,
+                   stream=None):
+    """One 8-bit AdamW step on bf16 parameters p (in place) with fp32
+    gradients g and a device-resident state."""
+    hp = _hparams(lr, beta1, beta2, eps, weight_decay, grad_scale)
+    st = state.as_struct()
+    _check("qn_adamw8_step", lib().qn_adamw8_step(
+        _ptr(p), _ptr(g), p.numel(), ctypes.byref(st), ctypes.byref(hp),
+        int(step), _stream(stream)))
+
+
+def qn_adamw8_staging_bytes(chunk: int) -> int:
+    return int(lib().qn_adamw8_staging_bytes(int(chunk)))
+
+
+def qn_adamw8_paged_step(p, g, host_state: AdamW8State, staging, chunk: int,
+                         step: int, lr=2e-4, beta1=0.9, beta2=0.999,
+                         eps=1e-8, weight_decay=0.0, grad_scale=1.0,
+                         stream=None, h2d_stream=None, d2h_stream=None):
+    """The same step with the state in pinned host memory, paged through
+    the device `staging` buffer in pages of `chunk` elements."""
+    hp = _hparams(lr, beta1, beta2, eps, weight_decay, grad_scale)
+    st = host_state.as_struct()
+    cs = _stream(stream)
+    hs = None if h2d_stream is None else getattr(h2d_stream, "cuda_stream", h2d_stream)
+    ds = None if d2h_stream is None else getattr(d2h_stream, "cuda_stream", d2h_stream)
+    _check("qn_adamw8_paged_step", lib().qn_adamw8_paged_step(
+        _ptr(p), _ptr(g), p.numel(), ctypes.byref(st), _ptr(staging),
+        staging.numel() * staging.element_size(), int(chunk),
+        ctypes.byref(hp), int(step), cs, hs, ds))
 
 
 def qlora_workspace_bytes(M: int, N: int, K: int, r: int, which: int) -> int:

@@ -245,6 +245,76 @@ int qn_quantize(const float* w, const qn_qtensor* out, int32_t* status_dev,
 int qn_dequantize(const qn_qtensor* w, uint16_t* w_bf16, void* stream);
 
 /*
+ * 8-bit AdamW on the adapters -- "Qlora Expert", Core Concept item 3 (paged
+ * optimizers keep the Adam moments in memory paged between GPU and CPU)
+ * and Hyperparameter Guidance (paged_adamw_8bit); "QLoRA Implementation
+ * Details (2025 Edition)", Step 5 (states in CPU RAM, paged in and out);
+ * "QLORA ... paper summary", Notes (adapters stored and trained in BF16).
+ * The pages give no state format; the one used:
+ *   - blocks of QN_ADAMW_BLOCK consecutive elements; per block m is stored
+ *     as OCP FP8 E4M3 codes of m / s_m and the second moment as E4M3 codes
+ *     of sqrt(v) / s_r, s = fp32(block absmax / 448) (0 and codes 0 for a
+ *     zero block); a fresh state is all zero bytes;
+ *   - E4M3 encoding clamps the magnitude to 448 and rounds to nearest
+ *     even; a value that rounds to zero is code 0.
+ * Step t (1-based), per element, in fp32 in this order with no fused
+ * multiply-add, host constants rounded once from double (c1 = 1-beta1,
+ * c2 = 1-beta2, bc1 = 1/(1-beta1^t), bc2 = 1/(1-beta2^t),
+ * decay = 1 - lr*weight_decay):
+ *   g = g*grad_scale;  m = beta1*m' + c1*g;  v = beta2*v' + c2*(g*g)
+ *   p = bf16_rne(p*decay - lr*((m*bc1) / (sqrt(v*bc2) + eps)))
+ * (AdamW with decoupled weight decay), with m', v' = r'^2 decoded from the
+ * stored state; then m and sqrt(v) are re-encoded.  grad_scale carries
+ * gradient clipping (the caller's min(1, max_norm/||g||)).  Gradients must
+ * be finite.
+ */
+#define QN_ADAMW_BLOCK 256
+
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay, grad_scale;
+} qn_adamw_hparams;
+
+/* State of n parameters: m_codes, r_codes: n bytes each (4-byte aligned);
+ * m_scale, r_scale: ceil(n/256) floats each. */
+typedef struct {
+  uint8_t* m_codes;
+  float* m_scale;
+  uint8_t* r_codes;
+  float* r_scale;
+} qn_adamw8_state;
+
+/* qn_adamw8_step -- one step with the state in device memory.
+ * p : device bf16 [n], updated in place, 8-byte aligned;
+ * g : device fp32 [n], 16-byte aligned;  st: device state;
+ * hp: host; step >= 1; 0 <= beta < 1, eps > 0.
+ * Errors: QN_EINVAL, QN_EHIP. */
+int qn_adamw8_step(uint16_t* p, const float* g, int64_t n,
+                   const qn_adamw8_state* st, const qn_adamw_hparams* hp,
+                   int64_t step, void* stream);
+
+/* qn_adamw8_staging_bytes -- device staging the paged step needs for pages
+ * of `chunk` elements (a positive multiple of QN_ADAMW_BLOCK); 0 if chunk
+ * is invalid. */
+size_t qn_adamw8_staging_bytes(int64_t chunk);
+
+/* qn_adamw8_paged_step -- the same step with the state in host memory
+ * (pinned, from hipHostMalloc, for the copies to be asynchronous).  The
+ * state is paged through the caller's device `staging` buffer in pages of
+ * `chunk` elements, two pages in flight: page i is copied in on
+ * `h2d_stream`, stepped on `stream`, and copied back on `d2h_stream`, so the
+ * copies of one page overlap the step of the next.  Null copy streams mean
+ * `stream`.  All work is ordered after what `stream` held at the call, and
+ * `stream` reaches the end of the call only after the last page is back in
+ * host memory.  The copy streams must have the default priority.
+ * Errors: QN_EINVAL, QN_EWORKSPACE (staging smaller than
+ * qn_adamw8_staging_bytes(chunk)), QN_EHIP. */
+int qn_adamw8_paged_step(uint16_t* p, const float* g, int64_t n,
+                         const qn_adamw8_state* host_st, void* staging,
+                         size_t staging_bytes, int64_t chunk,
+                         const qn_adamw_hparams* hp, int64_t step,
+                         void* stream, void* h2d_stream, void* d2h_stream);
+
+/*
  * qlora_workspace_bytes -- device workspace a fused call needs (host).
  * which: QN_FWD or QN_BWD.  Returns 0 for invalid arguments.
  */

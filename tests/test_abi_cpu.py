@@ -180,3 +180,36 @@ def test_variant_validation():
     assert quant(q(), w=p + 4) == capi.QN_EINVAL
     assert deq(q(), out=None) == capi.QN_EINVAL
     assert deq(q(), out=p + 2) == capi.QN_EINVAL
+
+
+def test_adamw8_validation():
+    L = capi.lib()
+    p = 0x10000
+    hp = capi._hparams(2e-4, 0.9, 0.999, 1e-8, 0.0, 1.0)
+    st = capi._Adam8State(p, p, p, p)
+
+    def step(pp=p, g=p, n=1000, s=st, h=hp, t=1):
+        return L.qn_adamw8_step(pp, g, n, ctypes.byref(s), ctypes.byref(h), t, None)
+    assert step(pp=None) == capi.QN_EINVAL
+    assert step(g=None) == capi.QN_EINVAL
+    assert step(g=p + 4) == capi.QN_EINVAL
+    assert step(pp=p + 2) == capi.QN_EINVAL
+    assert step(n=0) == capi.QN_EINVAL
+    assert step(t=0) == capi.QN_EINVAL
+    assert step(s=capi._Adam8State(p, None, p, p)) == capi.QN_EINVAL
+    assert step(s=capi._Adam8State(p + 1, p, p, p)) == capi.QN_EINVAL
+    assert step(h=capi._hparams(2e-4, 1.0, 0.999, 1e-8, 0.0, 1.0)) == capi.QN_EINVAL
+    assert step(h=capi._hparams(2e-4, 0.9, 0.999, 0.0, 0.0, 1.0)) == capi.QN_EINVAL
+    assert step(h=capi._hparams(float("nan"), 0.9, 0.999, 1e-8, 0.0, 1.0)) == capi.QN_EINVAL
+    assert capi.qn_adamw8_staging_bytes(100) == 0
+    assert capi.qn_adamw8_staging_bytes(0) == 0
+    need = capi.qn_adamw8_staging_bytes(4096)
+    assert need >= 2 * (2 * 4096 + 2 * 4 * 16)
+
+    def paged(staging=p, nbytes=need, chunk=4096):
+        return L.qn_adamw8_paged_step(p, p, 10000, ctypes.byref(st), staging,
+                                      nbytes, chunk, ctypes.byref(hp), 1,
+                                      None, None, None)
+    assert paged(staging=None) == capi.QN_EINVAL
+    assert paged(chunk=100) == capi.QN_EINVAL
+    assert paged(nbytes=need - 1) == capi.QN_EWORKSPACE
