@@ -9,7 +9,8 @@ imports nothing from ``bit_nf4_quantized_14_amd``.
 
 ``oracle.codec_variants`` holds the FP4 / INT4 tables and the other ways of
 storing the block constants (none, centered 8-bit); ``oracle.adamw8`` the
-8-bit AdamW step on the adapters.
+8-bit AdamW step on the adapters; ``oracle.dropout`` LoRA dropout with a
+Philox4x32-10 mask.
 
 Every function follows the passage of the source pages it cites; where the
 pages are silent or garbled, the reading taken is stated in the function's

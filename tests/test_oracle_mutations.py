@@ -272,3 +272,38 @@ def test_eps_inside_the_sqrt_is_caught(monkeypatch):
                 - (k["lr"] * u).astype(np.float32)).astype(np.float32)
     monkeypatch.setattr(awm, "param_update_f32", bad)
     _fails(apins.test_adamw_f32_matches_torch_adamw)
+
+
+# --- LoRA dropout -----------------------------------------------------------
+
+import oracle.dropout as drm  # noqa: E402
+import test_oracle_dropout_pins as dpins  # noqa: E402
+
+
+def test_philox_without_key_bump_is_caught(monkeypatch):
+    monkeypatch.setattr(drm, "PHILOX_W0", 0)
+    monkeypatch.setattr(drm, "PHILOX_W1", 0)
+    _fails(dpins.test_philox_known_answers)
+
+
+def test_dropout_without_rescale_is_caught(monkeypatch):
+    monkeypatch.setattr(drm, "keep_scale", lambda p: np.float32(1.0))
+    _fails(dpins.test_inverted_dropout_is_unbiased)
+
+
+def test_unmasked_dx_is_caught(monkeypatch):
+    real = drm.backward_f64
+
+    def bad(dy, x, xd, w, a, b, s, mask_scale, t):
+        return real(dy, x, xd, w, a, b, s, np.ones_like(mask_scale), t)
+    monkeypatch.setattr(drm, "backward_f64", bad)
+    _fails(dpins.test_backward_matches_autograd_of_the_dropout_forward)
+
+
+def test_da_from_undropped_x_is_caught(monkeypatch):
+    real = drm.backward_f64
+
+    def bad(dy, x, xd, w, a, b, s, mask_scale, t):
+        return real(dy, x, x, w, a, b, s, mask_scale, t)
+    monkeypatch.setattr(drm, "backward_f64", bad)
+    _fails(dpins.test_backward_matches_autograd_of_the_dropout_forward)
