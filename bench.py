@@ -50,7 +50,7 @@ def linear_flops(m, n, k, r, backward=True):
 class Problem:
     """Device inputs of one projection: NF4 weight + bf16 X, A, B, dY."""
 
-    def __init__(self, wk, proj, backward=True, y_dtype=None):
+    def __init__(self, wk, proj, backward=True, y_dtype=None, dropout=None):
         import numpy as np
         import torch
         from bit_nf4_quantized_14_amd import capi
@@ -76,7 +76,11 @@ class Problem:
         tdt = torch.bfloat16 if ydt == capi.QN_BF16 else torch.float32
         self.y = torch.empty((self.m, self.n), dtype=tdt, device=dev)
         self.t = torch.empty((self.m, self.r), dtype=torch.float32, device=dev)
-        fb = capi.qlora_workspace_bytes(self.m, self.n, self.k, self.r, capi.QN_FWD)
+        # dropout: (p, seed) of LoRA dropout on the adapter input, or None
+        self.dropout = dropout
+        fb = capi.qlora_workspace_bytes(
+            self.m, self.n, self.k, self.r,
+            capi.QN_FWD if dropout is None else capi.QN_FWD_DROPOUT)
         self.wsf = torch.empty(max(fb, 1), dtype=torch.uint8, device=dev)
         if backward:
             self.dx = torch.empty((self.m, self.k), dtype=tdt, device=dev)
@@ -87,11 +91,24 @@ class Problem:
             self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
     def fwd(self):
+        if self.dropout is not None:
+            p, seed = self.dropout
+            self.capi.qlora_linear_fwd_dropout(
+                self.x, self.w, self.a, self.b, self.r, self.alpha, p, seed,
+                y=self.y, y_dtype=self.ydt, t_save=self.t, ws=self.wsf)
+            return
         self.capi.qlora_linear_fwd(self.x, self.w, self.a, self.b, self.r,
                                    self.alpha, y=self.y, y_dtype=self.ydt,
                                    t_save=self.t, ws=self.wsf)
 
     def bwd(self):
+        if self.dropout is not None:
+            p, seed = self.dropout
+            self.capi.qlora_linear_bwd_dropout(
+                self.dy, self.x, self.w, self.a, self.b, self.r, self.alpha,
+                self.t, p, seed, dx=self.dx, dx_dtype=self.ydt, dA=self.da,
+                dB=self.db, ws=self.ws)
+            return
         self.capi.qlora_linear_bwd(self.dy, self.x, self.w, self.a, self.b,
                                    self.r, self.alpha, self.t, dx=self.dx,
                                    dx_dtype=self.ydt, dA=self.da, dB=self.db,
@@ -301,6 +318,32 @@ def bench_variants(reps, copies=3):
                            f"{copies} copies (> MALL)", "variants": res}}
 
 
+def bench_dropout(reps, p=0.05):
+    """gate7b fwd+bwd with LoRA dropout p on the adapter input (the pages'
+    lora_dropout), against the same step without dropout, both as graph
+    replays of one fwd+bwd."""
+    import torch
+    from bit_nf4_quantized_14_amd import workloads as wl
+    wk = wl.workload("gate7b")
+    res = {}
+    for name, drop in (("without", None), ("with", (p, 0x5EED))):
+        pr = Problem(wk, 0, dropout=drop)
+
+        def step():
+            pr.fwd()
+            pr.bwd()
+        sec = timed_graph(step, reps)
+        res[name] = {"ms_per_step": sec * 1e3,
+                     "TFLOP/s": linear_flops(pr.m, pr.n, pr.k, pr.r) / sec / 1e12}
+        del pr
+        torch.cuda.empty_cache()
+    res["p"] = p
+    res["overhead"] = res["with"]["ms_per_step"] / res["without"]["ms_per_step"] - 1
+    log(f"gate7b dropout p={p}: {res['with']['ms_per_step']:.3f} ms/step vs "
+        f"{res['without']['ms_per_step']:.3f} without ({100 * res['overhead']:+.1f}%)")
+    return {"gate7b_dropout": res}
+
+
 def adapter_params_70b(r=16, layers=80):
     """Parameters of r-rank adapters on all 7 linear projections of every
     layer of a Llama-70B-class model (hidden 8192, GQA k/v 1024, MLP 28672)."""
@@ -508,8 +551,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-70b", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    ap.add_argument("--only", choices=("dequant", "variants", "adamw", "skinny",
-                                       "layer70b"),
+    ap.add_argument("--only", choices=("dequant", "variants", "adamw", "dropout",
+                                       "skinny", "layer70b"),
                     help="run one component pass only (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy, the "
@@ -543,6 +586,8 @@ def main():
             res = bench_variants(reps)
         elif args.only == "adamw":
             res = bench_adamw(reps)
+        elif args.only == "dropout":
+            res = bench_dropout(reps)
         elif args.only == "skinny":
             res = bench_70b(reps, do_train=False)
         else:
@@ -630,6 +675,7 @@ def main():
         comps = bench_dequant_quant(max(5, args.steps // 2))
         comps.update(bench_variants(max(3, args.steps // 4)))
         comps.update(bench_adamw(max(5, args.steps // 2)))
+        comps.update(bench_dropout(max(5, args.steps // 2)))
         if not args.no_70b:
             comps.update(bench_70b(max(3, args.steps // 4)))
         out["components"] = comps

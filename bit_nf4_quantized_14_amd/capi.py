@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libqlora_nf4.so")
 
 QN_OK, QN_EINVAL, QN_EWORKSPACE, QN_EHIP, QN_ENONFINITE = 0, -1, -2, -3, -4
 QN_F32, QN_BF16 = 0, 1
-QN_FWD, QN_BWD = 0, 1
+QN_FWD, QN_BWD, QN_FWD_DROPOUT = 0, 1, 2
 QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 256
 
 # Every symbol the header declares (tests check the library exports them).
@@ -28,6 +28,7 @@ EXPORTS = ("nf4_codebook", "nf4_quantize", "nf4_dequantize",
            "nf4_dequantize_batch", "nf4_merge",
            "qn_codebook", "qn_quantize", "qn_dequantize",
            "qn_adamw8_step", "qn_adamw8_staging_bytes", "qn_adamw8_paged_step",
+           "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
            "qlora_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
            "qn_strerror", "qn_profile_kernel")
 QN_DEQUANT_BATCH_MAX = 16
@@ -59,6 +60,10 @@ class _AdamHP(ctypes.Structure):
 class _Adam8State(ctypes.Structure):
     _fields_ = [("m_codes", ctypes.c_void_p), ("m_scale", ctypes.c_void_p),
                 ("r_codes", ctypes.c_void_p), ("r_scale", ctypes.c_void_p)]
+
+
+class _Dropout(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_double), ("seed", ctypes.c_uint64)]
 
 
 _lib = None
@@ -109,6 +114,14 @@ def lib() -> ctypes.CDLL:
     L.qlora_linear_bwd.argtypes = [vp, vp, i64, sp, vp, vp, i32, f32, vp, vp,
                                    i32, vp, vp, vp, ctypes.c_size_t, vp]
     L.qlora_linear_bwd.restype = ctypes.c_int
+    dp = ctypes.POINTER(_Dropout)
+    L.qlora_linear_fwd_dropout.argtypes = [vp, i64, sp, vp, vp, i32, f32, vp,
+                                           i32, vp, dp, vp, ctypes.c_size_t, vp]
+    L.qlora_linear_fwd_dropout.restype = ctypes.c_int
+    L.qlora_linear_bwd_dropout.argtypes = [vp, vp, i64, sp, vp, vp, i32, f32,
+                                           vp, vp, i32, vp, vp, dp, vp,
+                                           ctypes.c_size_t, vp]
+    L.qlora_linear_bwd_dropout.restype = ctypes.c_int
     L.qn_profile_kernel.argtypes = [ctypes.c_char_p, vp, vp, i32]
     L.qn_profile_kernel.restype = ctypes.c_int
     L.qn_strerror.argtypes = [ctypes.c_int]
@@ -423,6 +436,61 @@ def qlora_linear_bwd(dy, x, w: NF4Tensor, A, B, r: int, alpha: float,
         _ptr(dy), _ptr(x), M, ctypes.byref(st), _ptr(A), _ptr(B), r,
         float(alpha), _ptr(t_saved), _ptr(dx), dx_dtype, _ptr(dA), _ptr(dB),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return dx, dA, dB
+
+
+def qlora_linear_fwd_dropout(x, w: NF4Tensor, A, B, r: int, alpha: float,
+                             p: float, seed: int, y=None,
+                             y_dtype: int = QN_F32, t_save=None, ws=None,
+                             stream=None):
+    """Fused forward with LoRA dropout (probability p, 64-bit seed) on the
+    adapter input; returns (y, t_save)."""
+    import torch
+    M = x.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, w.rows), device=dev,
+                        dtype=torch.float32 if y_dtype == QN_F32 else torch.bfloat16)
+    if t_save is None:
+        t_save = torch.empty((M, r), device=dev, dtype=torch.float32)
+    if ws is None:
+        ws = torch.empty(max(1, qlora_workspace_bytes(M, w.rows, w.cols, r,
+                                                      QN_FWD_DROPOUT)),
+                         dtype=torch.uint8, device=dev)
+    st = w.as_struct()
+    d = _Dropout(float(p), int(seed) & 0xFFFFFFFFFFFFFFFF)
+    _check("qlora_linear_fwd_dropout", lib().qlora_linear_fwd_dropout(
+        _ptr(x), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
+        _ptr(y), y_dtype, _ptr(t_save), ctypes.byref(d), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return y, t_save
+
+
+def qlora_linear_bwd_dropout(dy, x, w: NF4Tensor, A, B, r: int, alpha: float,
+                             t_saved, p: float, seed: int, dx=None,
+                             dx_dtype: int = QN_F32, dA=None, dB=None,
+                             ws=None, stream=None):
+    """Fused backward with the forward's dropout mask; returns (dx, dA, dB)."""
+    import torch
+    M = x.shape[0]
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((M, w.cols), device=dev,
+                         dtype=torch.float32 if dx_dtype == QN_F32 else torch.bfloat16)
+    if dA is None:
+        dA = torch.empty((r, w.cols), device=dev, dtype=torch.float32)
+    if dB is None:
+        dB = torch.empty((w.rows, r), device=dev, dtype=torch.float32)
+    if ws is None:
+        ws = torch.empty(max(1, qlora_workspace_bytes(M, w.rows, w.cols, r, QN_BWD)),
+                         dtype=torch.uint8, device=dev)
+    st = w.as_struct()
+    d = _Dropout(float(p), int(seed) & 0xFFFFFFFFFFFFFFFF)
+    _check("qlora_linear_bwd_dropout", lib().qlora_linear_bwd_dropout(
+        _ptr(dy), _ptr(x), M, ctypes.byref(st), _ptr(A), _ptr(B), r,
+        float(alpha), _ptr(t_saved), _ptr(dx), dx_dtype, _ptr(dA), _ptr(dB),
+        ctypes.byref(d), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
     return dx, dA, dB
 
 

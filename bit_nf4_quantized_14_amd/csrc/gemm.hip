@@ -306,13 +306,82 @@ __device__ __forceinline__ void gemm_step(
   Wc = Wn;
 }
 
+// Adapter term, 2 * rpad more reduction steps straight from global memory
+// (small, L2-resident arrays): A side the bf16 hi and lo parts of s*T
+// (forward) or s*G (backward), [M][rpad]; B side [NOUT][rpad], B (forward)
+// or A^T (backward), zero-padded to rpad columns.
 template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_adapter(
+    const uint16_t* La_hi, const uint16_t* La_lo, const uint16_t* Lb, int M,
+    int NOUT, int rpad, int m0, int c0, int wm, int wn, int lane,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
+  const rsrc_t rh = make_rsrc(La_hi, (uint32_t)((int64_t)M * rpad * 2));
+  const rsrc_t rl = make_rsrc(La_lo, (uint32_t)((int64_t)M * rpad * 2));
+  const rsrc_t rb = make_rsrc(Lb, (uint32_t)((int64_t)NOUT * rpad * 2));
+  for (int j0 = 0; j0 < rpad; j0 += 16) {
+    const int jc = j0 + 8 * (lane >> 5);
+    u32x4 ah[C::TM], al[C::TM], b[C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const uint32_t off =
+          (uint32_t)(((int64_t)(m0 + wm * C::WM + i * 32 + (lane & 31)) * rpad + jc) * 2);
+      ah[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+      al[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const uint32_t off =
+          (uint32_t)(((int64_t)(c0 + wn * C::WN + j * 32 + (lane & 31)) * rpad + jc) * 2);
+      b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        acc[i][j] = mfma32(ah[i], b[j], acc[i][j]);
+        acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
+      }
+  }
+}
+
+// LoRA dropout on the adapter term of dX: accumulator element (row, col)
+// times mask(row, col) / (1 - p).  Accumulator v of lane l holds row
+// 8 (v / 4) + 4 (l / 32) + v % 4 of its 32 x 32 tile, so each group of four
+// (rows r0 .. r0 + 3, r0 % 4 == 0, one column) is one generator call.
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_drop_acc(
+    int m0, int c0, int wm, int wn, int lane, const DropArgs& dp,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int col = c0 + wn * C::WN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int r0 = m0 + wm * C::WM + i * 32 + 8 * vg + 4 * (lane >> 5);
+        const u32x4 w = philox4x32_10(static_cast<uint32_t>(col),
+                                      static_cast<uint32_t>(r0) >> 2, dp.key0,
+                                      dp.key1);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float x = acc[i][j][4 * vg + t];
+          acc[i][j][4 * vg + t] = ws[t] >= dp.thresh ? x * dp.scale : 0.0f;
+        }
+      }
+    }
+}
+
+template <int BM, int BN, bool BWD, bool DROP>
 __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
     const uint16_t* __restrict__ Aop, const uint8_t* __restrict__ packed,
     const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
     const uint16_t* __restrict__ La_hi, const uint16_t* __restrict__ La_lo,
     const uint16_t* __restrict__ Lb, int M, int N, int K, int rpad,
-    void* __restrict__ out, int out_bf16, Codebook cb) {
+    void* __restrict__ out, int out_bf16, Codebook cb, DropArgs dp) {
   using C = GemmCfg<BM, BN, BWD>;
   // Four distinct LDS buffers so that the compiler can see that the tiles
   // being filled never alias the tiles being read.
@@ -343,6 +412,14 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  // with dropout the (masked) adapter term goes first; dY W' is then added
+  // on top by the main loop
+  if constexpr (DROP) {
+    gemm_adapter<BM, BN, BWD>(La_hi, La_lo, Lb, M, NOUT, rpad, m0, c0, wm, wn,
+                              lane, acc);
+    gemm_drop_acc<BM, BN, BWD>(m0, c0, wm, wn, lane, dp, acc);
+  }
+
   // Steps past the end read out of range: their tiles are zeros (a zero
   // block constant dequantizes every code to zero), so the loop runs whole
   // pairs of steps without branches.
@@ -365,39 +442,9 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
                            K, KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
   }
 
-  // Adapter term, 2 * rpad more reduction steps straight from global memory
-  // (small, L2-resident arrays): A side the bf16 hi and lo parts of s*T
-  // (forward) or s*G (backward), [M][rpad]; B side [NOUT][rpad], B (forward)
-  // or A^T (backward), zero-padded to rpad columns.
-  {
-    const rsrc_t rh = make_rsrc(La_hi, (uint32_t)((int64_t)M * rpad * 2));
-    const rsrc_t rl = make_rsrc(La_lo, (uint32_t)((int64_t)M * rpad * 2));
-    const rsrc_t rb = make_rsrc(Lb, (uint32_t)((int64_t)NOUT * rpad * 2));
-    for (int j0 = 0; j0 < rpad; j0 += 16) {
-      const int jc = j0 + 8 * (lane >> 5);
-      u32x4 ah[C::TM], al[C::TM], b[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const uint32_t off =
-            (uint32_t)(((int64_t)(m0 + wm * C::WM + i * 32 + (lane & 31)) * rpad + jc) * 2);
-        ah[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
-        al[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
-      }
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const uint32_t off =
-            (uint32_t)(((int64_t)(c0 + wn * C::WN + j * 32 + (lane & 31)) * rpad + jc) * 2);
-        b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
-      }
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-          acc[i][j] = mfma32(ah[i], b[j], acc[i][j]);
-          acc[i][j] = mfma32(al[i], b[j], acc[i][j]);
-        }
-    }
-  }
+  if constexpr (!DROP)
+    gemm_adapter<BM, BN, BWD>(La_hi, La_lo, Lb, M, NOUT, rpad, m0, c0, wm, wn,
+                              lane, acc);
 
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -423,34 +470,46 @@ template <int BM, int BN, bool BWD>
 void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                    const uint16_t* La_hi, const uint16_t* La_lo,
                    const uint16_t* Lb, int M, int rpad, void* out,
-                   int out_bf16) {
+                   int out_bf16, const DropArgs* drop) {
   const int N = (int)w->rows, K = (int)w->cols;
   const int nout = BWD ? K : N;
   const unsigned tiles = (unsigned)(cdiv(M, BM) * cdiv(nout, BN));
-  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD>),
+  if constexpr (BWD) {
+    if (drop != nullptr) {
+      QN_LAUNCH("k_bwd_dx_gemm", (k_gemm<BM, BN, BWD, true>), dim3(tiles),
+                dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
+                w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
+                qn::codebook(), *drop);
+      return;
+    }
+  }
+  const DropArgs none{};
+  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD, false>),
             dim3(tiles), dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs, w->gscale,
-            La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16, qn::codebook());
+            La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16, qn::codebook(), none);
 }
 
 template <bool BWD>
 void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  const uint16_t* La_hi, const uint16_t* La_lo,
                  const uint16_t* Lb, int M, int rpad, void* out,
-                 int out_bf16) {
+                 int out_bf16, const DropArgs* drop) {
   const int64_t nout = BWD ? w->cols : w->rows;
   if (cdiv(M, 256) * cdiv(nout, 256) >= 192)
     launch_gemm_t<256, 256, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
-                                 out_bf16);
+                                 out_bf16, drop);
   else
     launch_gemm_t<128, 128, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
-                                 out_bf16);
+                                 out_bf16, drop);
 }
 
 template void launch_gemm<false>(hipStream_t, const uint16_t*, const nf4_tensor*,
                                  const uint16_t*, const uint16_t*,
-                                 const uint16_t*, int, int, void*, int);
+                                 const uint16_t*, int, int, void*, int,
+                                 const DropArgs*);
 template void launch_gemm<true>(hipStream_t, const uint16_t*, const nf4_tensor*,
                                 const uint16_t*, const uint16_t*,
-                                const uint16_t*, int, int, void*, int);
+                                const uint16_t*, int, int, void*, int,
+                                const DropArgs*);
 
 }  // namespace qn

@@ -4,6 +4,8 @@
 // hook.  "QLoRA Guide" (Forward pass diagram: W_bf16 x + B(A(x)); only A
 // and B get gradients), "QLoRA Implementation Details (2025 Edition)"
 // (Step 4: scale alpha / r).
+#include <cmath>
+
 #include "qn_host.h"
 
 namespace qn {
@@ -36,10 +38,10 @@ bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
 }
 
 FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
-                                  int32_t r) {
+                                  int32_t r, bool general) {
   FwdWorkspace L{};
   L.rpad = 16 * rank_tiles(r);
-  if (M <= qn::QN_SKINNY_M) {
+  if (M <= qn::QN_SKINNY_M && !general) {
     const SkinnyPlan P = skinny_plan(M, N, K, r);
     L.slices = P.slices;
     L.ks = P.ks;
@@ -133,15 +135,38 @@ const char* qn_strerror(int code) {
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
                              int32_t which) {
   if (M <= 0 || N <= 0 || K <= 0 || r < 1 || r > QN_MAX_RANK) return 0;
-  if (which == QN_FWD) return qn::fwd_workspace_layout(M, N, K, r).total;
+  if (which == QN_FWD) return qn::fwd_workspace_layout(M, N, K, r, false).total;
+  if (which == QN_FWD_DROPOUT)
+    return qn::fwd_workspace_layout(M, N, K, r, true).total;
   if (which == QN_BWD) return qn::bwd_workspace_layout(M, N, K, r).total;
   return 0;
 }
 
-int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
-                     const uint16_t* A, const uint16_t* B, int32_t r,
-                     float alpha, void* y, int32_t y_dtype, float* t_save,
-                     void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Kernel arguments of a qn_dropout; false for p outside [0, 1).  p == 0
+// keeps every element unscaled, which is the layer without dropout, so it
+// maps to no dropout at all (*use = false).
+bool drop_args(const qn_dropout* d, qn::DropArgs* out, bool* use) {
+  *use = false;
+  if (d == nullptr) return true;
+  if (!(d->p >= 0.0 && d->p < 1.0)) return false;
+  if (d->p == 0.0) return true;
+  const double t = std::floor(d->p * 4294967296.0);
+  out->thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : static_cast<uint32_t>(t);
+  out->scale = static_cast<float>(1.0 / (1.0 - d->p));
+  out->key0 = static_cast<uint32_t>(d->seed & 0xFFFFFFFFu);
+  out->key1 = static_cast<uint32_t>(d->seed >> 32);
+  *use = true;
+  return true;
+}
+
+int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
+               const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+               void* y, int32_t y_dtype, float* t_save, const qn_dropout* drop,
+               void* ws, size_t ws_bytes, void* stream) {
   if (x == nullptr || A == nullptr || B == nullptr || y == nullptr ||
       t_save == nullptr)
     return QN_EINVAL;
@@ -149,14 +174,20 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   if (y_dtype != QN_F32 && y_dtype != QN_BF16) return QN_EINVAL;
   if (!aligned16(x) || !aligned16(A) || !aligned16(y) || !aligned16(t_save))
     return QN_EINVAL;
+  qn::DropArgs da{};
+  bool use_drop = false;
+  if (!drop_args(drop, &da, &use_drop)) return QN_EINVAL;
   const int64_t N = w->rows, K = w->cols;
-  const qn::FwdWorkspace L = qn::fwd_workspace_layout(M, N, K, r);
+  // a forward with dropout always takes the general path (the skinny
+  // kernel shares one X slice between W and A rows)
+  const qn::FwdWorkspace L =
+      qn::fwd_workspace_layout(M, N, K, r, drop != nullptr);
   if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
     return QN_EWORKSPACE;
   const float s = alpha / (float)r;
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
   hipStream_t st = (hipStream_t)stream;
-  if (M <= qn::QN_SKINNY_M) {
+  if (M <= qn::QN_SKINNY_M && !use_drop && drop == nullptr) {
     launch_skinny(st, x, Mi, w, A, B, (int)r, L.rpad, s, t_save, y,
                   (int)(y_dtype == QN_BF16), ws_at<float>(ws, L.part));
     return check_launch();
@@ -169,7 +200,8 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   // T = X A^T: partials over column blocks of X
   const StreamPlan P = stream_plan(RS_ROWS, M, K, jt);
   launch_rank_stream<RS_ROWS>(st, "k_rank_stream_t", P, x, Mi, Ki, A, (int)r,
-                              nullptr, nullptr, 0, prow, nullptr);
+                              nullptr, nullptr, 0, prow, nullptr,
+                              use_drop ? &da : nullptr);
   // T (fp32, saved), hi/lo parts of s T, B zero-padded to [N][rpad]
   FinishArgs fa = finish_args();
   fa.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, P.nb, Mi, Mi, (int)r,
@@ -181,12 +213,11 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   return check_launch();
 }
 
-int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
-                     const nf4_tensor* w, const uint16_t* A,
-                     const uint16_t* B, int32_t r, float alpha,
-                     const float* t_saved, void* dx, int32_t dx_dtype,
-                     float* dA, float* dB, void* ws, size_t ws_bytes,
-                     void* stream) {
+int linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
+               const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
+               int32_t r, float alpha, const float* t_saved, void* dx,
+               int32_t dx_dtype, float* dA, float* dB, const qn_dropout* drop,
+               void* ws, size_t ws_bytes, void* stream) {
   if (dy == nullptr || x == nullptr || A == nullptr || B == nullptr ||
       t_saved == nullptr || dx == nullptr || dA == nullptr || dB == nullptr)
     return QN_EINVAL;
@@ -194,6 +225,9 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
   if (dx_dtype != QN_F32 && dx_dtype != QN_BF16) return QN_EINVAL;
   if (!aligned16(dy) || !aligned16(x) || !aligned16(A) || !aligned16(dx))
     return QN_EINVAL;
+  qn::DropArgs da{};
+  bool use_drop = false;
+  if (!drop_args(drop, &da, &use_drop)) return QN_EINVAL;
   const int64_t N = w->rows, K = w->cols;
   const qn::BwdWorkspace L = qn::bwd_workspace_layout(M, N, K, r);
   if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
@@ -233,15 +267,62 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
   launch_finish(st, f1);
   // dX = dY W' + (s G) A
   launch_gemm<true>(st, dy, w, Gh, Gl, Atp, Mi, L.rpad, dx,
-                    (int)(dx_dtype == QN_BF16));
+                    (int)(dx_dtype == QN_BF16), use_drop ? &da : nullptr);
   // dA = (s G)^T X: row-block partials of out[k][j] -> dA[j][k]
   const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
   launch_rank_stream<RS_COLS>(st, "k_rank_stream_da", Pa, x, Mi, Ki, nullptr,
-                              (int)r, UGh, UGl, Mp, nullptr, pcol);
+                              (int)r, UGh, UGl, Mp, nullptr, pcol,
+                              use_drop ? &da : nullptr);
   FinishArgs f2 = finish_args();
   f2.Cc = FinishCols{pcol, Pa.mb, Ki, (int)r, L.rpad, dA, (int64_t)1, K};
   launch_finish(st, f2);
   return check_launch();
 }
 
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
+                     const uint16_t* A, const uint16_t* B, int32_t r,
+                     float alpha, void* y, int32_t y_dtype, float* t_save,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return linear_fwd(x, M, w, A, B, r, alpha, y, y_dtype, t_save, nullptr, ws,
+                    ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const uint16_t* x, int64_t M,
+                             const nf4_tensor* w, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float alpha,
+                             void* y, int32_t y_dtype, float* t_save,
+                             const qn_dropout* drop, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (drop == nullptr) return QN_EINVAL;
+  return linear_fwd(x, M, w, A, B, r, alpha, y, y_dtype, t_save, drop, ws,
+                    ws_bytes, stream);
+}
+
+int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
+                     const nf4_tensor* w, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha,
+                     const float* t_saved, void* dx, int32_t dx_dtype,
+                     float* dA, float* dB, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return linear_bwd(dy, x, M, w, A, B, r, alpha, t_saved, dx, dx_dtype, dA,
+                    dB, nullptr, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_dropout(const uint16_t* dy, const uint16_t* x,
+                             int64_t M, const nf4_tensor* w,
+                             const uint16_t* A, const uint16_t* B, int32_t r,
+                             float alpha, const float* t_saved, void* dx,
+                             int32_t dx_dtype, float* dA, float* dB,
+                             const qn_dropout* drop, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (drop == nullptr) return QN_EINVAL;
+  return linear_bwd(dy, x, M, w, A, B, r, alpha, t_saved, dx, dx_dtype, dA,
+                    dB, drop, ws, ws_bytes, stream);
+}
+
 }  // extern "C"
+

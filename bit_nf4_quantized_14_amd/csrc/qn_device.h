@@ -150,6 +150,96 @@ __device__ __forceinline__ uint16_t decode1(const Codebook& cb, uint32_t code,
 }
 
 // ---------------------------------------------------------------------------
+// LoRA dropout mask (inverted dropout on the adapter branch input).
+// Element (m, k) of X is kept when word m % 4 of Philox4x32-10 at counter
+// (k, m / 4, 0, 0) under key (key0, key1) is >= thresh; a kept element
+// becomes bf16_rne(fp32(x) * scale), a dropped one 0.
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011): ten rounds of two
+// 32x32 -> 64-bit products of words 0 and 2 with M0, M1, the output
+// (hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0), and the key advanced by
+// (W0, W1) after each round.
+// ---------------------------------------------------------------------------
+struct DropArgs {
+  uint32_t key0, key1;
+  uint32_t thresh;
+  float scale;
+};
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
+                                               uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t x0 = c0, x1 = c1, x2 = 0, x3 = 0;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t hi0 = __umulhi(M0, x0), lo0 = M0 * x0;
+    const uint32_t hi1 = __umulhi(M1, x2), lo1 = M1 * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  u32x4 r;
+  r.x = x0;
+  r.y = x1;
+  r.z = x2;
+  r.w = x3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pick4(const u32x4& w, int sel) {
+  const uint32_t a = w.x, b = w.y, c = w.z, d = w.w;
+  return sel == 0 ? a : (sel == 1 ? b : (sel == 2 ? c : d));
+}
+
+// One bf16 element (low 16 bits of x16) after dropout with Philox word w.
+__device__ __forceinline__ uint32_t drop_bf16(uint32_t x16, uint32_t w,
+                                              const DropArgs& d) {
+  return w >= d.thresh
+             ? (pack_bf16x2(bf16_to_f32(x16 & 0xFFFFu) * d.scale, 0.0f) & 0xFFFFu)
+             : 0u;
+}
+
+// 8 consecutive columns k0 .. k0 + 7 of row m (natural order, two per
+// dword): one generator call per column, word m % 4 of each.
+__device__ __forceinline__ u32x4 drop_row8(const u32x4& a, int m, int k0,
+                                           const DropArgs& d) {
+  const uint32_t q = static_cast<uint32_t>(m) >> 2;
+  const int sel = m & 3;
+  const uint32_t in[4] = {a.x, a.y, a.z, a.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t wl = pick4(philox4x32_10(k0 + 2 * h, q, d.key0, d.key1), sel);
+    const uint32_t wh = pick4(philox4x32_10(k0 + 2 * h + 1, q, d.key0, d.key1), sel);
+    out[h] = drop_bf16(in[h], wl, d) | (drop_bf16(in[h] >> 16, wh, d) << 16);
+  }
+  u32x4 r;
+  r.x = out[0];
+  r.y = out[1];
+  r.z = out[2];
+  r.w = out[3];
+  return r;
+}
+
+// 8 consecutive rows m0 .. m0 + 7 (m0 % 4 == 0) of column k (natural
+// order, two per dword): two generator calls.
+__device__ __forceinline__ u32x4 drop_col8(const u32x4& a, int m0, int k,
+                                           const DropArgs& d) {
+  const uint32_t q = static_cast<uint32_t>(m0) >> 2;
+  const u32x4 w0 = philox4x32_10(k, q, d.key0, d.key1);
+  const u32x4 w1 = philox4x32_10(k, q + 1, d.key0, d.key1);
+  u32x4 r;
+  r.x = drop_bf16(a.x, w0.x, d) | (drop_bf16(a.x >> 16, w0.y, d) << 16);
+  r.y = drop_bf16(a.y, w0.z, d) | (drop_bf16(a.y >> 16, w0.w, d) << 16);
+  r.z = drop_bf16(a.z, w1.x, d) | (drop_bf16(a.z >> 16, w1.y, d) << 16);
+  r.w = drop_bf16(a.w, w1.z, d) | (drop_bf16(a.w >> 16, w1.w, d) << 16);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // MFMA helpers.  v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of A
 // and column (l % 32) of B, each with 8 consecutive reduction elements
 // starting at 8 * (l / 32).  Accumulator register v of lane l holds

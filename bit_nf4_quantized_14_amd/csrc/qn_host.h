@@ -96,10 +96,13 @@ T* ws_at(void* ws, size_t off) {
 
 // ---- gemm.hip: fused dequant + MFMA GEMM (Y = X W'^T + s T B^T or
 // dX = dY W' + s G A), 256 x 256 or 128 x 128 tiles by size.
+// drop (backward only): the adapter term s G A is multiplied elementwise by
+// the dropout mask / (1 - p) before dY W' is added; nullptr for none.
 template <bool BWD>
 void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  const uint16_t* La_hi, const uint16_t* La_lo,
-                 const uint16_t* Lb, int M, int rpad, void* out, int out_bf16);
+                 const uint16_t* Lb, int M, int rpad, void* out, int out_bf16,
+                 const DropArgs* drop = nullptr);
 
 // ---- rank.hip: rank-r side products and their reductions.
 enum { RS_ROWS = 1, RS_COLS = 2 };
@@ -109,11 +112,14 @@ struct StreamPlan {
 };
 StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt);
 
+// drop: LoRA dropout applied to S (= X) in the RS_ROWS and RS_COLS passes,
+// or nullptr.
 template <int MODE>
 void launch_rank_stream(hipStream_t st, const char* kname, const StreamPlan& P,
                         const uint16_t* S, int M, int C, const uint16_t* R,
                         int r, const uint16_t* Uh, const uint16_t* Ul, int ldu,
-                        float* prow, float* pcol);
+                        float* prow, float* pcol,
+                        const DropArgs* drop = nullptr);
 
 struct FinishRows {
   const float* src;

@@ -42,7 +42,10 @@ struct BwdWorkspace {
   int32_t rpad;
 };
 
-FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K, int32_t r);
+// general: the layout of the general path also for M <= QN_SKINNY_M (a
+// forward with dropout never takes the skinny path).
+FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K, int32_t r,
+                                  bool general);
 BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
 }  // namespace qn

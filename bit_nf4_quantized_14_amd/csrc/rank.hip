@@ -178,15 +178,20 @@ __device__ __forceinline__ void rs_stage_dma(rsrc_t rs, rsrc_t rr, char* dS,
   }
 }
 
-template <int MODE, int JT>
+// With DROP, S is X and each operand read from the S tile is replaced by
+// its LoRA-dropout version (qn_device.h) at its absolute (row, column):
+// rows m0 + local row, columns 64 (SUB stage + u) + local column.
+template <int MODE, int JT, bool DROP>
 __device__ __forceinline__ void rs_stage_compute(
     const char* sS, const char* sR, const uint16_t* sUh, const uint16_t* sUl,
     int wave, int lane, f32x4 (&accR)[RsCfg<MODE, JT>::TR][JT],
-    f32x4 (&accC)[RsCfg<MODE, JT>::SUB][JT]) {
+    f32x4 (&accC)[RsCfg<MODE, JT>::SUB][JT], int stage, int m0,
+    const DropArgs& dp) {
   using G = RsCfg<MODE, JT>;
 #pragma unroll
   for (int u = 0; u < G::SUB; ++u) {
     const char* tS = sS + u * G::RM * 128;
+    const int col0 = (stage * G::SUB + u) * 64;
     if (G::ROWS) {
       const char* tR = sR + u * G::RP * 128;
 #pragma unroll
@@ -197,8 +202,10 @@ __device__ __forceinline__ void rs_stage_compute(
           b[t] = rs_read_row(tR, 16 * t + (lane & 15), 4 * s + (lane >> 4));
 #pragma unroll
         for (int tr = 0; tr < G::TR; ++tr) {
-          const u32x4 a = rs_read_row(
-              tS, wave * (G::RM / 4) + 16 * tr + (lane & 15), 4 * s + (lane >> 4));
+          const int lrow = wave * (G::RM / 4) + 16 * tr + (lane & 15);
+          u32x4 a = rs_read_row(tS, lrow, 4 * s + (lane >> 4));
+          if constexpr (DROP)
+            a = drop_row8(a, m0 + lrow, col0 + 8 * (4 * s + (lane >> 4)), dp);
 #pragma unroll
           for (int t = 0; t < JT; ++t) accR[tr][t] = mfma16(a, b[t], accR[tr][t]);
         }
@@ -209,7 +216,10 @@ __device__ __forceinline__ void rs_stage_compute(
       for (int t = 0; t < JT; ++t) accC[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
       for (int s2 = 0; s2 < G::RM / 32; ++s2) {
-        const u32x4 a = rs_read_colT(tS, 32 * s2, 16 * wave, lane);
+        u32x4 a = rs_read_colT(tS, 32 * s2, 16 * wave, lane);
+        if constexpr (DROP)
+          a = drop_col8(a, m0 + 32 * s2 + 8 * (lane >> 4),
+                        col0 + 16 * wave + (lane & 15), dp);
 #pragma unroll
         for (int t = 0; t < JT; ++t) {
           const int uo = (16 * t + (lane & 15)) * G::PU + 32 * s2 + 8 * (lane >> 4);
@@ -246,12 +256,12 @@ __device__ __forceinline__ void rs_store_cols(
   }
 }
 
-template <int MODE, int JT>
+template <int MODE, int JT, bool DROP>
 __global__ __launch_bounds__(256) void k_rank_stream(
     const uint16_t* __restrict__ S, int M, int C,
     const uint16_t* __restrict__ R, int r, const uint16_t* __restrict__ Uh,
     const uint16_t* __restrict__ Ul, int ldu, int cpb,
-    float* __restrict__ prow, float* __restrict__ pcol) {
+    float* __restrict__ prow, float* __restrict__ pcol, DropArgs dp) {
   using G = RsCfg<MODE, JT>;
   // distinct buffers, so the compiler can tell the tile being filled from
   // the tiles being read
@@ -322,7 +332,8 @@ __global__ __launch_bounds__(256) void k_rank_stream(
   do {                                                                        \
     if (G::COLS && (I) > sb)                                                  \
       rs_store_cols<MODE, JT>(rc, (I) - 1, C, wave, lane, accC);              \
-    rs_stage_compute<MODE, JT>(CS, CR, sUh, sUl, wave, lane, accR, accC);     \
+    rs_stage_compute<MODE, JT, DROP>(CS, CR, sUh, sUl, wave, lane, accR,      \
+                                     accC, (I), m0, dp);                      \
     if ((I) + G::NBUF - 1 < se) {                                             \
       rs_stage_dma<MODE, JT>(rs, rr, FS, FR, C, nvalid, r, (I) + G::NBUF - 1, \
                              wave, lane);                                     \
@@ -451,11 +462,22 @@ template <int MODE>
 void launch_rank_stream(hipStream_t st, const char* kname, const StreamPlan& P,
                         const uint16_t* S, int M, int C, const uint16_t* R,
                         int r, const uint16_t* Uh, const uint16_t* Ul, int ldu,
-                        float* prow, float* pcol) {
+                        float* prow, float* pcol, const DropArgs* drop) {
   const dim3 grid((unsigned)P.nb, (unsigned)P.mb);
-  QN_RANK_DISPATCH(r, QN_LAUNCH(kname, (k_rank_stream<MODE, JT>), grid,
+  // the dY pass (rows and columns at once) never carries dropout
+  if constexpr (MODE != (RS_ROWS | RS_COLS)) {
+    if (drop != nullptr) {
+      const DropArgs dp = *drop;
+      QN_RANK_DISPATCH(r, QN_LAUNCH(kname, (k_rank_stream<MODE, JT, true>), grid,
+                                    dim3(256), st, S, M, C, R, r, Uh, Ul, ldu,
+                                    P.cpb, prow, pcol, dp));
+      return;
+    }
+  }
+  const DropArgs none{};
+  QN_RANK_DISPATCH(r, QN_LAUNCH(kname, (k_rank_stream<MODE, JT, false>), grid,
                                 dim3(256), st, S, M, C, R, r, Uh, Ul, ldu,
-                                P.cpb, prow, pcol));
+                                P.cpb, prow, pcol, none));
 }
 
 FinishArgs finish_args() {
@@ -478,13 +500,14 @@ void launch_finish(hipStream_t st, FinishArgs& a) {
 template void launch_rank_stream<RS_ROWS>(hipStream_t, const char*, const StreamPlan&,
                                           const uint16_t*, int, int, const uint16_t*,
                                           int, const uint16_t*, const uint16_t*, int,
-                                          float*, float*);
+                                          float*, float*, const DropArgs*);
 template void launch_rank_stream<RS_COLS>(hipStream_t, const char*, const StreamPlan&,
                                           const uint16_t*, int, int, const uint16_t*,
                                           int, const uint16_t*, const uint16_t*, int,
-                                          float*, float*);
+                                          float*, float*, const DropArgs*);
 template void launch_rank_stream<RS_ROWS | RS_COLS>(
     hipStream_t, const char*, const StreamPlan&, const uint16_t*, int, int,
-    const uint16_t*, int, const uint16_t*, const uint16_t*, int, float*, float*);
+    const uint16_t*, int, const uint16_t*, const uint16_t*, int, float*, float*,
+    const DropArgs*);
 
 }  // namespace qn

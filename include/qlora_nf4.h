@@ -57,6 +57,7 @@ extern "C" {
 
 #define QN_FWD 0
 #define QN_BWD 1
+#define QN_FWD_DROPOUT 2    /* forward with LoRA dropout (general path) */
 
 #define QN_BLOCK 64         /* weights per absmax block */
 #define QN_GROUP 256        /* block constants per double-quant group */
@@ -316,7 +317,8 @@ int qn_adamw8_paged_step(uint16_t* p, const float* g, int64_t n,
 
 /*
  * qlora_workspace_bytes -- device workspace a fused call needs (host).
- * which: QN_FWD or QN_BWD.  Returns 0 for invalid arguments.
+ * which: QN_FWD, QN_BWD or QN_FWD_DROPOUT.  Returns 0 for invalid
+ * arguments.
  */
 size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
                              int32_t which);
@@ -371,6 +373,47 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
                      const float* t_saved, void* dx, int32_t dx_dtype,
                      float* dA, float* dB, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * LoRA dropout -- qlora_linear_fwd / qlora_linear_bwd with dropout on the
+ * adapter branch input.  The pages carry lora_dropout (0.05 in "Qlora
+ * Expert", Core Concept code and "QLoRA Guide", Example; 0.1 in "QLoRA
+ * Implementation Details (2025 Edition)", Step 4) next to r and
+ * lora_alpha.  Inverted dropout on X before A, the same mask in the
+ * backward:
+ *   X_d = X * mask / (1 - p)  (kept: bf16_rne(fp32(x) * fp32(1/(1-p))))
+ *   T = X_d A^T;  Y = X W'^T + s T B^T
+ *   dX = dY W' + s (G A) * mask / (1 - p);  dA = s G^T X_d;  dB = s dY^T T
+ * The mask is counter-based, so the backward regenerates it: element
+ * (m, k) of X is kept when word m % 4 of Philox4x32-10 (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) at counter
+ * (k, m / 4, 0, 0) under key (seed mod 2^32, seed / 2^32) is at least
+ * floor(p * 2^32).  Use one seed per layer and step; the forward and
+ * backward of one step must get the same p and seed.  p == 0 is the layer
+ * without dropout.  The forward's workspace is qlora_workspace_bytes(...,
+ * QN_FWD_DROPOUT) (the general path for every M); the backward's is
+ * QN_BWD.  Arguments otherwise as qlora_linear_fwd / qlora_linear_bwd.
+ * Errors: as those, and QN_EINVAL for a null drop or p outside [0, 1).
+ */
+typedef struct {
+  double p;
+  uint64_t seed;
+} qn_dropout;
+
+int qlora_linear_fwd_dropout(const uint16_t* x, int64_t M,
+                             const nf4_tensor* w, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float alpha,
+                             void* y, int32_t y_dtype, float* t_save,
+                             const qn_dropout* drop, void* ws,
+                             size_t ws_bytes, void* stream);
+
+int qlora_linear_bwd_dropout(const uint16_t* dy, const uint16_t* x,
+                             int64_t M, const nf4_tensor* w,
+                             const uint16_t* A, const uint16_t* B, int32_t r,
+                             float alpha, const float* t_saved, void* dx,
+                             int32_t dx_dtype, float* dA, float* dB,
+                             const qn_dropout* drop, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* qn_strerror -- static text for a QN_* code (host). */
 const char* qn_strerror(int code);

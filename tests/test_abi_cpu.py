@@ -213,3 +213,32 @@ def test_adamw8_validation():
     assert paged(staging=None) == capi.QN_EINVAL
     assert paged(chunk=100) == capi.QN_EINVAL
     assert paged(nbytes=need - 1) == capi.QN_EWORKSPACE
+
+
+def test_dropout_validation():
+    L = capi.lib()
+    p = 0x10000
+    st = _fake_tensor(128, 256)
+
+    def fwd(drop, M=16):
+        return L.qlora_linear_fwd_dropout(p, M, ctypes.byref(st), p, p, 8, 16.0, p,
+                                          capi.QN_F32, p, drop, p, 1 << 40, None)
+
+    def bwd(drop):
+        return L.qlora_linear_bwd_dropout(p, p, 64, ctypes.byref(st), p, p, 8, 16.0,
+                                          p, p, capi.QN_F32, p, p, drop, p, 1 << 40,
+                                          None)
+    for fn in (fwd, bwd):
+        assert fn(None) == capi.QN_EINVAL
+        assert fn(ctypes.byref(capi._Dropout(1.0, 1))) == capi.QN_EINVAL
+        assert fn(ctypes.byref(capi._Dropout(-0.1, 1))) == capi.QN_EINVAL
+        assert fn(ctypes.byref(capi._Dropout(float("nan"), 1))) == capi.QN_EINVAL
+    # a dropout forward takes the general path for every M: its workspace
+    # is at least the general layout's, never the skinny one
+    for M in (1, 8, 16):
+        wd = capi.qlora_workspace_bytes(M, 4096, 4096, 16, capi.QN_FWD_DROPOUT)
+        assert wd > 0
+        assert wd != capi.qlora_workspace_bytes(M, 4096, 4096, 16, capi.QN_FWD)
+    assert (capi.qlora_workspace_bytes(64, 256, 512, 8, capi.QN_FWD_DROPOUT)
+            == capi.qlora_workspace_bytes(64, 256, 512, 8, capi.QN_FWD))
+    assert capi.qlora_workspace_bytes(64, 256, 512, 8, 3) == 0
