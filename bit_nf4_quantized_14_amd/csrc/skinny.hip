@@ -139,6 +139,8 @@ __global__ __launch_bounds__(512) void k_skinny_partial(
         }
       };
       // two register sets, loaded one chunk ahead, no copies between them
+      // (the loop is VALU-bound on the decode; deeper prefetch measured no
+      // faster)
       SkRegs ra0, ra1;
       load(ra0, 0);
       for (int kc = 0; kc < klen; kc += 512) {
@@ -161,19 +163,22 @@ __global__ __launch_bounds__(512) void k_skinny_partial(
 }
 
 // Y[m][n] = sum_slices part[.][m][n] + s * sum_j T[m][j] B[n][j], and
-// T[m][j] = sum_slices part[.][m][Np16 + j] (written to t_save by block 0).
-// One thread per (m, n) output for 64 columns x 16 rows per workgroup; the
+// T[m][j] = sum_slices part[.][m][Np16 + j] (written to t_save by the
+// blocks with blockIdx.x == 0).  Workgroup (bx, by) covers columns
+// [64 bx, 64 bx + 64) of tokens [4 by, 4 by + 4), one output per thread; the
 // slices are summed as four interleaved running sums combined in a fixed
 // order, so the loads of a thread overlap and the result is deterministic.
 __global__ __launch_bounds__(256) void k_skinny_reduce(
     const float* __restrict__ part, int slices, int M, int N, int r, int rpad,
     const uint16_t* __restrict__ B, float s, float* __restrict__ t_save,
     void* __restrict__ Y, int y_bf16) {
-  __shared__ float sT[16 * QN_MAX_RANK];
+  __shared__ float sT[4 * QN_MAX_RANK];
   const int Np16 = (N + 15) & ~15;
   const int64_t rows_total = Np16 + rpad;
-  for (int idx = threadIdx.x; idx < M * r; idx += 256) {
-    const int m = idx / r, j = idx % r;
+  const int mb = 4 * blockIdx.y;
+  const int mrows = min(4, M - mb);
+  for (int idx = threadIdx.x; idx < mrows * r; idx += 256) {
+    const int m = mb + idx / r, j = idx % r;
     float t[4] = {0.f, 0.f, 0.f, 0.f};
     int sl = 0;
     for (; sl + 4 <= slices; sl += 4)
@@ -183,28 +188,25 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
     for (; sl < slices; ++sl) t[0] += part[((int64_t)sl * M + m) * rows_total + Np16 + j];
     const float v = (t[0] + t[1]) + (t[2] + t[3]);
     sT[idx] = v;
-    if (blockIdx.x == 0) t_save[idx] = v;
+    if (blockIdx.x == 0) t_save[(int64_t)m * r + j] = v;
   }
   __syncthreads();
   const int n = blockIdx.x * 64 + (threadIdx.x & 63);
-  if (n >= N) return;
+  const int mi = threadIdx.x >> 6;
+  if (n >= N || mi >= mrows) return;
+  const int m = mb + mi;
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  int sl = 0;
+  for (; sl + 4 <= slices; sl += 4)
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
-    const int m = (threadIdx.x >> 6) + 4 * mm;
-    if (m >= M) break;
-    float y[4] = {0.f, 0.f, 0.f, 0.f};
-    int sl = 0;
-    for (; sl + 4 <= slices; sl += 4)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        y[u] += part[((int64_t)(sl + u) * M + m) * rows_total + n];
-    for (; sl < slices; ++sl) y[0] += part[((int64_t)sl * M + m) * rows_total + n];
-    float lora = 0.f;
-    for (int j = 0; j < r; ++j)
-      lora += sT[m * r + j] * bf16_to_f32(B[(int64_t)n * r + j]);
-    store_out(Y, y_bf16, (int64_t)m * N + n,
-              ((y[0] + y[1]) + (y[2] + y[3])) + s * lora);
-  }
+    for (int u = 0; u < 4; ++u)
+      y[u] += part[((int64_t)(sl + u) * M + m) * rows_total + n];
+  for (; sl < slices; ++sl) y[0] += part[((int64_t)sl * M + m) * rows_total + n];
+  float lora = 0.f;
+  for (int jj = 0; jj < r; ++jj)
+    lora += sT[mi * r + jj] * bf16_to_f32(B[(int64_t)n * r + jj]);
+  store_out(Y, y_bf16, (int64_t)m * N + n,
+            ((y[0] + y[1]) + (y[2] + y[3])) + s * lora);
 }
 
 }  // namespace
@@ -248,7 +250,8 @@ void launch_skinny(hipStream_t st, const uint16_t* x, int M,
                 (int)N, (int)K, r, rpad, P.ks, P.wg_rows, nitems, part,
                 qn::codebook());
   QN_LAUNCH("k_skinny_reduce", k_skinny_reduce,
-            dim3((unsigned)cdiv(N, 64)), dim3(256), st, part, P.slices, M,
+            dim3((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 4)), dim3(256), st,
+            part, P.slices, M,
             (int)N, r, rpad, B, s, t_save, y, y_bf16);
 }
 
