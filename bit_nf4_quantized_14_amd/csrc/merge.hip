@@ -5,17 +5,18 @@
 // Implementation Details (2025 Edition)", Step 7 (Merge & Save).  s = alpha/r
 // as in the linear layer ("QLoRA Implementation Details", Step 4).
 //
-// One workgroup per 64 x 128 tile of W (256 threads):
-//  * each thread owns 32 consecutive weights of one row (half a 64-weight
-//    block): one 16-byte load of packed codes, its block code and group
-//    scale, the block's bf16 LUT and four decode8;
+// One workgroup per 64 x 64 tile of W (256 threads; about 30 KB of LDS, so
+// five workgroups share a CU and their phases overlap):
+//  * each thread owns 16 consecutive weights of one row (a quarter of a
+//    64-weight block): one 8-byte load of packed codes, its block code and
+//    group scale, the block's bf16 LUT and two decode8;
 //  * the rank-r product P = B_tile A_tile runs on v_mfma_f32_32x32x16_bf16:
 //    the A tile (r x 128, zero past r) and the B tile (64 x r) are staged in
 //    LDS, A read column-wise with ds_read_b64_tr_b16 (rows 16 banks apart);
 //  * P goes through LDS into row order, and each thread forms
 //    fma(s, P, W') in fp32 and rounds to bf16 (RNE) into an LDS output
 //    tile, which is written out so that every store instruction covers
-//    whole 256-byte row runs (non-temporal stores).
+//    whole 128-byte row runs (non-temporal stores).
 // HBM-bound: per weight 0.5 + 1/64 + 4/16384 bytes in and 2 bytes out, plus
 // A (L2-resident, shared by every row tile) and B.
 #include "qn_host.h"
@@ -24,7 +25,9 @@ namespace {
 
 using namespace qn;
 
-constexpr int MG_ROWS = 64, MG_COLS = 128, MG_THREADS = 256;
+constexpr int MG_ROWS = 64, MG_COLS = 64, MG_THREADS = 256;
+constexpr int MG_EPT = MG_ROWS * MG_COLS / MG_THREADS;   // weights per thread
+static_assert(MG_EPT == 16, "two packed dwords per thread");
 
 template <int JT>
 struct MgCfg {
@@ -83,25 +86,30 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge(
   const int n0 = blockIdx.x * MG_ROWS, k0 = blockIdx.y * MG_COLS;
   const int64_t numel = (int64_t)N * K;
 
-  // this thread's 32 weights: row n0 + rn, columns k0 + rc .. + 31
-  const int rn = tid >> 2, rc = 32 * (tid & 3);
+  // this thread's 16 weights: row n0 + rn, columns k0 + rc .. + 15
+  const int rn = tid >> 2, rc = MG_EPT * (tid & 3);
   const bool mine = n0 + rn < N && k0 + rc < K;
   const int64_t e = (int64_t)(n0 + rn) * K + k0 + rc;
   const rsrc_t rp = make_rsrc(packed, (uint32_t)((numel + 1) >> 1));
   const rsrc_t rq = make_rsrc(qabs, (uint32_t)((numel + 63) >> 6));
   const rsrc_t rd = make_rsrc(gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
-  const u32x4 wv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 wv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
       rp, mine ? (uint32_t)(e >> 1) : G_OOB, 0, 0));
   const uint32_t qv = __builtin_amdgcn_raw_buffer_load_b8(
       rq, mine ? (uint32_t)(e >> 6) : G_OOB, 0, 0);
   const float dv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
       rd, mine ? (uint32_t)((e >> 14) << 2) : G_OOB, 0, 0));
 
-  // A tile [RP][128]: rows j < r of A [r][K], zero past r and past K
+  // A tile [RP][MG_COLS]: rows j < r of A [r][K], zero past r and past K
   const rsrc_t ra = make_rsrc(A, (uint32_t)((int64_t)r * K * 2));
+  constexpr int ACH = MG_COLS / 8;                  // 16-byte chunks per row
+  static_assert((G::RP * ACH) % MG_THREADS == 0 || G::RP * ACH < MG_THREADS,
+                "A tile loads");
 #pragma unroll
-  for (int i0 = 0; i0 < G::RP * 16; i0 += MG_THREADS) {
-    const int i = i0 + tid, j = i >> 4, c = 8 * (i & 15);
+  for (int i0 = 0; i0 < G::RP * ACH; i0 += MG_THREADS) {
+    const int i = i0 + tid, j = i / ACH, c = 8 * (i % ACH);
+    if (j >= G::RP) break;
     const uint32_t off = (j < r && k0 + c < K)
                              ? (uint32_t)(((int64_t)j * K + k0 + c) * 2) : G_OOB;
     *reinterpret_cast<u32x4*>(sA + j * G::AP + c) = __builtin_bit_cast(
@@ -116,36 +124,29 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge(
   }
   __syncthreads();
 
-  // P = B_tile A_tile: wave (wn, wk) owns rows 32 wn .., columns 64 wk ..
-  f32x16 acc[2];
+  // P = B_tile A_tile: wave (wn, wk) owns rows 32 wn .., columns 32 wk ..
+  f32x16 acc;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 #pragma unroll
   for (int sj = 0; sj < JT; ++sj) {
     const u32x4 a = *reinterpret_cast<const u32x4*>(
         sB + (32 * wn + (lane & 31)) * G::BP + 16 * sj + 8 * (lane >> 5));
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      acc[t] = mfma32(a, mg_read_colT(sA, G::AP, 16 * sj, 64 * wk + 32 * t, lane),
-                      acc[t]);
+    acc = mfma32(a, mg_read_colT(sA, G::AP, 16 * sj, 32 * wk, lane), acc);
   }
-  // acc[t][v] = P[row 32 wn + 8 (v / 4) + 4 (l / 32) + v % 4][col 64 wk + 32 t + l % 32]
+  // acc[v] = P[row 32 wn + 8 (v / 4) + 4 (l / 32) + v % 4][col 32 wk + l % 32]
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      sP[(32 * wn + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * G::PP +
-         64 * wk + 32 * t + (lane & 31)] = acc[t][v];
+  for (int v = 0; v < 16; ++v)
+    sP[(32 * wn + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * G::PP +
+       32 * wk + (lane & 31)] = acc[v];
   __syncthreads();
 
   if (mine) {
     const Lut lut = make_lut(cb, static_cast<float>(qv) * dv);
-    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    const uint32_t wd[2] = {wv.x, wv.y};
     const float* prow = sP + rn * G::PP + rc;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < 2; ++g) {
       const u32x4 wb = decode8(wd[g], lut);    // 8 dequantized bf16 weights
       const uint32_t wp[4] = {wb.x, wb.y, wb.z, wb.w};
       u32x4 res;
@@ -160,12 +161,12 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge(
     }
   }
   __syncthreads();
-  // write-out in store order: each wave instruction covers 4 rows x 256
-  // contiguous bytes (16-byte chunk q of the tile is row q / 16, column
-  // chunk q % 16), non-temporal
+  // write-out in store order: each wave instruction covers 8 rows x 128
+  // contiguous bytes (16-byte chunk q of the tile is row q / ACH, column
+  // chunk q % ACH), non-temporal
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + MG_THREADS * i, row = q >> 4, c = 8 * (q & 15);
+  for (int i = 0; i < MG_ROWS * ACH / MG_THREADS; ++i) {
+    const int q = tid + MG_THREADS * i, row = q / ACH, c = 8 * (q % ACH);
     if (n0 + row < N && k0 + c < K)
       __builtin_nontemporal_store(
           *reinterpret_cast<const u32x4*>(sO + row * G::OP + c),
