@@ -226,6 +226,12 @@ def bench_dequant_quant(reps, copies=3):
                      "kernel": kname, "kernel_ms_per_pass": ksum * 1e3,
                      "kernel_GB/s": nbytes / ksum / 1e9,
                      "frac_hbm_peak": nbytes / ksum / 1e9 / HBM_PEAK_GBS}
+        if name == "dequant7b":
+            # HBM bytes of one whole-layer batched launch (counters)
+            res[name]["traffic"] = measured_traffic("k_dequant<0>")
+        else:
+            t = measured_traffic("k_quantize<0>")
+            res[name]["traffic_per_launch_avg"] = t
         log(f"{name}: {res[name]['GB/s']:.0f} GB/s graph, "
             f"{res[name]['kernel_GB/s']:.0f} GB/s kernel")
     # dequantize-and-merge of the same layer with an r = 16, alpha = 32
@@ -250,7 +256,8 @@ def bench_dequant_quant(reps, copies=3):
                                 f"cycling over {copies} weight copies (> MALL)",
                       "kernel": "k_merge", "kernel_ms_per_pass": ksum * 1e3,
                       "kernel_GB/s": m_bytes / ksum / 1e9,
-                      "frac_hbm_peak": m_bytes / sec / 1e9 / HBM_PEAK_GBS}
+                      "frac_hbm_peak": m_bytes / sec / 1e9 / HBM_PEAK_GBS,
+                      "traffic_per_launch_avg": measured_traffic("k_merge<1>")}
     log(f"merge7b (r=16): {res['merge7b']['GB/s']:.0f} GB/s graph, "
         f"{res['merge7b']['kernel_GB/s']:.0f} GB/s kernel")
     # the same pass as seven separate calls (one launch per projection)
@@ -379,6 +386,7 @@ def bench_adamw(reps, chunk=1 << 24):
            "GB/s": nbytes / sec / 1e9, "kernel": "k_adamw8",
            "kernel_ms": kt, "kernel_GB/s": nbytes / (kt * 1e-3) / 1e9,
            "frac_hbm_peak": nbytes / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "traffic": measured_traffic("k_adamw8"),
            "workload": "r=16 adapters on the 7 projections of 80 layers of "
                        "a 70B-class model, bf16 params, fp32 grads"}
     log(f"adamw8 resident: {sec*1e3:.3f} ms/step, {res['GB/s']:.0f} GB/s "
@@ -477,7 +485,8 @@ def bench_70b(reps, do_train=True):
 # source files that define each kernel (plus the shared device header)
 KERNEL_SOURCES = (("k_gemm", "gemm.hip"), ("k_rank", "rank.hip"),
                   ("k_dequant", "codec.hip"), ("k_quantize", "codec.hip"),
-                  ("k_skinny", "skinny.hip"))
+                  ("k_skinny", "skinny.hip"), ("k_merge", "merge.hip"),
+                  ("k_adamw8", "adamw.hip"))
 
 
 def kernel_source_sha(kernel_key: str):
@@ -677,8 +686,8 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic(
-                         "k_gemm<256, 256, true>" if dom == "k_bwd_dx_gemm"
-                         else "k_gemm<256, 256, false>"),
+                         "k_gemm<256, 256, true, false>" if dom == "k_bwd_dx_gemm"
+                         else "k_gemm<256, 256, false, false>"),
                      "traffic_unit": "HBM bytes per launch",
                      "avg_ms": dom_ms, "flops_per_launch": gemm_flops[dom]},
         "kernels": kernels,
