@@ -203,17 +203,33 @@ __device__ __forceinline__ uint32_t drop_bf16(uint32_t x16, uint32_t w,
 }
 
 // 8 consecutive columns k0 .. k0 + 7 of row m (natural order, two per
-// dword): one generator call per column, word m % 4 of each.
+// dword), where the four lanes of this lane's quad hold rows
+// m - m % 4 .. + 3 of the same columns (m % 4 == lane % 4).  The quad
+// shares the 8 generator calls: lane j = m % 4 computes columns
+// k0 + 2j + t (t = 0, 1), and source lane s sends word s ^ dd of each to
+// lane s ^ dd, so lane j receives word j of column 2 (j ^ dd) + t.
 __device__ __forceinline__ u32x4 drop_row8(const u32x4& a, int m, int k0,
                                            const DropArgs& d) {
   const uint32_t q = static_cast<uint32_t>(m) >> 2;
-  const int sel = m & 3;
+  const int j = m & 3;
+  const u32x4 p0 = philox4x32_10(k0 + 2 * j, q, d.key0, d.key1);
+  const u32x4 p1 = philox4x32_10(k0 + 2 * j + 1, q, d.key0, d.key1);
+  uint32_t recv0[4], recv1[4];   // [dd]: word j of columns 2 (j ^ dd) + 0 / 1
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd) {
+    const uint32_t s0 = pick4(p0, j ^ dd), s1 = pick4(p1, j ^ dd);
+    recv0[dd] = dd == 0 ? s0 : static_cast<uint32_t>(__shfl_xor(static_cast<int>(s0), dd));
+    recv1[dd] = dd == 0 ? s1 : static_cast<uint32_t>(__shfl_xor(static_cast<int>(s1), dd));
+  }
+  u32x4 v0, v1;
+  v0.x = recv0[0]; v0.y = recv0[1]; v0.z = recv0[2]; v0.w = recv0[3];
+  v1.x = recv1[0]; v1.y = recv1[1]; v1.z = recv1[2]; v1.w = recv1[3];
   const uint32_t in[4] = {a.x, a.y, a.z, a.w};
   uint32_t out[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const uint32_t wl = pick4(philox4x32_10(k0 + 2 * h, q, d.key0, d.key1), sel);
-    const uint32_t wh = pick4(philox4x32_10(k0 + 2 * h + 1, q, d.key0, d.key1), sel);
+    // columns 2h and 2h + 1 arrived with dd = h ^ j
+    const uint32_t wl = pick4(v0, h ^ j), wh = pick4(v1, h ^ j);
     out[h] = drop_bf16(in[h], wl, d) | (drop_bf16(in[h] >> 16, wh, d) << 16);
   }
   u32x4 r;
