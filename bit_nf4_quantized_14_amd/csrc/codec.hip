@@ -53,12 +53,44 @@ __device__ __forceinline__ uint32_t const_raw(const void* consts, int64_t b) {
 constexpr int QZ_THREADS = 256;
 constexpr int QZ_PASSES = 8;  // 8 * 256 * 8 = 16384 weights
 
+// Threshold search by buckets.  n = w / absmax lies in [-1, 1]; bucket
+// b = floor(64 n) + 64 (an exact scaling and floor) covers
+// [(b - 64) / 64, (b - 63) / 64).  Every table's thresholds are more than
+// 1/64 apart, so a bucket holds at most one of them: the code (the number
+// of thresholds strictly below n) is base[b], the number below the bucket,
+// plus (n > thr[b]) for the bucket's own threshold (thr = 2, above every n,
+// where there is none).  Built on the host from the fp32 thresholds.
+constexpr int QZ_BUCKETS = 129;
+struct QuantLut {
+  float thr[QZ_BUCKETS];
+  uint8_t base[QZ_BUCKETS];
+};
+
+bool make_quant_lut(const Codebook& cb, QuantLut* out) {
+  for (int b = 0; b < QZ_BUCKETS; ++b) {
+    const double lo = (b - 64) / 64.0, hi = (b - 63) / 64.0;
+    int below = 0, inside = 0;
+    float thr = 2.0f;
+    for (int j = 0; j < 15; ++j) {
+      if (double(cb.T[j]) < lo) ++below;
+      else if (double(cb.T[j]) < hi) { ++inside; thr = cb.T[j]; }
+    }
+    if (inside > 1) return false;
+    out->thr[b] = thr;
+    out->base[b] = static_cast<uint8_t>(below);
+  }
+  return true;
+}
+
 template <int CM>
 __global__ __launch_bounds__(QZ_THREADS) void k_quantize(
     const float* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
     void* __restrict__ consts, float* __restrict__ gscale,
-    float* __restrict__ gmean, int32_t* __restrict__ status, Codebook cb) {
+    float* __restrict__ gmean, int32_t* __restrict__ status, QuantLut lut) {
   __shared__ float s_c[256];
+  __shared__ uint2 s_lut[QZ_BUCKETS];     // (threshold bits, base code)
+  for (int i = threadIdx.x; i < QZ_BUCKETS; i += QZ_THREADS)
+    s_lut[i] = make_uint2(__float_as_uint(lut.thr[i]), lut.base[i]);
   __shared__ float s_wmax[QZ_THREADS / 64];
   __shared__ float s_wsum[QZ_THREADS / 64];
   const int tid = threadIdx.x;
@@ -166,9 +198,11 @@ __global__ __launch_bounds__(QZ_THREADS) void k_quantize(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float n = (c == 0.0f) ? 0.0f : v[it][i] / c;
-      uint32_t code = 0;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) code += (n > cb.T[j]) ? 1u : 0u;
+      // floor(64 n) in [-64, 64]; the clamp (NaN -> -64) only matters for
+      // non-finite weights, which set the status flag
+      const float fb = fminf(fmaxf(floorf(n * 64.0f), -64.0f), 64.0f);
+      const uint2 e = s_lut[static_cast<int>(fb) + 64];
+      const uint32_t code = e.y + (n > __uint_as_float(e.x) ? 1u : 0u);
       word |= code << (4 * i);
     }
     const int64_t byte0 = e0 >> 1;
@@ -287,8 +321,10 @@ int launch_quantize(const float* w, int64_t numel, uint8_t* packed,
   const int64_t nb = cdiv(numel, QN_BLOCK);
   const int64_t ng = cdiv(nb, QN_GROUP);
   if (ng > 0x7FFFFFFFLL) return QN_EINVAL;
+  QuantLut lut;
+  if (!make_quant_lut(cb, &lut)) return QN_EINVAL;   // not for these tables
   QN_LAUNCH("k_quantize", k_quantize<CM>, dim3((unsigned)ng), dim3(QZ_THREADS),
-            st, w, numel, packed, consts, gscale, gmean, status, cb);
+            st, w, numel, packed, consts, gscale, gmean, status, lut);
   return check_launch();
 }
 
