@@ -151,3 +151,35 @@ def test_adamw8_e4m3_rounding_at_ties():
     assert np.array_equal(got.r_codes, ref_st.r_codes)
     _assert_state_equal(got, ref_st)
     assert np.array_equal(bits_host(p), ref_p)
+
+
+def test_adamw8_benchmark_size_sampled_blocks():
+    """The benchmarked buffer: r = 16 adapters of all 7 projections of 80
+    layers of a 70B-class model, 207,093,760 parameters; two steps, 64
+    sampled state blocks of the second checked against the oracle."""
+    n = 80 * 16 * (2 * 8192 + 2 * (1024 + 8192) + 2 * 8192 + 3 * (28672 + 8192))
+    assert n == 207093760
+    rng = np.random.default_rng(530)
+    p0 = torch.from_numpy((rng.standard_normal(n, dtype=np.float32) * 0.01)).to(torch.bfloat16)
+    p = p0.to(DEV)
+    del p0
+    st = capi.AdamW8State.zeros(n)
+    g1 = _grads(rng, n, 1)
+    capi.qn_adamw8_step(p, torch.from_numpy(g1).to(DEV), st, 1, **HP)
+    del g1
+    torch.cuda.synchronize()
+    mid_p, mid_st = bits_host(p), _host_state(st)
+    g2 = _grads(rng, n, 2)
+    capi.qn_adamw8_step(p, torch.from_numpy(g2).to(DEV), st, 2, **HP)
+    torch.cuda.synchronize()
+    out_p, out_st = bits_host(p), _host_state(st)
+    nb = -(-n // 256)
+    blocks = sorted(set(rng.integers(0, nb, 62).tolist()) | {0, nb - 1})
+    for b in blocks:
+        s = slice(256 * b, min(256 * b + 256, n))
+        sub = aw.State8(mid_st.m_codes[s], mid_st.m_scales[b:b + 1],
+                        mid_st.r_codes[s], mid_st.r_scales[b:b + 1])
+        rp, rst = aw.adamw8_step(mid_p[s], g2[s], sub, _oracle_hp(), 2)
+        assert np.array_equal(out_p[s], rp)
+        _assert_state_equal(aw.State8(out_st.m_codes[s], out_st.m_scales[b:b + 1],
+                                      out_st.r_codes[s], out_st.r_scales[b:b + 1]), rst)

@@ -146,3 +146,44 @@ def test_dropout_deterministic_and_seed_dependent():
     for key in ("y", "t", "dx", "da", "db"):
         assert torch.equal(r1[key], r2[key]), key
     assert not torch.equal(r1["t"], r3["t"])
+
+
+def test_gate7b_full_size_with_dropout():
+    """The benchmarked configuration: 7B gate projection, M=4096, r=16,
+    alpha=32, p=0.05, bf16 Y and dX.  Full T, dA, dB and sampled rows of Y
+    and dX against the oracle (the mask over all 4096 x 4096 elements of X)."""
+    from gpu_util import TOL_BF16
+    wk = wl.workload("gate7b")
+    p, seed = 0.05, 0x5EED
+    w = wl.weight(wk, 0)
+    x, a, b = wl.activations(wk, 0), wl.lora_a(wk, 0), wl.lora_b(wk, 0)
+    dy = wl.grad_out(wk, 0)
+    r, alpha, m = wk.r, wk.alpha, wk.m
+    print(f"[dropout] gate7b full size p={p}", flush=True)
+    t, status = quantize_dev(w)
+    X, A, B, DY = bf16_dev(x), bf16_dev(a), bf16_dev(b), bf16_dev(dy)
+    y, ts = capi.qlora_linear_fwd_dropout(X, t, A, B, r, alpha, p, seed,
+                                          y_dtype=capi.QN_BF16)
+    dx, da, db = capi.qlora_linear_bwd_dropout(DY, X, t, A, B, r, alpha, ts, p,
+                                               seed, dx_dtype=capi.QN_BF16)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    W = oracle.bf16_bits_to_f64(_oracle_w(w))
+    Xf, Af, Bf, DYf = (oracle.bf16_bits_to_f64(v) for v in (x, a, b, dy))
+    Xd = oracle.bf16_bits_to_f64(dr.dropout_x_bits(x, p, seed))
+    keep = dr.keep_mask(m, x.shape[1], p, seed)
+    s = alpha / r
+    T = Xd @ Af.T
+    G = DYf @ Bf
+    rows = np.unique(np.concatenate([[0, m - 1],
+                                     np.random.default_rng(3).choice(m, 40, replace=False)]))
+    ms = np.where(keep[rows], float(dr.keep_scale(p)), 0.0)
+    y_ref = Xf[rows] @ W.T + s * (T[rows] @ Bf.T)
+    dx_ref = DYf[rows] @ W + s * (G[rows] @ Af) * ms
+    errs = {"y": rel_err(f64_host(y[rows]), y_ref), "t": rel_err(f64_host(ts), T),
+            "dx": rel_err(f64_host(dx[rows]), dx_ref),
+            "da": rel_err(f64_host(da), s * (G.T @ Xd)),
+            "db": rel_err(f64_host(db), s * (DYf.T @ T))}
+    print(f"[dropout] gate7b rel errors {errs}", flush=True)
+    assert errs["y"] <= TOL_BF16 and errs["dx"] <= TOL_BF16
+    assert errs["t"] <= TOL and errs["da"] <= TOL and errs["db"] <= TOL
