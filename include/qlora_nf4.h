@@ -9,25 +9,32 @@
  *   3. dequantization to bf16,
  *   4. the fused forward Y = X W'^T + (alpha/r) (X A^T) B^T and its backward
  *      (dX through the dequantized frozen base W', dA and dB for the bf16
- *      adapters; the base gets no gradient).
+ *      adapters; the base gets no gradient), optionally with LoRA dropout
+ *      on the adapter input;
+ * and around it: dequantize-and-merge of an adapter into a dense bf16
+ * weight, codec variants (FP4 / INT4 tables, fp32 or centered 8-bit block
+ * constants) for quantization-error comparisons, and an 8-bit AdamW step on
+ * the adapters with its state in device memory or paged through host memory.
  *
  * Sources for what each call computes are the pages "Qlora Expert" (Core
  * Concept), "QLoRA: The 4-bit Revolution" (sections 1 and 2), "QLoRA Guide"
  * (How QLoRA Works: Forward pass; NF4 vs uniform INT4), "QLoRA Implementation
  * Details (2025 Edition)" (Step 1 NF4 Math; Step 4 LoRA adapters) and
  * "QLORA: Efficient Finetuning of Quantized LLMs" (paper summary: Methods,
- * Notes).  The fixed configuration follows the pages' BitsAndBytesConfig:
- * quant type NF4, double quantization on, bf16 compute; and their LoraConfig:
- * rank r, lora_alpha, bias "none", no dropout.
+ * Notes).  The fused calls follow the pages' BitsAndBytesConfig: quant type
+ * NF4, double quantization on, bf16 compute; and their LoraConfig: rank r,
+ * lora_alpha, bias "none", lora_dropout (the *_dropout entry points).  Each
+ * further call cites its own passages.
  *
  * Conventions for every call
  *   - Shapes follow the Linear convention: W is [N, K] (out, in), X [M, K],
  *     Y [M, N], A [r, K], B [N, r].  All matrices are dense row-major.
  *   - bf16 tensors are passed as raw uint16_t bit patterns.
  *   - Pointers marked "device" are device (HBM) addresses; the caller owns
- *     every buffer, including workspaces.  The library never allocates,
- *     frees, or keeps a pointer after a call returns, and holds no global
- *     device state, so calls are reentrant.
+ *     every buffer, including workspaces.  The library never allocates or
+ *     frees memory, keeps no pointer after a call returns, and holds no
+ *     global device state, so calls are reentrant (the paged optimizer step
+ *     creates HIP events for its copies and destroys them before returning).
  *   - All device work is enqueued asynchronously on `stream` (a hipStream_t
  *     passed as void*; NULL is the default stream).  Outputs are valid once
  *     the stream reaches them; inputs must stay unchanged until then.
