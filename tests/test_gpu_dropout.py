@@ -86,6 +86,7 @@ def test_tiny_workload_with_dropout(p):
     (64, 128, 256, 256, 512.0, 0.1),   # maximum rank
     (257, 1024, 576, 16, 32.0, 0.05),  # M past a split
     (1024, 1024, 4096, 16, 32.0, 0.05),  # 256-wide GEMM tiles
+    (2048, 1024, 8448, 16, 32.0, 0.1),   # dX over more than one wave of tiles
 ])
 def test_ragged_shapes_with_dropout(m, n, k, r, alpha, p):
     w, x, a, b, dy = _inputs(m, n, k, r, b_sigma=0.3)

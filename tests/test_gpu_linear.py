@@ -104,6 +104,17 @@ def test_ragged_shapes(m, n, k, r, alpha):
     _compare_full(*_inputs(wk, 0, m=m, n=n, k=k, r=r), alpha=alpha)
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (2048, 8448, 1024),   # forward: 264 output tiles, a ragged second wave
+    (2048, 1024, 8448),   # backward dX: 264 tiles
+])
+def test_more_than_one_wave_of_tiles(m, n, k):
+    """256 x 256 tiles over more than one wave of workgroups (a ragged last
+    wave): full element-wise comparison with the oracle."""
+    wk = wl.workload("tiny")
+    _compare_full(*_inputs(wk, 0, m=m, n=n, k=k, r=16), alpha=32.0)
+
+
 def test_zero_adapter_matches_hipblaslt_on_dequantized_weight():
     """With B = 0 the layer is X W'^T: compare with torch.matmul (hipBLASLt,
     a black-box library) on the GPU-dequantized W'."""
