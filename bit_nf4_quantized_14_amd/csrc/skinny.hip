@@ -30,6 +30,21 @@ constexpr int SK_WAVES = 8;
 constexpr int SK_ROWS = 16 * SK_WAVES;       // rows per workgroup
 constexpr int SK_KS_MAX = 4096;              // longest K slice
 
+// Items [ib, ie) of this workgroup.  The grid is two workgroups per CU;
+// workgroups b and b + gridDim.x / 2 (the same XCD, typically the same CU)
+// split one CU's share of the items, and the CU shares differ by at most
+// one item.
+__device__ __forceinline__ void skinny_items(int nitems, int& ib, int& ie) {
+  const int per = gridDim.x / 2;                 // CU slots
+  const int b = blockIdx.x;
+  const int c = b % per, h = b / per;
+  const int cb = (int)((int64_t)c * nitems / per);
+  const int ce = (int)((int64_t)(c + 1) * nitems / per);
+  const int mid = cb + (ce - cb + 1) / 2;
+  ib = h == 0 ? cb : mid;
+  ie = h == 0 ? mid : ce;
+}
+
 struct SkRegs {
   u32x4 w0, w1;
   uint32_t q;
@@ -58,8 +73,8 @@ __global__ __launch_bounds__(512) void k_skinny_partial(
 
   // work items (block of SK_ROWS rows, K slice), item = slice * wg_rows +
   // row block; this workgroup takes items [ib, ie)
-  const int ipw = (nitems + gridDim.x - 1) / gridDim.x;
-  const int ib = blockIdx.x * ipw, ie = min(nitems, ib + ipw);
+  int ib, ie;
+  skinny_items(nitems, ib, ie);
   for (int c = tid; c < KS / 8; c += 512)
     *reinterpret_cast<u32x4*>(sX + M * XP + 8 * c) = u32x4{0u, 0u, 0u, 0u};
   int staged = -1;                               // slice held in sX
@@ -213,9 +228,13 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
 
 namespace qn {
 
-// Skinny path plan: K slices of ks columns (multiple of 256, <= 2048),
-// enough slices for ~2 workgroups per CU.
+// Skinny path plan: K slices of ks columns (multiple of 256, short enough
+// that the X slice leaves LDS room for two workgroups per CU), and enough
+// slices for ~2 items per workgroup.  The grid is two workgroups per CU
+// whatever the item count; the items are split so that the CUs' shares
+// differ by at most one item (skinny_items).
 constexpr int SK_WGS_PER_CU = 2;     // resident skinny workgroups per CU
+constexpr int SK_CUS = 256;          // MI355X compute units
 constexpr int64_t SK_LDS_PER_WG = 64 * 1024;   // X tile budget (bytes)
 
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
@@ -228,7 +247,7 @@ SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
   int64_t ks_max = (SK_LDS_PER_WG / (2 * (M + 1)) - 8) / 256 * 256;
   ks_max = std::max<int64_t>(256, std::min<int64_t>(ks_max, SK_KS_MAX));
   int64_t slices = std::max<int64_t>(cdiv(K, ks_max),
-                                     cdiv(256 * SK_WGS_PER_CU * 2, P.wg_rows));
+                                     cdiv((int64_t)SK_CUS * SK_WGS_PER_CU * 2, P.wg_rows));
   slices = std::min<int64_t>(slices, kchunks);
   const int64_t ks = cdiv(kchunks, slices) * 256;
   P.ks = (int)ks;
@@ -245,7 +264,7 @@ void launch_skinny(hipStream_t st, const uint16_t* x, int M,
   const int nitems = P.wg_rows * P.slices;
   const size_t shm = size_t(M + 1) * (P.ks + 8) * 2;
   QN_LAUNCH_SHM("k_skinny_partial", k_skinny_partial,
-                dim3((unsigned)std::min(nitems, 256 * SK_WGS_PER_CU)),
+                dim3((unsigned)(SK_CUS * SK_WGS_PER_CU)),
                 dim3(512), shm, st, x, M, w->packed, w->qabs, w->gscale, A,
                 (int)N, (int)K, r, rpad, P.ks, P.wg_rows, nitems, part,
                 qn::codebook());
