@@ -177,12 +177,26 @@ __global__ __launch_bounds__(512) void k_skinny_partial(
   }
 }
 
+// Sum over the K slices of one partial-sum element, slice order fixed; the
+// loads of eight slices are issued before they are added.
+__device__ __forceinline__ float sum_slices(const float* __restrict__ p,
+                                            int64_t stride, int slices) {
+  float acc = 0.f;
+  for (int sl = 0; sl < slices; sl += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = sl + u < slices ? p[(int64_t)(sl + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  return acc;
+}
+
 // Y[m][n] = sum_slices part[.][m][n] + s * sum_j T[m][j] B[n][j], and
 // T[m][j] = sum_slices part[.][m][Np16 + j] (written to t_save by the
 // blocks with blockIdx.x == 0).  Workgroup (bx, by) covers columns
-// [64 bx, 64 bx + 64) of tokens [4 by, 4 by + 4), one output per thread; the
-// slices are summed as four interleaved running sums combined in a fixed
-// order, so the loads of a thread overlap and the result is deterministic.
+// [64 bx, 64 bx + 64) of tokens [4 by, 4 by + 4), one output per thread.
 __global__ __launch_bounds__(256) void k_skinny_reduce(
     const float* __restrict__ part, int slices, int M, int N, int r, int rpad,
     const uint16_t* __restrict__ B, float s, float* __restrict__ t_save,
@@ -190,18 +204,12 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
   __shared__ float sT[4 * QN_MAX_RANK];
   const int Np16 = (N + 15) & ~15;
   const int64_t rows_total = Np16 + rpad;
+  const int64_t stride = (int64_t)M * rows_total;      // between slices
   const int mb = 4 * blockIdx.y;
   const int mrows = min(4, M - mb);
   for (int idx = threadIdx.x; idx < mrows * r; idx += 256) {
     const int m = mb + idx / r, j = idx % r;
-    float t[4] = {0.f, 0.f, 0.f, 0.f};
-    int sl = 0;
-    for (; sl + 4 <= slices; sl += 4)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        t[u] += part[((int64_t)(sl + u) * M + m) * rows_total + Np16 + j];
-    for (; sl < slices; ++sl) t[0] += part[((int64_t)sl * M + m) * rows_total + Np16 + j];
-    const float v = (t[0] + t[1]) + (t[2] + t[3]);
+    const float v = sum_slices(part + (int64_t)m * rows_total + Np16 + j, stride, slices);
     sT[idx] = v;
     if (blockIdx.x == 0) t_save[(int64_t)m * r + j] = v;
   }
@@ -210,18 +218,25 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
   const int mi = threadIdx.x >> 6;
   if (n >= N || mi >= mrows) return;
   const int m = mb + mi;
-  float y[4] = {0.f, 0.f, 0.f, 0.f};
-  int sl = 0;
-  for (; sl + 4 <= slices; sl += 4)
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      y[u] += part[((int64_t)(sl + u) * M + m) * rows_total + n];
-  for (; sl < slices; ++sl) y[0] += part[((int64_t)sl * M + m) * rows_total + n];
+  const float y = sum_slices(part + (int64_t)m * rows_total + n, stride, slices);
+  const float* t = sT + mi * r;
+  const uint16_t* b = B + (int64_t)n * r;
   float lora = 0.f;
-  for (int jj = 0; jj < r; ++jj)
-    lora += sT[mi * r + jj] * bf16_to_f32(B[(int64_t)n * r + jj]);
-  store_out(Y, y_bf16, (int64_t)m * N + n,
-            ((y[0] + y[1]) + (y[2] + y[3])) + s * lora);
+  if ((r & 7) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0) {
+    // 16-byte aligned rows of B: 8 weights per load
+    for (int j0 = 0; j0 < r; j0 += 8) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(b + j0);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        lora += t[j0 + 2 * h] * __uint_as_float(ww[h] << 16);
+        lora += t[j0 + 2 * h + 1] * __uint_as_float(ww[h] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    for (int jj = 0; jj < r; ++jj) lora += t[jj] * bf16_to_f32(b[jj]);
+  }
+  store_out(Y, y_bf16, (int64_t)m * N + n, y + s * lora);
 }
 
 }  // namespace
