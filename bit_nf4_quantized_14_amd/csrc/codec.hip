@@ -193,11 +193,13 @@ __global__ __launch_bounds__(QZ_THREADS) void k_quantize(
   for (int it = 0; it < QZ_PASSES; ++it) {
     const int64_t e0 = gbase + it * (QZ_THREADS * 8) + tid * 8;
     if (e0 >= numel) break;
-    const float c = cmine[it];
+    // an all-zero block (c = 0) holds only +-0, and +-0 / 1 = +-0 gets the
+    // code of n = 0: dividing by 1 there keeps the divides branch-free
+    const float c = cmine[it] == 0.0f ? 1.0f : cmine[it];
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float n = (c == 0.0f) ? 0.0f : v[it][i] / c;
+      const float n = v[it][i] / c;
       // floor(64 n) in [-64, 64]; the clamp (NaN -> -64) only matters for
       // non-finite weights, which set the status flag
       const float fb = fminf(fmaxf(floorf(n * 64.0f), -64.0f), 64.0f);
