@@ -384,6 +384,21 @@ __global__ __launch_bounds__(256) void k_rank_stream(
 //  pad:  dst[row dw + col] = col < valid ? src[row rs + col cs] : 0.
 // ---------------------------------------------------------------------------
 
+// sum_{k < nb} src[k stride], added in k order, eight loads in flight
+// before they are added.
+__device__ __forceinline__ float finish_sum(const float* __restrict__ src,
+                                            int64_t stride, int nb) {
+  float v = 0.0f;
+  for (int k0 = 0; k0 < nb; k0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = k0 + u < nb ? src[(k0 + u) * stride] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += t[u];
+  }
+  return v;
+}
+
 __device__ __forceinline__ void finish_pad(const FinishPad& p, int64_t idx) {
   if (idx >= (int64_t)p.rows * p.dw) return;
   const int64_t row = idx / p.dw, col = idx % p.dw;
@@ -400,8 +415,7 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
     const int m = (int)(idx / p.rpad), j = (int)(idx % p.rpad);
     float v = 0.0f;
     if (m < p.M && j < p.jvalid)
-      for (int k = 0; k < p.nb; ++k)
-        v += p.src[k * p.bstride + (int64_t)m * p.ld + j];
+      v = finish_sum(p.src + (int64_t)m * p.ld + j, p.bstride, p.nb);
     uint16_t h, l;
     split_bf16(p.scale * v, h, l);
     if (m < p.M) {
@@ -423,9 +437,7 @@ __global__ __launch_bounds__(256) void k_rank_finish(FinishArgs a) {
     const int64_t idx = (int64_t)b * 256 + tid;
     if (idx >= (int64_t)p.C * p.r) return;
     const int64_t c = idx / p.r, j = idx % p.r;
-    float v = 0.0f;
-    for (int k = 0; k < p.nb; ++k)
-      v += p.src[((int64_t)k * p.C + c) * p.rpad + j];
+    const float v = finish_sum(p.src + c * p.rpad + j, (int64_t)p.C * p.rpad, p.nb);
     p.out[c * p.sc + j * p.sj] = v;
     return;
   }
