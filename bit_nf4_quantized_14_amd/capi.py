@@ -70,7 +70,13 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load the HIP library once; raise if it has not been built."""
+    """Load the HIP library once; raise if it has not been built.
+
+    torch is imported first: PyTorch ships its own HIP runtime, and the
+    library's dependency on the HIP runtime must resolve to that one (which
+    owns the streams and memory the calls receive).  Loaded before torch,
+    the library would bind the system runtime, and its launches on torch's
+    streams would fail."""
     global _lib
     if _lib is not None:
         return _lib
@@ -78,6 +84,7 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(
             f"{LIB_PATH} is not built; run `python -m "
             "bit_nf4_quantized_14_amd.build` (hipcc, gfx950)")
+    import torch  # noqa: F401  (binds torch's HIP runtime first)
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     sp = ctypes.POINTER(_NF4Struct)
