@@ -87,6 +87,7 @@ def test_tiny_workload_with_dropout(p):
     (257, 1024, 576, 16, 32.0, 0.05),  # M past a split
     (1024, 1024, 4096, 16, 32.0, 0.05),  # 256-wide GEMM tiles
     (2048, 1024, 8448, 16, 32.0, 0.1),   # dX over more than one wave of tiles
+    (2050, 1032, 8256, 16, 32.0, 0.1),   # dX on 256 x 256 tiles, ragged edges
 ])
 def test_ragged_shapes_with_dropout(m, n, k, r, alpha, p):
     w, x, a, b, dy = _inputs(m, n, k, r, b_sigma=0.3)

@@ -107,10 +107,16 @@ def test_ragged_shapes(m, n, k, r, alpha):
 @pytest.mark.parametrize("m,n,k", [
     (2048, 8448, 1024),   # forward: 264 output tiles, a ragged second wave
     (2048, 1024, 8448),   # backward dX: 264 tiles
+    # 256 x 256 tiles with ragged edges: forward M and N ragged and an odd
+    # number of 64-wide steps (17); backward M and K ragged and a partial
+    # last step (N = 1032)
+    (2050, 8200, 1088),
+    (2050, 1032, 8256),
 ])
 def test_more_than_one_wave_of_tiles(m, n, k):
     """256 x 256 tiles over more than one wave of workgroups (a ragged last
-    wave): full element-wise comparison with the oracle."""
+    wave), and with ragged tile edges: full element-wise comparison with
+    the oracle."""
     wk = wl.workload("tiny")
     _compare_full(*_inputs(wk, 0, m=m, n=n, k=k, r=16), alpha=32.0)
 
