@@ -37,8 +37,8 @@ using namespace qn;
 // LDS is double-buffered.  While the MFMAs consume step i, the A tile of
 // step i+1 streams into the other buffer and the weight tile of step i+1
 // (loaded one step earlier) is dequantized into it; the dequantization is
-// woven between the MFMAs in fenced groups (one MFMA, then up to six VALU
-// ops).  Global loads go through buffer resources whose range check returns
+// woven between the MFMAs in fenced groups (one MFMA, the next slice's
+// fragment read, then up to four VALU ops).  Global loads go through buffer resources whose range check returns
 // zeros, which covers ragged M, N and K tiles without branches.
 // The adapter term is 2r extra reduction steps with the A side s*T (or s*G)
 // split into bf16 hi + lo parts, so the fp32 intermediate keeps ~16
@@ -228,12 +228,16 @@ __device__ __forceinline__ void gemm_frags(const char* sA, const uint16_t* sW,
 }
 
 // VALU instructions placed after each MFMA by the interleaving below.
-constexpr int G_VALU_PER_MFMA = 6;
+constexpr int G_VALU_PER_MFMA = 4;
 
 // The four k16 slices of one step with the dequantization of the next weight
 // tile woven in: one decode8 (28 VALU ops and a 16-byte LDS write) after
 // every MPD MFMAs, each group fenced and ordered MFMA / VALU so the VALU
-// work issues in the shadow of the MFMAs instead of after them.
+// work issues in the shadow of the MFMAs instead of after them.  The next
+// slice's fragment reads are pinned one behind each of the first MFMAs, so
+// they issue early instead of just before the MFMAs that consume them
+// (forward -1.5% per launch; the register allocator otherwise sinks them
+// to reuse the current fragments' registers).
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_mma_deq(
     const char* sA, const uint16_t* sW, uint16_t* sWn, const WRegs& R,
@@ -265,6 +269,8 @@ __device__ __forceinline__ void gemm_mma_deq(
 #pragma unroll
         for (int h = 0; h < MPD; ++h) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          if (kk < 3 && h < (BWD ? C::TM + 2 * C::TN : C::TM + C::TN))
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
           __builtin_amdgcn_sched_group_barrier(0x002, G_VALU_PER_MFMA, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
