@@ -74,6 +74,26 @@ __device__ __forceinline__ int bwd_swz(int r, int c) {
   return BN == 256 ? 4 * (r & 3) + 2 * (r & 1) + ((c >> 4) & 1) : 5 * (r & 3);
 }
 
+// Eight weights as stored in the LDS tile.  Forward rows run along the
+// reduction, so the order must match the A operand: natural order.  The
+// backward tile's rows run along the output columns, so its 16-byte chunks
+// hold their eight columns in decode8p order (0 2 4 6 1 3 5 7), four
+// v_perm_b32 cheaper; gemm_col maps an MFMA output column back.
+template <bool BWD>
+__device__ __forceinline__ u32x4 gemm_decode(uint32_t p, const Lut& t) {
+  return BWD ? decode8p(p, t) : decode8(p, t);
+}
+
+// Output column of accumulator column (lane % 32) of MFMA tile j.  In the
+// backward, position q of each group of eight holds column
+// 2 (q % 4) + q / 4.
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ int gemm_col(int c0, int wn, int j, int lane) {
+  const int q = lane & 31;
+  const int base = c0 + wn * GemmCfg<BM, BN, BWD>::WN + j * 32;
+  return BWD ? base + (q & ~7) + ((q & 3) << 1) + ((q >> 2) & 1) : base + q;
+}
+
 // Packed weight bytes of one step for one thread (32 weights), plus its
 // block code and group scale (raw; c' = q * d is formed when the tile is
 // dequantized).
@@ -130,7 +150,7 @@ __device__ __forceinline__ void gemm_dequant_w(const WRegs& R, uint16_t* sW,
   const uint32_t wd[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
 #pragma unroll
   for (int d = 0; d < 4; ++d)
-    *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = decode8(wd[d], t);
+    *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = gemm_decode<BWD>(wd[d], t);
 }
 
 // A tile of one step: 16-byte global loads into registers (thread t takes
@@ -270,7 +290,7 @@ __device__ __forceinline__ void gemm_mma_deq(
       acc[i][j] = mfma32(a[kk & 1][i], b[kk & 1][j], acc[i][j]);
       if (g % MPD == MPD - 1) {
         const int d = kk * DPK + g / MPD;
-        *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = decode8(wd[d], t);
+        *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = gemm_decode<BWD>(wd[d], t);
 #pragma unroll
         for (int h = 0; h < MPD; ++h) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -344,7 +364,7 @@ __device__ __forceinline__ void gemm_adapter(
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
       const uint32_t off =
-          (uint32_t)(((int64_t)(c0 + wn * C::WN + j * 32 + (lane & 31)) * rpad + jc) * 2);
+          (uint32_t)(((int64_t)gemm_col<BM, BN, BWD>(c0, wn, j, lane) * rpad + jc) * 2);
       b[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
     }
 #pragma unroll
@@ -370,7 +390,7 @@ __device__ __forceinline__ void gemm_drop_acc(
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
-      const int col = c0 + wn * C::WN + j * 32 + (lane & 31);
+      const int col = gemm_col<BM, BN, BWD>(c0, wn, j, lane);
 #pragma unroll
       for (int vg = 0; vg < 4; ++vg) {
         const int r0 = m0 + wm * C::WM + i * 32 + 8 * vg + 4 * (lane >> 5);
@@ -466,7 +486,7 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * C::WM + i * 32 + 8 * (v >> 2) +
                         4 * (lane >> 5) + (v & 3);
-        const int col = c0 + wn * C::WN + j * 32 + (lane & 31);
+        const int col = gemm_col<BM, BN, BWD>(c0, wn, j, lane);
         if (row < M && col < NOUT)
           store_out(out, out_bf16, (int64_t)row * NOUT + col, acc[i][j][v]);
       }
