@@ -690,8 +690,8 @@ def main():
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic(
-                         "k_gemm<256, 256, true, false>" if dom == "k_bwd_dx_gemm"
-                         else "k_gemm<256, 256, false, false>"),
+                         "k_gemm<256, 256, true, false, false>" if dom == "k_bwd_dx_gemm"
+                         else "k_gemm<256, 256, false, false, false>"),
                      "traffic_unit": "HBM bytes per launch",
                      "avg_ms": dom_ms, "flops_per_launch": gemm_flops[dom]},
         "kernels": kernels,

@@ -310,13 +310,74 @@ __device__ __forceinline__ void gemm_mma_deq(
 // hardware deals workgroups round-robin over 8 XCDs) works on a contiguous
 // run of tiles, and runs walk the N direction first: a run shares A rows in
 // that XCD's L2.
-__device__ __forceinline__ void gemm_tile_of(int tiles_m, int tiles_n,
+__device__ __forceinline__ void gemm_tile_of(int pid, int total, int tiles_n,
                                              int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  int pid = blockIdx.x;
   if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
   tm = pid / tiles_n;
   tn = pid % tiles_n;
+}
+
+// Kernel-side view of a GemmSplit: workgroups [0, whole) take whole tiles,
+// [whole, whole + rem) the first piece of split tile b - whole (reduction
+// steps [ks, end)), [whole + rem, whole + 2 rem) its second piece ([0, ks)).
+struct SplitArgs {
+  int whole, rem, ks;
+  float* part;       // [rem][TM TN 4][NT] float4: one partial tile each
+  uint32_t* cnt;     // [rem][2]: arrivals, partial-ready flag
+};
+
+// The partial moves through device-coherent (sc1) buffer accesses, the
+// counters through relaxed agent-scope atomics, so the two pieces may run
+// on different XCDs (their L2 caches are not coherent with each other).
+// (Keeping the partial in one XCD's L2, with the pieces placed there,
+// measured the same.)
+constexpr int G_SC1 = 16;
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_put_partial(
+    rsrc_t rp, int tid,
+    const f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = (i * C::TN + j) * 4 + q;
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp,
+                                               (uint32_t)((u * C::NT + tid) * 16), 0,
+                                               G_SC1);
+      }
+}
+
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ void gemm_add_partial(
+    rsrc_t rp, int tid,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
+  using C = GemmCfg<BM, BN, BWD>;
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = (i * C::TN + j) * 4 + q;
+        const f32x4 v = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rp, (uint32_t)((u * C::NT + tid) * 16), 0, G_SC1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+        if (q == 3) {
+          // the sums are formed here, one accumulator tile at a time, not
+          // sunk into the epilogue's conditional stores (where the loaded
+          // values would stay live and spill)
+          asm volatile("" : "+v"(acc[i][j]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
 }
 
 // One reduction step: MFMAs on (sAc, sWc) while the next A tile streams into
@@ -407,13 +468,16 @@ __device__ __forceinline__ void gemm_drop_acc(
     }
 }
 
-template <int BM, int BN, bool BWD, bool DROP>
+// SPLIT: the grid holds split pieces (SplitArgs); without it the kernel
+// has none of their code.
+template <int BM, int BN, bool BWD, bool DROP, bool SPLIT>
 __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
     const uint16_t* __restrict__ Aop, const uint8_t* __restrict__ packed,
     const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
     const uint16_t* __restrict__ La_hi, const uint16_t* __restrict__ La_lo,
     const uint16_t* __restrict__ Lb, int M, int N, int K, int rpad,
-    void* __restrict__ out, int out_bf16, Codebook cb, DropArgs dp) {
+    void* __restrict__ out, int out_bf16, Codebook cb, DropArgs dp,
+    SplitArgs sp) {
   using C = GemmCfg<BM, BN, BWD>;
   // Four distinct LDS buffers so that the compiler can see that the tiles
   // being filled never alias the tiles being read.
@@ -426,8 +490,21 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  int tm, tn;
-  gemm_tile_of((M + BM - 1) / BM, (NOUT + BN - 1) / BN, tm, tn);
+  const int tiles_n = (NOUT + BN - 1) / BN;
+  const int nsteps = (KRED + G_BK - 1) / G_BK;
+  int tm, tn, s0 = 0, s1 = nsteps, split = -1;
+  if (!SPLIT || (int)blockIdx.x < sp.whole) {
+    gemm_tile_of(blockIdx.x, SPLIT ? sp.whole : ((M + BM - 1) / BM) * tiles_n,
+                 tiles_n, tm, tn);
+  } else {
+    const int q = blockIdx.x - sp.whole;
+    const bool first = q < sp.rem;
+    split = first ? q : q - sp.rem;
+    tm = (sp.whole + split) / tiles_n;
+    tn = (sp.whole + split) % tiles_n;
+    s0 = first ? sp.ks : 0;
+    s1 = first ? nsteps : sp.ks;
+  }
   const int m0 = tm * BM, c0 = tn * BN;
 
   const int64_t numel = (int64_t)N * K;
@@ -454,29 +531,86 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
 
   // Steps past the end read out of range: their tiles are zeros (a zero
   // block constant dequantizes every code to zero), so the loop runs whole
-  // pairs of steps without branches.
-  const int nsteps = (KRED + G_BK - 1) / G_BK;
-  WRegs Wc;
-  {
-    ARegs<BM, BN, BWD> A0;
-    gemm_load_a<BM, BN, BWD>(A0, ra, M, KRED, m0, 0, tid);
-    gemm_store_a<BM, BN, BWD>(A0, sA0, tid);
-  }
-  gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, 0, tid);
-  gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);
-  gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, G_BK, tid);
-  __builtin_amdgcn_s_waitcnt(0);   // all counters: loads landed in LDS/regs
-  __syncthreads();
-  for (int st = 0; st < nsteps; st += 2) {
-    gemm_step<BM, BN, BWD>(st, sA0, sW0, sA1, sW1, Wc, ra, rp, rq, rd, M, N, K,
-                           KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
-    gemm_step<BM, BN, BWD>(st + 1, sA1, sW1, sA0, sW0, Wc, ra, rp, rq, rd, M, N,
-                           K, KRED, m0, c0, wave, wm, wn, tid, lane, cb, acc);
-  }
+  // pairs of steps without branches.  A small piece covers an even number
+  // of steps, so only a range that ends at the last step can run over.
+  // reduction steps [R0, R1) into acc
+#define GEMM_MAINLOOP(R0, R1)                                                  \
+  do {                                                                         \
+    const int r0_ = (R0), r1_ = (R1);                                          \
+    WRegs Wc;                                                                  \
+    {                                                                          \
+      ARegs<BM, BN, BWD> A0;                                                   \
+      gemm_load_a<BM, BN, BWD>(A0, ra, M, KRED, m0, r0_ * G_BK, tid);          \
+      gemm_store_a<BM, BN, BWD>(A0, sA0, tid);                                 \
+    }                                                                          \
+    gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, r0_ * G_BK, tid);       \
+    gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);                             \
+    gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, (r0_ + 1) * G_BK, tid); \
+    __builtin_amdgcn_s_waitcnt(0); /* loads landed in LDS and registers */     \
+    __syncthreads();                                                           \
+    for (int st = r0_; st < r1_; st += 2) {                                    \
+      gemm_step<BM, BN, BWD>(st, sA0, sW0, sA1, sW1, Wc, ra, rp, rq, rd, M, N, \
+                             K, KRED, m0, c0, wave, wm, wn, tid, lane, cb,     \
+                             acc);                                             \
+      gemm_step<BM, BN, BWD>(st + 1, sA1, sW1, sA0, sW0, Wc, ra, rp, rq, rd,   \
+                             M, N, K, KRED, m0, c0, wave, wm, wn, tid, lane,   \
+                             cb, acc);                                         \
+    }                                                                          \
+  } while (0)
+  GEMM_MAINLOOP(s0, s1);
+#undef GEMM_MAINLOOP
 
+  // With SPLIT, the adapter term and the partial sum of a split tile's other
+  // piece are added by code that every tile runs, with zero-sized buffer
+  // ranges (reads return zeros, no memory traffic) where they do not apply:
+  // with one path for acc the accumulators stay in registers.  The adapter
+  // goes with the piece that starts at step 0.
   if constexpr (!DROP)
-    gemm_adapter<BM, BN, BWD>(La_hi, La_lo, Lb, M, NOUT, rpad, m0, c0, wm, wn,
-                              lane, acc);
+    gemm_adapter<BM, BN, BWD>(La_hi, La_lo, Lb,
+                              (!SPLIT || split < 0 || s0 == 0) ? M : 0, NOUT,
+                              rpad, m0, c0, wm, wn, lane, acc);
+
+  if constexpr (SPLIT) {
+  rsrc_t rpart = make_rsrc(sp.part, 0u);
+  if (split >= 0) {
+    // The first piece of a split tile to get here leaves its partial and
+    // exits; the second adds it and finishes the tile.
+    __shared__ uint32_t s_arrived;
+    uint32_t* cnt = sp.cnt + 2 * split;
+    rpart = make_rsrc(sp.part + (int64_t)split * BM * BN,
+                      (uint32_t)(BM * BN * 4));
+    if (tid == 0)
+      s_arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_arrived == 0) {
+      gemm_put_partial<BM, BN, BWD>(rpart, tid, acc);
+      __builtin_amdgcn_s_waitcnt(0);   // the partial's stores are complete
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // The other piece is past its arrival and only has stores left, so this
+    // wait is short; the bound only guards against a hang.
+    if (tid == 0) {
+      for (int it = 0; it < (1 << 24) &&
+                       __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == 0u;
+           ++it)
+        __builtin_amdgcn_s_sleep(2);
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+  gemm_add_partial<BM, BN, BWD>(rpart, tid, acc);
+  // Keep those loads out of the stores below: a wait for a load would also
+  // wait for every store issued before it (one counter, in order).
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);
+  }
 
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -498,50 +632,108 @@ namespace qn {
 
 // Fused GEMM launch: 256 x 256 tiles when they give at least ~one
 // workgroup per CU, otherwise 128 x 128.
+constexpr int G_CUS = 256;   // MI355X compute units, one 256 x 256 tile each
+
+bool gemm_big_tiles(int64_t M, int64_t nout) {
+  return cdiv(M, 256) * cdiv(nout, 256) >= 192;
+}
+
+// Split of the ragged last wave: with R <= G_CUS / 2 tiles left, each of
+// them becomes two pieces over half the reduction each, 2 R workgroups that
+// all run at once.  With more tiles left the split does not pay: a wave
+// that leaves CUs idle runs its tiles at a higher clock (the package is
+// power-limited), and splitting 174-176 of 256 into a 3/4 and a 1/4 piece
+// measured 3-5% slower than leaving them whole, against 6-13% faster for
+// halves of 2-90 tiles.  No split with dropout either (its adapter term is
+// masked before the main loop).
+GemmSplit gemm_split_plan(int64_t M, int64_t nout, int64_t kred, bool drop) {
+  GemmSplit sp{0, 0, 0};
+  if (drop || !gemm_big_tiles(M, nout)) return sp;
+  const int64_t tiles = cdiv(M, 256) * cdiv(nout, 256);
+  const int64_t rem = tiles % G_CUS;
+  if (rem == 0 || 2 * rem > G_CUS) return sp;
+  const int64_t nsteps = cdiv(kred, G_BK);
+  const int64_t ks = (nsteps / 2) & ~int64_t(1);
+  if (ks < 2 || nsteps - ks < 2) return sp;
+  sp.whole = (int)(tiles - rem);
+  sp.rem = (int)rem;
+  sp.ks = (int)ks;
+  return sp;
+}
+
+size_t gemm_split_counters(const GemmSplit& sp) {
+  return size_t(sp.rem) * 256 * 256 * 4;
+}
+
+size_t gemm_split_bytes(const GemmSplit& sp) {
+  return sp.rem == 0 ? 0 : gemm_split_counters(sp) + size_t(sp.rem) * 8;
+}
+
 template <int BM, int BN, bool BWD>
 void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                    const uint16_t* La_hi, const uint16_t* La_lo,
                    const uint16_t* Lb, int M, int rpad, void* out,
-                   int out_bf16, const DropArgs* drop) {
+                   int out_bf16, const DropArgs* drop, const SplitArgs& sp) {
   const int N = (int)w->rows, K = (int)w->cols;
   const int nout = BWD ? K : N;
   const unsigned tiles = (unsigned)(cdiv(M, BM) * cdiv(nout, BN));
+  const unsigned grid = sp.rem == 0 ? tiles : (unsigned)(sp.whole + 2 * sp.rem);
   if constexpr (BWD) {
     if (drop != nullptr) {
-      QN_LAUNCH("k_bwd_dx_gemm", (k_gemm<BM, BN, BWD, true>), dim3(tiles),
+      QN_LAUNCH("k_bwd_dx_gemm", (k_gemm<BM, BN, BWD, true, false>), dim3(grid),
                 dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
                 w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
-                qn::codebook(), *drop);
+                qn::codebook(), *drop, sp);
       return;
     }
   }
   const DropArgs none{};
-  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD, false>),
-            dim3(tiles), dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs, w->gscale,
-            La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16, qn::codebook(), none);
+  if (sp.rem > 0) {
+    if constexpr (BM == 256) {
+      QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm",
+                (k_gemm<BM, BN, BWD, false, true>), dim3(grid),
+                dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
+                w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
+                qn::codebook(), none, sp);
+      return;
+    }
+  }
+  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD, false, false>),
+            dim3(grid), dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed,
+            w->qabs, w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
+            qn::codebook(), none, sp);
 }
 
 template <bool BWD>
 void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  const uint16_t* La_hi, const uint16_t* La_lo,
                  const uint16_t* Lb, int M, int rpad, void* out,
-                 int out_bf16, const DropArgs* drop) {
+                 int out_bf16, const DropArgs* drop, void* split_ws) {
   const int64_t nout = BWD ? w->cols : w->rows;
-  if (cdiv(M, 256) * cdiv(nout, 256) >= 192)
+  const int64_t kred = BWD ? w->rows : w->cols;
+  SplitArgs sa{0, 0, 0, nullptr, nullptr};
+  if (split_ws != nullptr) {
+    const GemmSplit sp = gemm_split_plan(M, nout, kred, drop != nullptr);
+    if (sp.rem > 0)
+      sa = SplitArgs{sp.whole, sp.rem, sp.ks, static_cast<float*>(split_ws),
+                     reinterpret_cast<uint32_t*>(static_cast<char*>(split_ws) +
+                                                 gemm_split_counters(sp))};
+  }
+  if (gemm_big_tiles(M, nout))
     launch_gemm_t<256, 256, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
-                                 out_bf16, drop);
+                                 out_bf16, drop, sa);
   else
     launch_gemm_t<128, 128, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
-                                 out_bf16, drop);
+                                 out_bf16, drop, sa);
 }
 
 template void launch_gemm<false>(hipStream_t, const uint16_t*, const nf4_tensor*,
                                  const uint16_t*, const uint16_t*,
                                  const uint16_t*, int, int, void*, int,
-                                 const DropArgs*);
+                                 const DropArgs*, void*);
 template void launch_gemm<true>(hipStream_t, const uint16_t*, const nf4_tensor*,
                                 const uint16_t*, const uint16_t*,
                                 const uint16_t*, int, int, void*, int,
-                                const DropArgs*);
+                                const DropArgs*, void*);
 
 }  // namespace qn

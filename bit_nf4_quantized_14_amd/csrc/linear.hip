@@ -37,6 +37,14 @@ bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
   return true;
 }
 
+// A pad job with no valid columns that zeroes the split GEMM's counters
+// (2 words per split tile) before the GEMM runs.
+void zero_split_counters(FinishPad& p, char* split_ws, const GemmSplit& sp) {
+  if (sp.rem == 0) return;
+  uint16_t* c = reinterpret_cast<uint16_t*>(split_ws + gemm_split_counters(sp));
+  p = FinishPad{c, c, 1, 4 * sp.rem, 0, 0, 0};
+}
+
 FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
                                   int32_t r, bool general) {
   FwdWorkspace L{};
@@ -59,6 +67,8 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
   off += align256(size_t(N) * L.rpad * 2);
   L.prow = off;
   off += align256(size_t(P.nb) * M * L.rpad * 4);
+  L.split = off;
+  off += align256(gemm_split_bytes(gemm_split_plan(M, N, K, false)));
   L.total = off;
   return L;
 }
@@ -93,6 +103,8 @@ BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K,
   off += align256(size_t(Pg.nb) * M * L.rpad * 4);
   L.pcol = off;
   off += align256(pcol * L.rpad * 4);
+  L.split = off;
+  off += align256(gemm_split_bytes(gemm_split_plan(M, K, N, false)));
   L.total = off;
   return L;
 }
@@ -207,9 +219,11 @@ int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   fa.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, P.nb, Mi, Mi, (int)r,
                     L.rpad, s, t_save, Th, Tl, nullptr, nullptr};
   fa.P1 = FinishPad{B, Bp, Ni, L.rpad, (int)r, (int64_t)r, (int64_t)1};
+  char* split_ws = ws_at<char>(ws, L.split);
+  zero_split_counters(fa.P2, split_ws, gemm_split_plan(M, N, K, false));
   launch_finish(st, fa);
   launch_gemm<false>(st, x, w, Th, Tl, Bp, Mi, L.rpad, y,
-                     (int)(y_dtype == QN_BF16));
+                     (int)(y_dtype == QN_BF16), nullptr, split_ws);
   return check_launch();
 }
 
@@ -264,10 +278,13 @@ int linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
   f1.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, Pg.nb, Mi, Mp, (int)r,
                     L.rpad, s, nullptr, Gh, Gl, UGh, UGl};
   f1.Cc = FinishCols{pcol, Pg.mb, Ni, (int)r, L.rpad, dB, (int64_t)r, 1};
+  char* split_ws = ws_at<char>(ws, L.split);
+  zero_split_counters(f1.P1, split_ws, gemm_split_plan(M, K, N, use_drop));
   launch_finish(st, f1);
   // dX = dY W' + (s G) A
   launch_gemm<true>(st, dy, w, Gh, Gl, Atp, Mi, L.rpad, dx,
-                    (int)(dx_dtype == QN_BF16), use_drop ? &da : nullptr);
+                    (int)(dx_dtype == QN_BF16), use_drop ? &da : nullptr,
+                    split_ws);
   // dA = (s G)^T X: row-block partials of out[k][j] -> dA[j][k]
   const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
   launch_rank_stream<RS_COLS>(st, "k_rank_stream_da", Pa, x, Mi, Ki, nullptr,

@@ -98,11 +98,28 @@ T* ws_at(void* ws, size_t off) {
 // dX = dY W' + s G A), 256 x 256 or 128 x 128 tiles by size.
 // drop (backward only): the adapter term s G A is multiplied elementwise by
 // the dropout mask / (1 - p) before dY W' is added; nullptr for none.
+//
+// Ragged last wave: when the 256 x 256 tiles leave a last wave that fills
+// only part of the GPU, each of its tiles is computed as two pieces over
+// disjoint reduction ranges, a big one and a small one, sized so that the
+// pieces fill the CUs about evenly (GemmSplit; no split with dropout).  The
+// first piece to finish leaves its fp32 partial tile in `split_part`, the
+// second adds it and stores the tile.  split_part holds rem * 256 * 256
+// floats, split_cnt 2 * rem words that must be zero at launch (the second
+// piece of each tile sets them back to zero).
+struct GemmSplit {
+  int whole, rem, ks;   // whole tiles, split tiles, reduction steps of the
+                        // small piece (the big one takes the rest)
+};
+GemmSplit gemm_split_plan(int64_t M, int64_t nout, int64_t kred, bool drop);
+size_t gemm_split_bytes(const GemmSplit& sp);   // partials + counters
+size_t gemm_split_counters(const GemmSplit& sp); // byte offset of the counters
+
 template <bool BWD>
 void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  const uint16_t* La_hi, const uint16_t* La_lo,
                  const uint16_t* Lb, int M, int rpad, void* out, int out_bf16,
-                 const DropArgs* drop = nullptr);
+                 const DropArgs* drop = nullptr, void* split_ws = nullptr);
 
 // ---- rank.hip: rank-r side products and their reductions.
 enum { RS_ROWS = 1, RS_COLS = 2 };

@@ -24,6 +24,7 @@ struct FwdWorkspace {
   size_t bp;        // bf16 [N, rpad]  B zero-padded           (GEMM path)
   size_t prow;      // fp32 [nb, M, rpad] column-block partials of T
   size_t part;      // fp32 [slices, 16, rows] K-slice partials (skinny path)
+  size_t split;     // partial tiles + counters of the GEMM's split last wave
   int32_t slices, ks;
   size_t total;
   int32_t rpad;
@@ -37,6 +38,7 @@ struct BwdWorkspace {
   size_t ugh, ugl;  // bf16 [r, Mp]    hi/lo parts of s*G, transposed
   size_t prow;      // fp32 [nb, M, rpad] column-block partials of G
   size_t pcol;      // fp32 [mb, max(N, K), rpad] row-block partials of dB, dA
+  size_t split;     // partial tiles + counters of the dX GEMM's split last wave
   size_t total;
   int64_t mp;       // M rounded up to a multiple of 8
   int32_t rpad;

@@ -344,8 +344,11 @@ size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
  * y      : device [M, N] of y_dtype (QN_F32 or QN_BF16);
  * t_save : device fp32 [M, r], T for the backward;
  * ws     : device workspace of ws_bytes >= qlora_workspace_bytes(M, N, K,
- *          r, QN_FWD), 16-byte aligned (holds the bf16 hi/lo parts of s T
- *          and B padded to a multiple of 16 columns).
+ *          r, QN_FWD), 16-byte aligned (holds the bf16 hi/lo parts of s T,
+ *          B padded to a multiple of 16 columns and, when the GEMM's last
+ *          wave of 256 x 256 output tiles is ragged, one fp32 partial tile
+ *          per tile of that wave); calls that run at the same time need
+ *          workspaces of their own.
  * Requires K % 64 == 0 (blocks never straddle rows), N % 8 == 0 (16-byte
  * aligned rows), M, N >= 1, every operand smaller than 2 GiB, and all
  * matrix pointers 16-byte aligned.
