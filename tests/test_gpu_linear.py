@@ -143,6 +143,20 @@ def test_linear_deterministic():
         assert torch.equal(r1[key], r2[key]), key
 
 
+@pytest.mark.parametrize("m,n,k", [(2048, 8448, 1024), (2050, 1032, 8256)])
+def test_split_last_wave_repeatable(m, n, k):
+    """Shapes whose last wave of 256 x 256 tiles is split into two
+    reduction halves per tile (forward: 264 tiles; backward: 297 tiles):
+    three calls in a row give bit-identical results, whichever half of a
+    tile finishes first and with the counters the halves leave behind."""
+    wk = wl.workload("tiny")
+    w, x, a, b, dy, r = _inputs(wk, 0, m=m, n=n, k=k, r=16)
+    runs = [_run(w, x, a, b, dy, r, 32.0) for _ in range(3)]
+    for res in runs[1:]:
+        for key in ("y", "t", "dx", "da", "db"):
+            assert torch.equal(runs[0][key], res[key]), key
+
+
 def _sampled_rows_check(w, x, a, b, dy, r, alpha, res, rows, out_dtype):
     """Reference for sampled rows of Y and dX, full T, dA and dB."""
     n, k = w.shape
@@ -181,10 +195,11 @@ def test_gate7b_full_size(out_dtype):
     _sampled_rows_check(w, x, a, b, dy, r, wk.alpha, res, rows, out_dtype)
 
 
-@pytest.mark.parametrize("proj", [1, 6])
+@pytest.mark.parametrize("proj", [1, 4, 6])
 def test_layer70b_projection_full_size(proj):
-    """70B-layer projections k (1024x8192) and down (8192x28672) at M=2048,
-    r=64, alpha=16."""
+    """70B-layer projections k (1024x8192), gate (28672x8192; its forward
+    GEMM splits the last 128 of 896 tiles) and down (8192x28672; its dX GEMM
+    splits) at M=2048, r=64, alpha=16."""
     wk = wl.workload("layer70b")
     w, x, a, b, dy, r = _inputs(wk, proj)
     res = _run(w, x, a, b, dy, r, wk.alpha, capi.QN_F32)
