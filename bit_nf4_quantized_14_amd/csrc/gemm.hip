@@ -612,12 +612,13 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
   __builtin_amdgcn_sched_barrier(0);
   }
 
-  // bf16 output: one 32-bit offset per accumulator tile (OOB for a column
-  // past the edge), the row step as a scalar offset, and rows past M beyond
-  // the buffer's range, so each element is one convert and one store.  Used
-  // while every offset of the tile stays below 2^31.
-  if (out_bf16 && ((int64_t)m0 + BM) * NOUT * 2 < (int64_t(1) << 31)) {
-    const rsrc_t ro = make_rsrc(out, (uint32_t)((int64_t)M * NOUT * 2));
+  // One 32-bit offset per accumulator tile (out of range for a column past
+  // the edge), the row step as a scalar offset, and rows past M beyond the
+  // buffer's range, so each element is one store (and one convert for
+  // bf16).  Used while every offset of the tile stays below 2^31.
+  const int es = out_bf16 ? 2 : 4;
+  if (((int64_t)m0 + BM) * NOUT * es < (int64_t(1) << 31)) {
+    const rsrc_t ro = make_rsrc(out, (uint32_t)((int64_t)M * NOUT * es));
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -625,13 +626,19 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
         const int row0 = m0 + wm * C::WM + i * 32 + 4 * (lane >> 5);
         const int col = gemm_col<BM, BN, BWD>(c0, wn, j, lane);
         const uint32_t vo =
-            col < NOUT ? (uint32_t)(row0 * NOUT + col) * 2u : G_OOB;
+            col < NOUT ? (uint32_t)(row0 * NOUT + col) * (uint32_t)es : G_OOB;
+        if (out_bf16) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int dr = 8 * (v >> 2) + (v & 3);
-          __builtin_amdgcn_raw_buffer_store_b16(
-              static_cast<uint16_t>(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu),
-              ro, vo, dr * NOUT * 2, 0);
+          for (int v = 0; v < 16; ++v)
+            __builtin_amdgcn_raw_buffer_store_b16(
+                static_cast<uint16_t>(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu),
+                ro, vo, (8 * (v >> 2) + (v & 3)) * NOUT * 2, 0);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(acc[i][j][v]), ro, vo,
+                (8 * (v >> 2) + (v & 3)) * NOUT * 4, 0);
         }
       }
     return;
