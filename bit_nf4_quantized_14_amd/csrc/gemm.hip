@@ -571,45 +571,45 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
                               rpad, m0, c0, wm, wn, lane, acc);
 
   if constexpr (SPLIT) {
-  rsrc_t rpart = make_rsrc(sp.part, 0u);
-  if (split >= 0) {
-    // The first piece of a split tile to get here leaves its partial and
-    // exits; the second adds it and finishes the tile.
-    __shared__ uint32_t s_arrived;
-    uint32_t* cnt = sp.cnt + 2 * split;
-    rpart = make_rsrc(sp.part + (int64_t)split * BM * BN,
-                      (uint32_t)(BM * BN * 4));
-    if (tid == 0)
-      s_arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (s_arrived == 0) {
-      gemm_put_partial<BM, BN, BWD>(rpart, tid, acc);
-      __builtin_amdgcn_s_waitcnt(0);   // the partial's stores are complete
-      __syncthreads();
+    rsrc_t rpart = make_rsrc(sp.part, 0u);
+    if (split >= 0) {
+      // The first piece of a split tile to get here leaves its partial and
+      // exits; the second adds it and finishes the tile.
+      __shared__ uint32_t s_arrived;
+      uint32_t* cnt = sp.cnt + 2 * split;
+      rpart = make_rsrc(sp.part + (int64_t)split * BM * BN,
+                        (uint32_t)(BM * BN * 4));
       if (tid == 0)
-        __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      return;
+        s_arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_arrived == 0) {
+        gemm_put_partial<BM, BN, BWD>(rpart, tid, acc);
+        __builtin_amdgcn_s_waitcnt(0);   // the partial's stores are complete
+        __syncthreads();
+        if (tid == 0)
+          __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+      // The other piece is past its arrival and only has stores left, so this
+      // wait is short; the bound only guards against a hang.
+      if (tid == 0) {
+        for (int it = 0; it < (1 << 24) &&
+                         __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == 0u;
+             ++it)
+          __builtin_amdgcn_s_sleep(2);
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
     }
-    // The other piece is past its arrival and only has stores left, so this
-    // wait is short; the bound only guards against a hang.
-    if (tid == 0) {
-      for (int it = 0; it < (1 << 24) &&
-                       __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == 0u;
-           ++it)
-        __builtin_amdgcn_s_sleep(2);
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-  }
-  gemm_add_partial<BM, BN, BWD>(rpart, tid, acc);
-  // Keep those loads out of the stores below: a wait for a load would also
-  // wait for every store issued before it (one counter, in order).
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_sched_barrier(0);
+    gemm_add_partial<BM, BN, BWD>(rpart, tid, acc);
+    // Keep those loads out of the stores below: a wait for a load would also
+    // wait for every store issued before it (one counter, in order).
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // One 32-bit offset per accumulator tile (out of range for a column past
