@@ -63,8 +63,9 @@ def test_codec_degenerate_blocks():
         np.full(64, 7.5, np.float32),                           # constant block
         np.full(64, -1e-30, np.float32),                        # tiny
         (np.arange(64, dtype=np.float32) - 31.5) * np.float32(1e3),  # large
+        (np.arange(64, dtype=np.float32) - 31.5) * np.float32(1e-40),  # subnormal
     ]
-    w = np.concatenate(parts + [np.zeros(64 * 249, np.float32)])  # one group
+    w = np.concatenate(parts + [np.zeros(64 * 248, np.float32)])  # one group
     w = np.concatenate([w, np.zeros(GROUP_ELEMS, np.float32)])   # + zero group
     _check_full(w.reshape(2, -1))
 
