@@ -373,7 +373,9 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
  * t_saved: device fp32 [M, r] from qlora_linear_fwd;
  * dx     : device [M, K] of dx_dtype;  dA, dB: device fp32 outputs;
  * ws     : device workspace, ws_bytes >= qlora_workspace_bytes(M, N, K, r,
- *          QN_BWD).
+ *          QN_BWD) (the transposed and padded adapter operands, the rank-r
+ *          partial sums and, when the dX GEMM's last wave of 256 x 256 tiles
+ *          is ragged, one fp32 partial tile per tile of that wave).
  * Same shape and alignment rules as qlora_linear_fwd.
  * Errors: QN_EINVAL, QN_EWORKSPACE, QN_EHIP.
  */
