@@ -218,11 +218,14 @@ int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   FinishArgs fa = finish_args();
   fa.R = FinishRows{prow, (int64_t)M * L.rpad, L.rpad, P.nb, Mi, Mi, (int)r,
                     L.rpad, s, t_save, Th, Tl, nullptr, nullptr};
-  fa.P1 = FinishPad{B, Bp, Ni, L.rpad, (int)r, (int64_t)r, (int64_t)1};
+  // B already has rpad columns and 16-byte rows: the GEMM reads it as is
+  const bool b_as_is = r == L.rpad && aligned16(B);
+  if (!b_as_is)
+    fa.P1 = FinishPad{B, Bp, Ni, L.rpad, (int)r, (int64_t)r, (int64_t)1};
   char* split_ws = ws_at<char>(ws, L.split);
   zero_split_counters(fa.P2, split_ws, gemm_split_plan(M, N, K, false));
   launch_finish(st, fa);
-  launch_gemm<false>(st, x, w, Th, Tl, Bp, Mi, L.rpad, y,
+  launch_gemm<false>(st, x, w, Th, Tl, b_as_is ? B : Bp, Mi, L.rpad, y,
                      (int)(y_dtype == QN_BF16), nullptr, split_ws);
   return check_launch();
 }
