@@ -44,7 +44,6 @@ using namespace qn;
 // split into bf16 hi + lo parts, so the fp32 intermediate keeps ~16
 // mantissa bits.
 // ---------------------------------------------------------------------------
-constexpr int G_BK = 64;
 
 template <int BM, int BN, bool BWD>
 struct GemmCfg {
@@ -324,14 +323,18 @@ struct SplitArgs {
   int whole, rem, ks;
   float* part;       // [rem][TM TN 4][NT] float4: one partial tile each
   uint32_t* cnt;     // [rem][2]: arrivals, partial-ready flag
+  int32_t* status;   // QN_ESYNC when a partial never became ready
 };
 
-// The partial moves through device-coherent (sc1) buffer accesses, the
-// counters through relaxed agent-scope atomics, so the two pieces may run
-// on different XCDs (their L2 caches are not coherent with each other).
-// (Keeping the partial in one XCD's L2, with the pieces placed there,
-// measured the same.)
-constexpr int G_SC1 = 16;
+// Exchange of a split tile's partial (AMDGPU memory model, agent scope, so
+// the two pieces may run on different XCDs): the piece that arrives first
+// stores its partial with ordinary stores, meets its workgroup barrier and
+// sets the ready flag with a release store (L2 write-back before the flag);
+// the second piece polls the flag with relaxed loads, then an acquire fence
+// (L2 and L1 invalidate) orders its ordinary loads of the partial after it.
+// The poll is bounded: if the flag never rises the tile is written as NaN
+// and the status word reports QN_ESYNC instead of adding an unready partial.
+constexpr int G_SPLIT_SPIN = 1 << 22;    // polls of ~2 x 64 cycles each
 
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_put_partial(
@@ -349,7 +352,7 @@ __device__ __forceinline__ void gemm_put_partial(
                          acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp,
                                                (uint32_t)((u * C::NT + tid) * 16), 0,
-                                               G_SC1);
+                                               0);
       }
 }
 
@@ -367,7 +370,7 @@ __device__ __forceinline__ void gemm_add_partial(
         const int u = (i * C::TN + j) * 4 + q;
         const f32x4 v = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rp, (uint32_t)((u * C::NT + tid) * 16), 0, G_SC1));
+                       rp, (uint32_t)((u * C::NT + tid) * 16), 0, 0));
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
         if (q == 3) {
@@ -575,7 +578,7 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
     if (split >= 0) {
       // The first piece of a split tile to get here leaves its partial and
       // exits; the second adds it and finishes the tile.
-      __shared__ uint32_t s_arrived;
+      __shared__ uint32_t s_arrived, s_ready;
       uint32_t* cnt = sp.cnt + 2 * split;
       rpart = make_rsrc(sp.part + (int64_t)split * BM * BN,
                         (uint32_t)(BM * BN * 4));
@@ -585,25 +588,41 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
       __syncthreads();
       if (s_arrived == 0) {
         gemm_put_partial<BM, BN, BWD>(rpart, tid, acc);
-        __builtin_amdgcn_s_waitcnt(0);   // the partial's stores are complete
-        __syncthreads();
+        __syncthreads();   // every wave's stores precede the release below
         if (tid == 0)
-          __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELAXED,
+          __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELEASE,
                              __HIP_MEMORY_SCOPE_AGENT);
         return;
       }
       // The other piece is past its arrival and only has stores left, so this
       // wait is short; the bound only guards against a hang.
       if (tid == 0) {
-        for (int it = 0; it < (1 << 24) &&
-                         __hip_atomic_load(cnt + 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) == 0u;
-             ++it)
+        int it = 0;
+        while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) == 0u &&
+               ++it < G_SPLIT_SPIN)
           __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_ready = it < G_SPLIT_SPIN;
+        if (it >= G_SPLIT_SPIN)
+          __hip_atomic_store(sp.status, (int32_t)QN_ESYNC, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        // back to zero for the next launch (a kernel boundary orders these
+        // stores before it)
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
+      if (s_ready == 0) {
+        // an unready partial is never added: the tile becomes NaN
+        rpart = make_rsrc(sp.part, 0u);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
+      }
     }
     gemm_add_partial<BM, BN, BWD>(rpart, tid, acc);
     // Keep those loads out of the stores below: a wait for a load would also
@@ -613,12 +632,16 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
   }
 
   // One 32-bit offset per accumulator tile (out of range for a column past
-  // the edge), the row step as a scalar offset, and rows past M beyond the
-  // buffer's range, so each element is one store (and one convert for
-  // bf16).  Used while every offset of the tile stays below 2^31.
+  // the edge), so each element is one store (and one convert for bf16).
+  // Used while every offset of the tile stays below 2^31.  A tile whose
+  // rows all lie below M puts the row step in the scalar offset; the range
+  // check covers only the vector offset (plus the instruction offset), so
+  // the last row tile of a ragged M adds the row step to the vector offset
+  // instead and its rows past M land beyond the buffer's range.
   const int es = out_bf16 ? 2 : 4;
   if (((int64_t)m0 + BM) * NOUT * es < (int64_t(1) << 31)) {
     const rsrc_t ro = make_rsrc(out, (uint32_t)((int64_t)M * NOUT * es));
+    const bool rows_full = m0 + BM <= M;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -627,18 +650,33 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
         const int col = gemm_col<BM, BN, BWD>(c0, wn, j, lane);
         const uint32_t vo =
             col < NOUT ? (uint32_t)(row0 * NOUT + col) * (uint32_t)es : G_OOB;
-        if (out_bf16) {
+        if (rows_full) {
+          if (out_bf16) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            __builtin_amdgcn_raw_buffer_store_b16(
-                static_cast<uint16_t>(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu),
-                ro, vo, (8 * (v >> 2) + (v & 3)) * NOUT * 2, 0);
+            for (int v = 0; v < 16; ++v)
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  static_cast<uint16_t>(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu),
+                  ro, vo, (8 * (v >> 2) + (v & 3)) * NOUT * 2, 0);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __float_as_uint(acc[i][j][v]), ro, vo,
+                  (8 * (v >> 2) + (v & 3)) * NOUT * 4, 0);
+          }
         } else {
+          // vo + step stays below 2^32: step < (m0 + BM) * NOUT * es < 2^31
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            __builtin_amdgcn_raw_buffer_store_b32(
-                __float_as_uint(acc[i][j][v]), ro, vo,
-                (8 * (v >> 2) + (v & 3)) * NOUT * 4, 0);
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t o = vo + (uint32_t)((8 * (v >> 2) + (v & 3)) * NOUT * es);
+            if (out_bf16)
+              __builtin_amdgcn_raw_buffer_store_b16(
+                  static_cast<uint16_t>(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu),
+                  ro, o, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]),
+                                                    ro, o, 0, 0);
+          }
         }
       }
     return;
@@ -660,45 +698,6 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
 }  // namespace
 
 namespace qn {
-
-// Fused GEMM launch: 256 x 256 tiles when they give at least ~one
-// workgroup per CU, otherwise 128 x 128.
-constexpr int G_CUS = 256;   // MI355X compute units, one 256 x 256 tile each
-
-bool gemm_big_tiles(int64_t M, int64_t nout) {
-  return cdiv(M, 256) * cdiv(nout, 256) >= 192;
-}
-
-// Split of the ragged last wave: with R <= G_CUS / 2 tiles left, each of
-// them becomes two pieces over half the reduction each, 2 R workgroups that
-// all run at once.  With more tiles left the split does not pay: a wave
-// that leaves CUs idle runs its tiles at a higher clock (the package is
-// power-limited), and splitting 174-176 of 256 into a 3/4 and a 1/4 piece
-// measured 3-5% slower than leaving them whole, against 6-13% faster for
-// halves of 2-90 tiles.  No split with dropout either (its adapter term is
-// masked before the main loop).
-GemmSplit gemm_split_plan(int64_t M, int64_t nout, int64_t kred, bool drop) {
-  GemmSplit sp{0, 0, 0};
-  if (drop || !gemm_big_tiles(M, nout)) return sp;
-  const int64_t tiles = cdiv(M, 256) * cdiv(nout, 256);
-  const int64_t rem = tiles % G_CUS;
-  if (rem == 0 || 2 * rem > G_CUS) return sp;
-  const int64_t nsteps = cdiv(kred, G_BK);
-  const int64_t ks = (nsteps / 2) & ~int64_t(1);
-  if (ks < 2 || nsteps - ks < 2) return sp;
-  sp.whole = (int)(tiles - rem);
-  sp.rem = (int)rem;
-  sp.ks = (int)ks;
-  return sp;
-}
-
-size_t gemm_split_counters(const GemmSplit& sp) {
-  return size_t(sp.rem) * 256 * 256 * 4;
-}
-
-size_t gemm_split_bytes(const GemmSplit& sp) {
-  return sp.rem == 0 ? 0 : gemm_split_counters(sp) + size_t(sp.rem) * 8;
-}
 
 template <int BM, int BN, bool BWD>
 void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
@@ -742,13 +741,15 @@ void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  int out_bf16, const DropArgs* drop, void* split_ws) {
   const int64_t nout = BWD ? w->cols : w->rows;
   const int64_t kred = BWD ? w->rows : w->cols;
-  SplitArgs sa{0, 0, 0, nullptr, nullptr};
+  SplitArgs sa{0, 0, 0, nullptr, nullptr, nullptr};
   if (split_ws != nullptr) {
     const GemmSplit sp = gemm_split_plan(M, nout, kred, drop != nullptr);
+    char* base = static_cast<char*>(split_ws);
     if (sp.rem > 0)
-      sa = SplitArgs{sp.whole, sp.rem, sp.ks, static_cast<float*>(split_ws),
-                     reinterpret_cast<uint32_t*>(static_cast<char*>(split_ws) +
-                                                 gemm_split_counters(sp))};
+      sa = SplitArgs{sp.whole, sp.rem, sp.ks,
+                     reinterpret_cast<float*>(base + gemm_split_part_offset(sp)),
+                     reinterpret_cast<uint32_t*>(base + G_SPLIT_HDR),
+                     reinterpret_cast<int32_t*>(base)};
   }
   if (gemm_big_tiles(M, nout))
     launch_gemm_t<256, 256, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
