@@ -10,7 +10,9 @@
 
 namespace qn {
 
+#ifdef QN_PROFILE_HOOK
 ProfileHook g_prof;
+#endif
 
 const Codebook& codebook() {
   static const Codebook cb = [] {
@@ -21,92 +23,12 @@ const Codebook& codebook() {
   return cb;
 }
 
-bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r) {
-  if (!valid_tensor(w) || M <= 0) return false;
-  if (r < 1 || r > QN_MAX_RANK) return false;
-  const int64_t N = w->rows, K = w->cols;
-  if (K % QN_BLOCK != 0 || N % 8 != 0) return false;
-  // 32-bit index arithmetic inside the GEMM kernels
-  if (M > (1LL << 30) || N > (1LL << 30) || K > (1LL << 30)) return false;
-  // buffer-resource ranges are 32-bit byte counts (offsets past 2^31 mean
-  // "out of range"): every operand read through one stays below 2 GiB
-  const int64_t lim = 1LL << 31;
-  if (M * K * 2 >= lim || M * N * 2 >= lim || N * K / 2 >= lim) return false;
-  // fp32 rank-r partial rows [N or K][rpad] addressed through a resource
-  if (std::max(N, K) * 4 * 16 * rank_tiles(r) >= lim) return false;
-  return true;
-}
-
-// A pad job with no valid columns that zeroes the split GEMM's counters
-// (2 words per split tile) before the GEMM runs.
+// A pad job with no valid columns that zeroes the status word and the split
+// GEMM's counters (the split area's first G_SPLIT_HDR + 8 rem bytes) before
+// the GEMM runs.
 void zero_split_counters(FinishPad& p, char* split_ws, const GemmSplit& sp) {
-  if (sp.rem == 0) return;
-  uint16_t* c = reinterpret_cast<uint16_t*>(split_ws + gemm_split_counters(sp));
-  p = FinishPad{c, c, 1, 4 * sp.rem, 0, 0, 0};
-}
-
-FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
-                                  int32_t r, bool general) {
-  FwdWorkspace L{};
-  L.rpad = 16 * rank_tiles(r);
-  if (M <= qn::QN_SKINNY_M && !general) {
-    const SkinnyPlan P = skinny_plan(M, N, K, r);
-    L.slices = P.slices;
-    L.ks = P.ks;
-    L.part = 0;
-    L.total = align256(size_t(P.slices) * M * P.rows_total * 4);
-    return L;
-  }
-  const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r));
-  size_t off = 0;
-  L.th = off;
-  off += align256(size_t(M) * L.rpad * 2);
-  L.tl = off;
-  off += align256(size_t(M) * L.rpad * 2);
-  L.bp = off;
-  off += align256(size_t(N) * L.rpad * 2);
-  L.prow = off;
-  off += align256(size_t(P.nb) * M * L.rpad * 4);
-  L.split = off;
-  off += align256(gemm_split_bytes(gemm_split_plan(M, N, K, false)));
-  L.total = off;
-  return L;
-}
-
-BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K,
-                                  int32_t r) {
-  BwdWorkspace L{};
-  const int jt = rank_tiles(r);
-  L.rpad = 16 * jt;
-  L.mp = cdiv(M, 8) * 8;
-  const StreamPlan Pg = stream_plan(RS_ROWS | RS_COLS, M, N, jt);
-  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
-  const size_t pcol = std::max(size_t(Pg.mb) * N, size_t(Pa.mb) * K);
-  size_t off = 0;
-  L.bt = off;
-  off += align256(size_t(r) * N * 2);
-  L.uth = off;
-  off += align256(size_t(r) * L.mp * 2);
-  L.utl = off;
-  off += align256(size_t(r) * L.mp * 2);
-  L.atp = off;
-  off += align256(size_t(K) * L.rpad * 2);
-  L.gh = off;
-  off += align256(size_t(M) * L.rpad * 2);
-  L.gl = off;
-  off += align256(size_t(M) * L.rpad * 2);
-  L.ugh = off;
-  off += align256(size_t(r) * L.mp * 2);
-  L.ugl = off;
-  off += align256(size_t(r) * L.mp * 2);
-  L.prow = off;
-  off += align256(size_t(Pg.nb) * M * L.rpad * 4);
-  L.pcol = off;
-  off += align256(pcol * L.rpad * 4);
-  L.split = off;
-  off += align256(gemm_split_bytes(gemm_split_plan(M, K, N, false)));
-  L.total = off;
-  return L;
+  uint16_t* c = reinterpret_cast<uint16_t*>(split_ws);
+  p = FinishPad{c, c, 1, (int)(G_SPLIT_HDR / 2) + 4 * sp.rem, 0, 0, 0};
 }
 
 }  // namespace qn
@@ -117,6 +39,7 @@ extern "C" {
 
 int qn_profile_kernel(const char* name, void** ev_start, void** ev_stop,
                       int32_t capacity) {
+#ifdef QN_PROFILE_HOOK
   const int32_t recorded = g_prof.count;
   if (name == nullptr) {
     g_prof = ProfileHook();
@@ -131,6 +54,13 @@ int qn_profile_kernel(const char* name, void** ev_start, void** ev_stop,
   g_prof.ev_stop = ev_stop;
   g_prof.capacity = capacity;
   return recorded;
+#else
+  (void)name;
+  (void)ev_start;
+  (void)ev_stop;
+  (void)capacity;
+  return QN_EINVAL;   // the default build has no hook
+#endif
 }
 
 const char* qn_strerror(int code) {
@@ -140,6 +70,7 @@ const char* qn_strerror(int code) {
     case QN_EWORKSPACE: return "workspace too small";
     case QN_EHIP: return "HIP launch error";
     case QN_ENONFINITE: return "non-finite weight";
+    case QN_ESYNC: return "split tile partial never became ready";
     default: return "unknown error";
   }
 }

@@ -18,35 +18,17 @@ namespace qn {
 // Codebook kernel argument (host-derived once, codebook.cpp).
 const Codebook& codebook();
 
-inline bool aligned16(const void* p) {
-  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
-}
 
 inline int check_launch() {
   return hipGetLastError() == hipSuccess ? QN_OK : QN_EHIP;
 }
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-inline bool valid_tensor(const nf4_tensor* w) {
-  return w != nullptr && w->packed != nullptr && w->qabs != nullptr &&
-         w->gscale != nullptr && w->rows > 0 && w->cols > 0 &&
-         aligned16(w->packed);
-}
-
-// Rank-tile dispatch: JT = number of 16-wide tiles of r, rounded up to a
-// power of two (1, 2, 4, 8, 16 covers r <= 256); rpad = 16 JT.
-inline int rank_tiles(int r) {
-  int jt = 1;
-  while (jt * 16 < r) jt *= 2;
-  return jt;
-}
-
-bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r);
-
-// Per-launch event recording for one named kernel (qn_profile_kernel).
+// Kernel launch.  The library built with QN_PROFILE_HOOK (the profiling
+// variant, libqlora_nf4_prof.so) can record HIP events around the launches
+// of one named kernel (qn_profile_kernel); the default build has no such
+// state and launches directly.
+#ifdef QN_PROFILE_HOOK
 struct ProfileHook {
   char name[64] = {0};
   void** ev_start = nullptr;
@@ -76,9 +58,12 @@ struct ProfScope {
     ProfScope qn_prof_scope_(kname, st);                              \
     hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);    \
   } while (0)
+#else
+#define QN_LAUNCH_SHM(kname, kernel, grid, block, shm, st, ...) \
+  hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__)
+#endif
 #define QN_LAUNCH(kname, kernel, grid, block, st, ...) \
   QN_LAUNCH_SHM(kname, kernel, grid, block, 0, st, __VA_ARGS__)
-
 
 #define QN_RANK_DISPATCH(r, CALL)                \
   switch (qn::rank_tiles(r)) {                   \
@@ -99,22 +84,6 @@ T* ws_at(void* ws, size_t off) {
 // drop (backward only): the adapter term s G A is multiplied elementwise by
 // the dropout mask / (1 - p) before dY W' is added; nullptr for none.
 //
-// Ragged last wave: when the 256 x 256 tiles leave a last wave that fills
-// only part of the GPU, each of its tiles is computed as two pieces over
-// disjoint reduction ranges, a big one and a small one, sized so that the
-// pieces fill the CUs about evenly (GemmSplit; no split with dropout).  The
-// first piece to finish leaves its fp32 partial tile in `split_part`, the
-// second adds it and stores the tile.  split_part holds rem * 256 * 256
-// floats, split_cnt 2 * rem words that must be zero at launch (the second
-// piece of each tile sets them back to zero).
-struct GemmSplit {
-  int whole, rem, ks;   // whole tiles, split tiles, reduction steps of the
-                        // small piece (the big one takes the rest)
-};
-GemmSplit gemm_split_plan(int64_t M, int64_t nout, int64_t kred, bool drop);
-size_t gemm_split_bytes(const GemmSplit& sp);   // partials + counters
-size_t gemm_split_counters(const GemmSplit& sp); // byte offset of the counters
-
 template <bool BWD>
 void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  const uint16_t* La_hi, const uint16_t* La_lo,
@@ -122,12 +91,6 @@ void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  const DropArgs* drop = nullptr, void* split_ws = nullptr);
 
 // ---- rank.hip: rank-r side products and their reductions.
-enum { RS_ROWS = 1, RS_COLS = 2 };
-
-struct StreamPlan {
-  int rm, sub, mb, nb, cpb;
-};
-StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt);
 
 // drop: LoRA dropout applied to S (= X) in the RS_ROWS and RS_COLS passes,
 // or nullptr.
@@ -169,10 +132,6 @@ FinishArgs finish_args();
 void launch_finish(hipStream_t st, FinishArgs& a);
 
 // ---- skinny.hip: forward for M <= 16 tokens.
-struct SkinnyPlan {
-  int slices, ks, rows_total, wg_rows;
-};
-SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r);
 void launch_skinny(hipStream_t st, const uint16_t* x, int M,
                    const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
                    int r, int rpad, float s, float* t_save, void* y,

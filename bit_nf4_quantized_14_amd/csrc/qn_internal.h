@@ -5,6 +5,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "qlora_nf4.h"
+
 namespace qn {
 
 // 16 NF4 levels and 15 midpoint thresholds, derived on the host in double
@@ -14,23 +16,106 @@ void derive_codebook(float levels[16], float thresholds[15]);
 // Levels and thresholds of a QN_CODE_* table; false for an unknown table.
 bool derive_variant_codebook(int code, float levels[16], float thresholds[15]);
 
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline bool valid_tensor(const nf4_tensor* w) {
+  return w != nullptr && w->packed != nullptr && w->qabs != nullptr &&
+         w->gscale != nullptr && w->rows > 0 && w->cols > 0 &&
+         aligned16(w->packed);
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Rank-tile dispatch: JT = number of 16-wide tiles of r, rounded up to a
+// power of two (1, 2, 4, 8, 16 covers r <= 256); rpad = 16 JT.
+inline int rank_tiles(int r) {
+  int jt = 1;
+  while (jt * 16 < r) jt *= 2;
+  return jt;
+}
+
+// Shape rules of the fused calls (plan.cpp).
+bool valid_linear(int64_t M, const nf4_tensor* w, int32_t r);
+
+// ---- fused GEMM (gemm.hip): 256 x 256 output tiles when they give at
+// least ~one workgroup per CU, otherwise 128 x 128.
+constexpr int G_CUS = 256;     // MI355X compute units
+constexpr int G_BK = 64;       // reduction step
+bool gemm_big_tiles(int64_t M, int64_t nout);
+
+// Ragged last wave: when the 256 x 256 tiles leave a last wave that fills
+// at most half of the GPU, each of its tiles is computed as two pieces over
+// the two halves of the reduction (GemmSplit; no split with dropout).  The
+// first piece to finish leaves its fp32 partial tile in the split area, the
+// second adds it and stores the tile.  Split area (the first bytes of a
+// general-path workspace): int32 status word (QN_OK, or QN_ESYNC if a
+// partial never became ready), 4 bytes of padding, 2 * rem counter words,
+// then at gemm_split_part_offset rem partial tiles of 256 * 256 floats.
+// The status word and the counters must be zero at launch (the second piece
+// of each tile sets its counters back to zero).
+struct GemmSplit {
+  int whole, rem, ks;   // whole tiles, split tiles, reduction steps of the
+                        // second piece (the first takes the rest)
+};
+constexpr size_t G_SPLIT_HDR = 8;   // status word + padding before the counters
+GemmSplit gemm_split_plan(int64_t M, int64_t nout, int64_t kred, bool drop);
+size_t gemm_split_bytes(const GemmSplit& sp);        // whole split area
+size_t gemm_split_part_offset(const GemmSplit& sp);  // offset of the partials
+
+// ---- rank-r streams (rank.hip): one pass over X or dY forming row sums
+// (T = X A^T, G = dY B) and/or column sums (dB, dA) as per-block partials.
+enum { RS_ROWS = 1, RS_COLS = 2 };
+
+// RM rows per workgroup, stages of 64 SUB columns, NBUF LDS buffers (NBUF - 1
+// stages in flight): about 32 KB of S per stage for r <= 32, less for the
+// wider adapters whose R and U tiles take more LDS.
+constexpr int rs_rm(int mode, int jt) {
+  return mode == RS_ROWS ? 64 : (jt <= 2 ? 256 : 64);
+}
+constexpr int rs_sub(int mode, int jt) {
+  return jt >= 8 ? 1 : (jt == 4 ? 2 : (mode == RS_ROWS ? 4 : 1));
+}
+constexpr int rs_nbuf(int jt) { return jt >= 16 ? 2 : 3; }
+
+struct StreamPlan {
+  int rm, sub, mb, nb, cpb;   // rows per block, stage width (x64), row
+                              // blocks, column blocks, stages per block
+};
+StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt);
+
+// ---- skinny forward (skinny.hip), M <= QN_SKINNY_M tokens.
+constexpr int64_t QN_SKINNY_M = 16;
+constexpr int SK_WAVES = 8;                  // waves per workgroup
+constexpr int SK_ROWS = 16 * SK_WAVES;       // rows per workgroup
+constexpr int SK_KS_MAX = 4096;              // longest K slice
+constexpr int SK_WGS_PER_CU = 2;             // resident workgroups per CU
+struct SkinnyPlan {
+  int slices, ks, rows_total, wg_rows;
+};
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r);
+
 // Workspace layouts of the fused calls (byte offsets, 256-byte aligned).
 // rpad = r rounded up to 16, 32, 64, 128 or 256 (the adapter MFMA width).
 // M <= QN_SKINNY_M takes the skinny (GEMV) forward.
-constexpr int64_t QN_SKINNY_M = 16;
-
 struct FwdWorkspace {
+  size_t split;     // status word, counters and partial tiles of the GEMM's
+                    // split last wave (GEMM path; offset 0)
   size_t th, tl;    // bf16 [M, rpad]  hi/lo parts of s*T      (GEMM path)
   size_t bp;        // bf16 [N, rpad]  B zero-padded           (GEMM path)
   size_t prow;      // fp32 [nb, M, rpad] column-block partials of T
-  size_t part;      // fp32 [slices, 16, rows] K-slice partials (skinny path)
-  size_t split;     // partial tiles + counters of the GEMM's split last wave
+  size_t part;      // fp32 [slices, M, rows] K-slice partials (skinny path)
   int32_t slices, ks;
   size_t total;
   int32_t rpad;
 };
 
 struct BwdWorkspace {
+  size_t split;     // status word, counters and partial tiles of the dX
+                    // GEMM's split last wave (offset 0)
   size_t bt;        // bf16 [r, N]     B transposed
   size_t uth, utl;  // bf16 [r, Mp]    hi/lo parts of s*T, transposed
   size_t atp;       // bf16 [K, rpad]  A transposed, zero-padded
@@ -38,7 +123,6 @@ struct BwdWorkspace {
   size_t ugh, ugl;  // bf16 [r, Mp]    hi/lo parts of s*G, transposed
   size_t prow;      // fp32 [nb, M, rpad] column-block partials of G
   size_t pcol;      // fp32 [mb, max(N, K), rpad] row-block partials of dB, dA
-  size_t split;     // partial tiles + counters of the dX GEMM's split last wave
   size_t total;
   int64_t mp;       // M rounded up to a multiple of 8
   int32_t rpad;

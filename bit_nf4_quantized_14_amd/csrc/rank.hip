@@ -35,17 +35,6 @@ using namespace qn;
 // and r.
 // ---------------------------------------------------------------------------
 
-// RM rows per workgroup, stages of 64 SUB columns, NBUF LDS buffers (NBUF - 1
-// stages in flight): about 32 KB of S per stage for r <= 32, less for the
-// wider adapters whose R and U tiles take more LDS.
-__host__ __device__ constexpr int rs_rm(int mode, int jt) {
-  return mode == RS_ROWS ? 64 : (jt <= 2 ? 256 : 64);
-}
-__host__ __device__ constexpr int rs_sub(int mode, int jt) {
-  return jt >= 8 ? 1 : (jt == 4 ? 2 : (mode == RS_ROWS ? 4 : 1));
-}
-__host__ __device__ constexpr int rs_nbuf(int jt) { return jt >= 16 ? 2 : 3; }
-
 __device__ __forceinline__ int rs_swz(int row) {
   return (((row >> 3) & 1) << 2) | (((row >> 1) & 1) << 1) | ((row >> 2) & 1);
 }
@@ -457,19 +446,6 @@ namespace qn {
 // Rank-stream geometry: RM rows per workgroup, stages of 64 SUB columns,
 // and enough column blocks for one long-lived workgroup per CU (each keeps
 // two stages in flight).
-StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt) {
-  StreamPlan P;
-  P.rm = rs_rm(mode, jt);
-  P.sub = rs_sub(mode, jt);
-  P.mb = (int)cdiv(M, P.rm);
-  const int64_t nst = cdiv(C, 64 * P.sub);
-  const int64_t want = std::max<int64_t>(1, cdiv(256, P.mb));
-  const int64_t nb = std::min(nst, want);
-  P.cpb = (int)cdiv(nst, nb);
-  P.nb = (int)cdiv(nst, P.cpb);
-  return P;
-}
-
 template <int MODE>
 void launch_rank_stream(hipStream_t st, const char* kname, const StreamPlan& P,
                         const uint16_t* S, int M, int C, const uint16_t* R,

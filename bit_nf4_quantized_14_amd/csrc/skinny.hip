@@ -26,9 +26,6 @@ using namespace qn;
 // slice.  Partial sums go to part[slice][m][row] (fp32, m < M), combined by
 // k_skinny_reduce.
 // ---------------------------------------------------------------------------
-constexpr int SK_WAVES = 8;
-constexpr int SK_ROWS = 16 * SK_WAVES;       // rows per workgroup
-constexpr int SK_KS_MAX = 4096;              // longest K slice
 
 // Items [ib, ie) of this workgroup.  The grid is two workgroups per CU;
 // workgroups b and b + gridDim.x / 2 (the same XCD, typically the same CU)
@@ -243,33 +240,6 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
 
 namespace qn {
 
-// Skinny path plan: K slices of ks columns (multiple of 256, short enough
-// that the X slice leaves LDS room for two workgroups per CU), and enough
-// slices for ~2 items per workgroup.  The grid is two workgroups per CU
-// whatever the item count; the items are split so that the CUs' shares
-// differ by at most one item (skinny_items).
-constexpr int SK_WGS_PER_CU = 2;     // resident skinny workgroups per CU
-constexpr int SK_CUS = 256;          // MI355X compute units
-constexpr int64_t SK_LDS_PER_WG = 64 * 1024;   // X tile budget (bytes)
-
-SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
-  SkinnyPlan P;
-  P.rows_total = (int)(((N + 15) & ~15LL) + 16 * rank_tiles(r));
-  P.wg_rows = (int)cdiv(P.rows_total, SK_ROWS);
-  const int64_t kchunks = cdiv(K, 256);
-  // longest slice whose X tile ((M + 1) rows, zero row included) leaves room
-  // for two workgroups per CU, and enough slices for ~2 items per workgroup
-  int64_t ks_max = (SK_LDS_PER_WG / (2 * (M + 1)) - 8) / 256 * 256;
-  ks_max = std::max<int64_t>(256, std::min<int64_t>(ks_max, SK_KS_MAX));
-  int64_t slices = std::max<int64_t>(cdiv(K, ks_max),
-                                     cdiv((int64_t)SK_CUS * SK_WGS_PER_CU * 2, P.wg_rows));
-  slices = std::min<int64_t>(slices, kchunks);
-  const int64_t ks = cdiv(kchunks, slices) * 256;
-  P.ks = (int)ks;
-  P.slices = (int)cdiv(K, ks);
-  return P;
-}
-
 void launch_skinny(hipStream_t st, const uint16_t* x, int M,
                    const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
                    int r, int rpad, float s, float* t_save, void* y,
@@ -279,7 +249,7 @@ void launch_skinny(hipStream_t st, const uint16_t* x, int M,
   const int nitems = P.wg_rows * P.slices;
   const size_t shm = size_t(M + 1) * (P.ks + 8) * 2;
   QN_LAUNCH_SHM("k_skinny_partial", k_skinny_partial,
-                dim3((unsigned)(SK_CUS * SK_WGS_PER_CU)),
+                dim3((unsigned)(G_CUS * SK_WGS_PER_CU)),
                 dim3(512), shm, st, x, M, w->packed, w->qabs, w->gscale, A,
                 (int)N, (int)K, r, rpad, P.ks, P.wg_rows, nitems, part,
                 qn::codebook());

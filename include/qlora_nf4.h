@@ -58,6 +58,11 @@ extern "C" {
 #define QN_EWORKSPACE (-2)  /* workspace smaller than qlora_workspace_bytes */
 #define QN_EHIP (-3)        /* the HIP runtime reported a launch error */
 #define QN_ENONFINITE (-4)  /* written to *status_dev by nf4_quantize */
+#define QN_ESYNC (-5)       /* written to a fused call's workspace status
+                               word when one piece of a split output tile
+                               never published its partial sum (see
+                               qlora_linear_fwd); never observed in normal
+                               operation, the wait is bounded against hangs */
 
 #define QN_F32 0            /* output element type: fp32 */
 #define QN_BF16 1           /* output element type: bf16 (RNE) */
@@ -348,7 +353,12 @@ size_t qlora_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
  *          B padded to a multiple of 16 columns and, when the GEMM's last
  *          wave of 256 x 256 output tiles is ragged, one fp32 partial tile
  *          per tile of that wave); calls that run at the same time need
- *          workspaces of their own.
+ *          workspaces of their own.  Status word: when M > 16 (the general
+ *          path), the first int32 of ws is zeroed by the call and set to
+ *          QN_ESYNC if a tile of the ragged last wave was split in two and
+ *          its second piece waited in vain for the first piece's partial
+ *          sum; that tile of y is then NaN.  Read it after the stream has
+ *          reached the call's end.
  * Requires K % 64 == 0 (blocks never straddle rows), N % 8 == 0 (16-byte
  * aligned rows), M, N >= 1, every operand smaller than 2 GiB, and all
  * matrix pointers 16-byte aligned.
@@ -375,7 +385,9 @@ int qlora_linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
  * ws     : device workspace, ws_bytes >= qlora_workspace_bytes(M, N, K, r,
  *          QN_BWD) (the transposed and padded adapter operands, the rank-r
  *          partial sums and, when the dX GEMM's last wave of 256 x 256 tiles
- *          is ragged, one fp32 partial tile per tile of that wave).
+ *          is ragged, one fp32 partial tile per tile of that wave).  The
+ *          first int32 of ws is a status word as in qlora_linear_fwd (for
+ *          every M), about the dX tiles.
  * Same shape and alignment rules as qlora_linear_fwd.
  * Errors: QN_EINVAL, QN_EWORKSPACE, QN_EHIP.
  */
@@ -431,7 +443,10 @@ int qlora_linear_bwd_dropout(const uint16_t* dy, const uint16_t* x,
 const char* qn_strerror(int code);
 
 /*
- * qn_profile_kernel -- measurement hook (host), for benchmarks.
+ * qn_profile_kernel -- measurement hook (host), for benchmarks; active only
+ * in the profiling build of the library (compiled with QN_PROFILE_HOOK:
+ * libqlora_nf4_prof.so).  The default build keeps no state for it and
+ * returns QN_EINVAL.
  *
  * Arms per-launch timing of one internal kernel: each later launch of the
  * kernel called `name` (e.g. "k_fwd_gemm", "k_bwd_dx_gemm", "k_dequant")
@@ -439,8 +454,9 @@ const char* qn_strerror(int code);
  * right after, for i = 0, 1, ... up to `capacity` launches.  ev_start and
  * ev_stop are host arrays of hipEvent_t (as void*) created by the caller and
  * must stay valid while armed.  name == NULL disarms.  Returns the number of
- * launches recorded since the last arming (>= 0), or QN_EINVAL.  Process
- * global and not thread-safe.
+ * launches recorded since the last arming (>= 0), or QN_EINVAL.  In the
+ * profiling build the armed state is process-global and not thread-safe:
+ * arm it from one thread while no other thread calls the library.
  */
 int qn_profile_kernel(const char* name, void** ev_start, void** ev_stop,
                       int32_t capacity);

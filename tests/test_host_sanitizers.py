@@ -1,6 +1,8 @@
 """Host C++ of the library under AddressSanitizer and UndefinedBehavior-
-Sanitizer: tests/host/codebook_check.cpp linked with the codebook source,
-built with g++ and run on the CPU."""
+Sanitizer, built with g++ and run on the CPU: tests/host/codebook_check.cpp
+linked with the codebook source, and tests/host/plan_check.cpp linked with
+the planning source (tile choice, the split of a ragged last wave, rank
+stream and skinny plans, workspace layouts)."""
 
 import os
 import shutil
@@ -12,14 +14,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bit_nf4_quantized_14_amd", "csrc")
 
 
-@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
-def test_codebook_under_asan_and_ubsan(tmp_path):
-    exe = tmp_path / "codebook_check"
+def _build_and_run(tmp_path, check_src, lib_src):
+    exe = tmp_path / os.path.splitext(os.path.basename(check_src))[0]
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(ROOT, "tests", "host", "codebook_check.cpp"),
-           os.path.join(CSRC, "codebook.cpp"), "-o", str(exe)]
+           os.path.join(ROOT, "tests", "host", check_src),
+           os.path.join(CSRC, lib_src), "-o", str(exe)]
     build = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert build.returncode == 0, build.stderr
     # verify_asan_link_order=0: the sanitizer runtime need not be the first
@@ -31,3 +32,13 @@ def test_codebook_under_asan_and_ubsan(tmp_path):
                          env=env)
     assert run.returncode == 0, run.stdout + run.stderr
     assert run.stdout.strip() == "ok"
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_codebook_under_asan_and_ubsan(tmp_path):
+    _build_and_run(tmp_path, "codebook_check.cpp", "codebook.cpp")
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_plans_and_layouts_under_asan_and_ubsan(tmp_path):
+    _build_and_run(tmp_path, "plan_check.cpp", "plan.cpp")
