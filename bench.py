@@ -467,40 +467,26 @@ def bench_70b(reps, do_train=True):
         def step():
             pr.fwd()
             pr.bwd()
-        sec = timed(step, reps)
+        sec = timed_graph(step, reps)
         f = linear_flops(pr.m, n, k, pr.r)
         per[name] = {"ms": sec * 1e3, "TFLOP/s": f / sec / 1e12}
+        for kname, kf in (("k_fwd_gemm", 2 * pr.m * n * k + 2 * pr.m * n * pr.r),
+                          ("k_bwd_dx_gemm", 2 * pr.m * n * k + 2 * pr.m * k * pr.r)):
+            ms, _ = kernel_times_ms(capi, kname, step, 1, reps)
+            if ms is not None:
+                per[name][kname] = {"avg_ms": ms, "TFLOP/s": kf / (ms * 1e-3) / 1e12}
         flops += f
         total += sec
         del pr
         torch.cuda.empty_cache()
     res["layer70b"] = {"flops_per_pass": flops, "ms_per_pass": total * 1e3,
                        "TFLOP/s": flops / total / 1e12,
+                       "timing": "graph replay of each projection's fwd+bwd; "
+                                 "GEMM kernels by per-launch HIP events",
                        "frac_mfma_peak": flops / total / 1e12 / BF16_PEAK_TFLOPS,
                        "per_projection": per}
     log(f"layer70b: {res['layer70b']['TFLOP/s']:.1f} TFLOP/s")
     return res
-
-
-# source files that define each kernel (plus the shared device header)
-KERNEL_SOURCES = (("k_gemm", "gemm.hip"), ("k_rank", "rank.hip"),
-                  ("k_dequant", "codec.hip"), ("k_quantize", "codec.hip"),
-                  ("k_skinny", "skinny.hip"), ("k_merge", "merge.hip"),
-                  ("k_adamw8", "adamw.hip"))
-
-
-def kernel_source_sha(kernel_key: str):
-    """sha256[:16] of the sources a kernel is built from, or None."""
-    import hashlib
-    csrc = os.path.join(ROOT, "bit_nf4_quantized_14_amd", "csrc")
-    for prefix, fname in KERNEL_SOURCES:
-        if kernel_key.startswith(prefix):
-            h = hashlib.sha256()
-            for f in ("qn_device.h", fname):
-                with open(os.path.join(csrc, f), "rb") as fh:
-                    h.update(fh.read())
-            return h.hexdigest()[:16]
-    return None
 
 
 def measured_traffic(kernel_key: str):
@@ -514,7 +500,8 @@ def measured_traffic(kernel_key: str):
         k = rec["kernels"][kernel_key]
     except (OSError, ValueError, KeyError):
         return None
-    if k.get("source_sha256_16") != kernel_source_sha(kernel_key):
+    from bit_nf4_quantized_14_amd.profiling import source_sha
+    if k.get("source_sha256_16") != source_sha(kernel_key):
         return None
     return k["read_bytes"] + k["write_bytes"]
 
@@ -594,6 +581,9 @@ def main():
     from bit_nf4_quantized_14_amd import capi
     from bit_nf4_quantized_14_amd import workloads as wl
 
+    # the profiling build: the same kernels, plus per-launch HIP events
+    # around one named kernel (qn_profile_kernel) for the roofline figures
+    capi.use_profiling_build()
     capi.lib()
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -667,6 +657,35 @@ def main():
     for kname, f in gemm_flops.items():
         kernels[kname]["TFLOP/s"] = f / (kernels[kname]["avg_ms"] * 1e-3) / 1e12
 
+    # the same step with fp32 Y and dX (the mode the 2e-3 parity gate is
+    # stated on), timed the same way
+    pr32 = Problem(wk, 0, y_dtype=capi.QN_F32)
+
+    def step32():
+        pr32.fwd()
+        pr32.bwd()
+    for _ in range(args.warmup):
+        step32()
+    sec32 = timed(step32, args.steps, warmup=0)
+    fp32_mode = {"ms_per_step": sec32 * 1e3, "TFLOP/s": flops / sec32 / 1e12,
+                 "frac_mfma_peak": flops / sec32 / 1e12 / BF16_PEAK_TFLOPS}
+    log(f"gate7b fp32 outputs: {sec32*1e3:.3f} ms/step, "
+        f"{fp32_mode['TFLOP/s']:.1f} TFLOP/s")
+    del pr32
+    # context: hipBLASLt (torch) bf16 GEMMs of the same shapes on the
+    # dequantized weight, without the adapter terms
+    wd = capi.nf4_dequantize(pr.w)
+    import torch.nn.functional as F
+    ref = {}
+    for key, fn, f in (
+            ("forward X W'^T", lambda: F.linear(pr.x, wd), 2 * m * n * k),
+            ("backward dY W'", lambda: torch.matmul(pr.dy, wd), 2 * m * n * k)):
+        sec_ref = timed(fn, args.steps, warmup=3)
+        ref[key] = {"ms": sec_ref * 1e3, "TFLOP/s": f / sec_ref / 1e12}
+    del wd
+    log("hipBLASLt bf16: " + ", ".join(f"{k2} {v['TFLOP/s']:.0f} TFLOP/s"
+                                      for k2, v in ref.items()))
+
     out = {
         "metric": METRIC,
         "value": value,
@@ -695,6 +714,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch",
                      "avg_ms": dom_ms, "flops_per_launch": gemm_flops[dom]},
         "kernels": kernels,
+        "fp32_mode": fp32_mode,
+        "hipblaslt_bf16_reference": ref,
     }
     del pr
     torch.cuda.empty_cache()

@@ -1,9 +1,14 @@
-"""Build the HIP library ``libqlora_nf4.so`` in-tree for gfx950.
+"""Build the HIP library in-tree for gfx950.
 
 ``python -m bit_nf4_quantized_14_amd.build`` (or ``__graft_entry__.build()``)
-compiles every source under ``csrc/`` with hipcc and writes the shared
-library next to this file, where :mod:`bit_nf4_quantized_14_amd.capi` loads
-it.
+compiles every source under ``csrc/`` with hipcc (one object per source, in
+parallel) and links two shared libraries next to this file:
+
+* ``libqlora_nf4.so``      -- the library (:mod:`bit_nf4_quantized_14_amd.capi`
+  loads it by default);
+* ``libqlora_nf4_prof.so`` -- the same sources built with QN_PROFILE_HOOK,
+  whose ``qn_profile_kernel`` records HIP events around one named kernel's
+  launches (used by bench.py).
 """
 
 from __future__ import annotations
@@ -12,14 +17,18 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
+OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+PROF_LIB_PATH = os.path.join(PKG_DIR, "libqlora_nf4_prof.so")
 ARCH = "gfx950"
+VARIANTS = {LIB_PATH: [], PROF_LIB_PATH: ["-DQN_PROFILE_HOOK"]}
 
 
 def hipcc() -> str:
@@ -35,28 +44,51 @@ def sources() -> list[str]:
                   if f.endswith((".hip", ".cpp")))
 
 
-def compile_command(out: str = LIB_PATH) -> list[str]:
+def compile_flags(defines: list[str]) -> list[str]:
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-        "-shared", "-Wall", "-Wno-unused-function",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-Wall", "-Wno-unused-function",
         # keep packed-fp32 instructions out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        f"-I{INCLUDE}", f"-I{CSRC}",
-        *sources(), "-o", out,
+        f"-I{INCLUDE}", f"-I{CSRC}", *defines,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always; no up-to-date check) and return its
-    path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_command(tmp)
+def compile_command(src: str, obj: str, defines: list[str]) -> list[str]:
+    return [hipcc(), *compile_flags(defines), "-c", src, "-o", obj]
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" +
+                           res.stdout + res.stderr)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile both library variants (always; no up-to-date check) and
+    return the path of the default one."""
+    jobs = jobs or max(1, min(8, os.cpu_count() or 1))
+    srcs = sources()
+    plan = []        # (lib, objects, compile commands)
+    for lib, defines in VARIANTS.items():
+        tag = os.path.splitext(os.path.basename(lib))[0]
+        odir = os.path.join(OBJ_DIR, tag)
+        os.makedirs(odir, exist_ok=True)
+        objs = [os.path.join(odir, os.path.basename(s) + ".o") for s in srcs]
+        plan.append((lib, objs, [compile_command(s, o, defines)
+                                 for s, o in zip(srcs, objs)]))
+    cmds = [c for _, _, cs in plan for c in cs]
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    for lib, objs, _ in plan:
+        tmp = lib + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+              "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB_PATH
 
 

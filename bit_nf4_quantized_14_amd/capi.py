@@ -17,8 +17,12 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqlora_nf4.so")
+# the same library built with QN_PROFILE_HOOK (qn_profile_kernel active)
+PROF_LIB_PATH = os.path.join(_PKG, "libqlora_nf4_prof.so")
+_use_prof = False
 
 QN_OK, QN_EINVAL, QN_EWORKSPACE, QN_EHIP, QN_ENONFINITE = 0, -1, -2, -3, -4
+QN_ESYNC = -5
 QN_F32, QN_BF16 = 0, 1
 QN_FWD, QN_BWD, QN_FWD_DROPOUT = 0, 1, 2
 QN_BLOCK, QN_GROUP, QN_MAX_RANK = 64, 256, 256
@@ -69,6 +73,20 @@ class _Dropout(ctypes.Structure):
 _lib = None
 
 
+def use_profiling_build() -> None:
+    """Load the profiling variant (libqlora_nf4_prof.so, whose
+    qn_profile_kernel records per-launch HIP events) instead of the default
+    library.  Must be called before the first call into the library."""
+    global _use_prof
+    if _lib is not None and not _use_prof:
+        raise RuntimeError("the default library is already loaded")
+    _use_prof = True
+
+
+def lib_path() -> str:
+    return PROF_LIB_PATH if _use_prof else LIB_PATH
+
+
 def lib() -> ctypes.CDLL:
     """Load the HIP library once; raise if it has not been built.
 
@@ -80,12 +98,13 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    path = lib_path()
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is not built; run `python -m "
+            f"{path} is not built; run `python -m "
             "bit_nf4_quantized_14_amd.build` (hipcc, gfx950)")
     import torch  # noqa: F401  (binds torch's HIP runtime first)
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     sp = ctypes.POINTER(_NF4Struct)
     L.nf4_codebook.argtypes = [vp, vp]
