@@ -34,11 +34,12 @@ EXPORTS = ("nf4_codebook", "nf4_quantize", "nf4_dequantize",
            "qn_adamw8_step", "qn_adamw8_staging_bytes", "qn_adamw8_paged_step",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
            "qlora_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
-           "qn_strerror", "qn_profile_kernel")
+           "qn_strerror", "qn_profile_kernel", "qlora_linear_fwd_noalloc")
 QN_DEQUANT_BATCH_MAX = 16
 QN_CODE_NF4, QN_CODE_FP4, QN_CODE_INT4 = 0, 1, 2
 QN_CONST_DQ8, QN_CONST_FP32, QN_CONST_CENTERED = 0, 1, 2
 QN_ADAMW_BLOCK = 256
+QN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class _NF4Struct(ctypes.Structure):
@@ -148,6 +149,9 @@ def lib() -> ctypes.CDLL:
                                            vp, vp, i32, vp, vp, dp, vp,
                                            ctypes.c_size_t, vp]
     L.qlora_linear_bwd_dropout.restype = ctypes.c_int
+    L.qlora_linear_fwd_noalloc.argtypes = [vp, i64, sp, vp, vp, i32, f32, vp,
+                                           i32, vp, vp]
+    L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
     L.qn_profile_kernel.argtypes = [ctypes.c_char_p, vp, vp, i32]
     L.qn_profile_kernel.restype = ctypes.c_int
     L.qn_strerror.argtypes = [ctypes.c_int]
@@ -437,6 +441,27 @@ def qlora_linear_fwd(x, w: NF4Tensor, A, B, r: int, alpha: float, y=None,
         _ptr(x), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
         _ptr(y), y_dtype, _ptr(t_save), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return y, t_save
+
+
+def qlora_linear_fwd_noalloc(x, w: NF4Tensor, A, B, r: int, alpha: float,
+                             y=None, y_dtype: int = QN_F32, t_save=None,
+                             stream=None):
+    """Fused forward with the library's own per-GPU scratch array as its
+    workspace (no workspace argument); returns (y, t_save).  Calls on one
+    GPU share the array: do not overlap them."""
+    import torch
+    M = x.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, w.rows), device=dev,
+                        dtype=torch.float32 if y_dtype == QN_F32 else torch.bfloat16)
+    if t_save is None:
+        t_save = torch.empty((M, r), device=dev, dtype=torch.float32)
+    st = w.as_struct()
+    _check("qlora_linear_fwd_noalloc", lib().qlora_linear_fwd_noalloc(
+        _ptr(x), M, ctypes.byref(st), _ptr(A), _ptr(B), r, float(alpha),
+        _ptr(y), y_dtype, _ptr(t_save), _stream(stream)))
     return y, t_save
 
 

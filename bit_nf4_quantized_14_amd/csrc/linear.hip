@@ -4,7 +4,9 @@
 // hook.  "QLoRA Guide" (Forward pass diagram: W_bf16 x + B(A(x)); only A
 // and B get gradients), "QLoRA Implementation Details (2025 Edition)"
 // (Step 4: scale alpha / r).
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "qn_host.h"
 
@@ -106,10 +108,13 @@ bool drop_args(const qn_dropout* d, qn::DropArgs* out, bool* use) {
   return true;
 }
 
+// allow_split: the GEMM may split a ragged last wave (its partial tiles need
+// workspace); without it the workspace is the smaller no-split layout.
 int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
                const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                void* y, int32_t y_dtype, float* t_save, const qn_dropout* drop,
-               void* ws, size_t ws_bytes, void* stream) {
+               void* ws, size_t ws_bytes, void* stream,
+               bool allow_split = true) {
   if (x == nullptr || A == nullptr || B == nullptr || y == nullptr ||
       t_save == nullptr)
     return QN_EINVAL;
@@ -124,7 +129,7 @@ int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   // a forward with dropout always takes the general path (the skinny
   // kernel shares one X slice between W and A rows)
   const qn::FwdWorkspace L =
-      qn::fwd_workspace_layout(M, N, K, r, drop != nullptr);
+      qn::fwd_workspace_layout(M, N, K, r, drop != nullptr, allow_split);
   if (ws == nullptr || ws_bytes < L.total || !aligned16(ws))
     return QN_EWORKSPACE;
   const float s = alpha / (float)r;
@@ -154,10 +159,13 @@ int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   if (!b_as_is)
     fa.P1 = FinishPad{B, Bp, Ni, L.rpad, (int)r, (int64_t)r, (int64_t)1};
   char* split_ws = ws_at<char>(ws, L.split);
-  zero_split_counters(fa.P2, split_ws, gemm_split_plan(M, N, K, false));
+  zero_split_counters(fa.P2, split_ws,
+                      allow_split ? gemm_split_plan(M, N, K, false)
+                                  : GemmSplit{0, 0, 0});
   launch_finish(st, fa);
   launch_gemm<false>(st, x, w, Th, Tl, b_as_is ? B : Bp, Mi, L.rpad, y,
-                     (int)(y_dtype == QN_BF16), nullptr, split_ws);
+                     (int)(y_dtype == QN_BF16), nullptr,
+                     allow_split ? split_ws : nullptr);
   return check_launch();
 }
 
@@ -276,4 +284,58 @@ int qlora_linear_bwd_dropout(const uint16_t* dy, const uint16_t* x,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is a file-scope device array, one
+// copy per GPU, shared by every call on that GPU.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) char scratch[QN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int QN_MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_addr[QN_MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.  The host-side name is only a stand-in
+// for the symbol; kernels get this address instead.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= QN_MAX_DEVICES)
+    return QN_EHIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess ||
+          p == nullptr)
+        return QN_EHIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return QN_OK;
+}
+
+}  // namespace
+
+extern "C" int qlora_linear_fwd_noalloc(const uint16_t* x, int64_t M,
+                                        const nf4_tensor* w, const uint16_t* A,
+                                        const uint16_t* B, int32_t r,
+                                        float alpha, void* y, int32_t y_dtype,
+                                        float* t_save, void* stream) {
+  if (!valid_linear(M, w, r)) return QN_EINVAL;
+  // no split of a ragged last wave: its partial tiles would need up to
+  // 32 MiB of their own
+  const qn::FwdWorkspace L =
+      qn::fwd_workspace_layout(M, w->rows, w->cols, r, false, false);
+  if (L.total > QN_NOALLOC_SCRATCH_BYTES) return QN_EWORKSPACE;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc != QN_OK) return rc;
+  return linear_fwd(x, M, w, A, B, r, alpha, y, y_dtype, t_save, nullptr, ws,
+                    QN_NOALLOC_SCRATCH_BYTES, stream, false);
+}
 

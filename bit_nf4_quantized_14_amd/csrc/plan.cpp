@@ -101,7 +101,7 @@ SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
-                                  int32_t r, bool general) {
+                                  int32_t r, bool general, bool split) {
   FwdWorkspace L{};
   L.rpad = 16 * rank_tiles(r);
   if (M <= qn::QN_SKINNY_M && !general) {
@@ -115,7 +115,8 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
   const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r));
   size_t off = 0;
   L.split = off;   // status word first
-  off += align256(gemm_split_bytes(gemm_split_plan(M, N, K, false)));
+  off += align256(gemm_split_bytes(split ? gemm_split_plan(M, N, K, false)
+                                         : GemmSplit{0, 0, 0}));
   L.th = off;
   off += align256(size_t(M) * L.rpad * 2);
   L.tl = off;

@@ -129,9 +129,11 @@ struct BwdWorkspace {
 };
 
 // general: the layout of the general path also for M <= QN_SKINNY_M (a
-// forward with dropout never takes the skinny path).
+// forward with dropout never takes the skinny path).  split: room for the
+// partial tiles of a split last wave (without it the GEMM never splits and
+// the split area holds only the status word).
 FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K, int32_t r,
-                                  bool general);
+                                  bool general, bool split = true);
 BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
 }  // namespace qn

@@ -439,6 +439,36 @@ int qlora_linear_bwd_dropout(const uint16_t* dy, const uint16_t* x,
                              const qn_dropout* drop, void* ws,
                              size_t ws_bytes, void* stream);
 
+/*
+ * qlora_linear_fwd_noalloc -- qlora_linear_fwd without a workspace argument
+ * (device), for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation.  It computes exactly what qlora_linear_fwd computes, with the
+ * same kernels, and calls no allocating routine.
+ *
+ * Its workspace is a file-scope device array of QN_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) inside the library, one copy per GPU, held until the process
+ * ends; its device address is looked up once per GPU on the first call
+ * made with that GPU current (`stream` must belong to the current device).
+ * Every call on a GPU uses the same array, so calls that overlap on one
+ * GPU (different streams, or different host threads) race: serialize them.
+ * The GEMM does not split a ragged last wave here (no room is kept for
+ * partial tiles), so results can differ from qlora_linear_fwd's in the fp32
+ * summation order of such tiles; with no split planned they are identical.
+ * The first int32 of the array is the status word described under
+ * qlora_linear_fwd.
+ * Arguments as qlora_linear_fwd without ws / ws_bytes.
+ * Errors: QN_EINVAL, QN_EWORKSPACE (the shape's workspace exceeds
+ * QN_NOALLOC_SCRATCH_BYTES), QN_EHIP.
+ */
+#define QN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int qlora_linear_fwd_noalloc(const uint16_t* x, int64_t M,
+                             const nf4_tensor* w, const uint16_t* A,
+                             const uint16_t* B, int32_t r, float alpha,
+                             void* y, int32_t y_dtype, float* t_save,
+                             void* stream);
+
 /* qn_strerror -- static text for a QN_* code (host). */
 const char* qn_strerror(int code);
 

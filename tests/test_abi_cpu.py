@@ -242,3 +242,18 @@ def test_dropout_validation():
     assert (capi.qlora_workspace_bytes(64, 256, 512, 8, capi.QN_FWD_DROPOUT)
             == capi.qlora_workspace_bytes(64, 256, 512, 8, capi.QN_FWD))
     assert capi.qlora_workspace_bytes(64, 256, 512, 8, 3) == 0
+
+
+def test_noalloc_forward_rejects_shapes_beyond_its_scratch():
+    """The allocation-free forward checks its workspace need against the
+    fixed scratch array on the host and returns QN_EWORKSPACE before any
+    launch (r = 256 at M = 16384 needs more than 32 MiB)."""
+    L = capi.lib()
+    p = 0x10000
+    st = _fake_tensor(4096, 4096)
+    assert capi.qlora_workspace_bytes(16384, 4096, 4096, 256, capi.QN_FWD) > \
+        capi.QN_NOALLOC_SCRATCH_BYTES
+    assert L.qlora_linear_fwd_noalloc(p, 16384, ctypes.byref(st), p, p, 256, 1.0,
+                                      p, capi.QN_F32, p, None) == capi.QN_EWORKSPACE
+    assert L.qlora_linear_fwd_noalloc(p, 16, ctypes.byref(st), p, p, 0, 1.0,
+                                      p, capi.QN_F32, p, None) == capi.QN_EINVAL
