@@ -191,6 +191,92 @@ __device__ __forceinline__ void gemm_store_a(const ARegs<BM, BN, BWD>& R,
   }
 }
 
+// Global loads of one reduction step, for a thread of a tile.
+//
+// Fast addressing (CHK = false): every bound a load depends on is either a
+// per-thread constant (rows of A past M, weight rows or columns past the
+// tile's edge) or the same for the whole workgroup (steps past the end of
+// the reduction), because the reduction length is a multiple of the 64-wide
+// step.  Each thread's offsets of step 0 are formed once, with G_OOB baked
+// in where its element lies outside the operand; a step adds its advance as
+// the scalar offset, and a step past the end loads through a zero-sized
+// range.  The only per-step vector work is the group-scale offset, whose
+// 16384-weight groups do not follow the 64-wide steps.  The scalar offset
+// is outside the range check, so it is only ever added to offsets that
+// stay inside the operand.
+// Checked addressing (CHK = true, the backward when N % 64 != 0, whose last
+// step is partial): every offset and bound is formed per step.
+template <int BM, int BN, bool BWD, bool CHK>
+struct GemmLoader {
+  using C = GemmCfg<BM, BN, BWD>;
+  const uint16_t* Aop;
+  const uint8_t* packed;
+  const uint8_t* qabs;
+  const float* gscale;
+  uint32_t a_bytes, p_bytes, q_bytes, d_bytes;
+  int M, N, K, KRED, m0, c0, tid;
+  uint32_t a_vo[C::A_CHUNKS];   // A chunk offsets at step 0 (fast)
+  uint32_t w_vo, q_vo, e0;      // packed / code offsets and element index
+                                // at step 0 (fast)
+
+  __device__ __forceinline__ void init() {
+    if constexpr (!CHK) {
+#pragma unroll
+      for (int i = 0; i < C::A_CHUNKS; ++i) {
+        const int q = tid + C::NT * i, row = q >> 3;
+        a_vo[i] = m0 + row < M
+                      ? (uint32_t)(((int64_t)(m0 + row) * KRED + 8 * (q & 7)) * 2)
+                      : G_OOB;
+      }
+      int n, k;
+      if (!BWD) {
+        n = c0 + tid / C::TPR;
+        k = (tid % C::TPR) * C::EPT;
+      } else {
+        n = tid / C::TPR;
+        k = c0 + (tid % C::TPR) * C::EPT;
+      }
+      const bool ok = BWD ? k < K : n < N;
+      e0 = (uint32_t)((int64_t)n * K + k);
+      w_vo = ok ? e0 >> 1 : G_OOB;
+      q_vo = ok ? e0 >> 6 : G_OOB;
+    }
+  }
+
+  __device__ __forceinline__ void load_a(ARegs<BM, BN, BWD>& R, int red0) const {
+    if constexpr (CHK) {
+      gemm_load_a<BM, BN, BWD>(R, make_rsrc(Aop, a_bytes), M, KRED, m0, red0, tid);
+    } else {
+      const rsrc_t ra = make_rsrc(Aop, red0 < KRED ? a_bytes : 0u);
+#pragma unroll
+      for (int i = 0; i < C::A_CHUNKS; ++i)
+        R.v[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, a_vo[i], red0 * 2, 0));
+    }
+  }
+
+  __device__ __forceinline__ void load_w(WRegs& R, int red0) const {
+    if constexpr (CHK) {
+      gemm_load_w<BM, BN, BWD>(R, make_rsrc(packed, p_bytes),
+                               make_rsrc(qabs, q_bytes), make_rsrc(gscale, d_bytes),
+                               N, K, c0, red0, tid);
+    } else {
+      const bool live = red0 < KRED;
+      const rsrc_t rp = make_rsrc(packed, live ? p_bytes : 0u);
+      const rsrc_t rq = make_rsrc(qabs, live ? q_bytes : 0u);
+      const rsrc_t rd = make_rsrc(gscale, live ? d_bytes : 0u);
+      // element advance of the step: along the row (forward) or red0 rows
+      // down (backward)
+      const uint32_t adv = BWD ? (uint32_t)red0 * (uint32_t)K : (uint32_t)red0;
+      R.w = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, w_vo, (int)(adv >> 1), 0));
+      R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, q_vo, (int)(adv >> 6), 0);
+      R.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                          rd, ((e0 + adv) >> 14) << 2, 0, 0));
+    }
+  }
+};
+
 // Transposed B operand for the backward: lane l needs 8 consecutive
 // reduction rows (8 * (l / 32) ...) of output column (col0 + l % 32).  Each
 // ds_read_b64_tr_b16 serves 4 rows: in every group of 16 lanes, lane
@@ -305,15 +391,29 @@ __device__ __forceinline__ void gemm_mma_deq(
   }
 }
 
-// Maps the linear workgroup index to an output tile so that each XCD (the
-// hardware deals workgroups round-robin over 8 XCDs) works on a contiguous
-// run of tiles, and runs walk the N direction first: a run shares A rows in
-// that XCD's L2.
-__device__ __forceinline__ void gemm_tile_of(int pid, int total, int tiles_n,
+// Output tile of tile index i in grouped order: groups of G_GROUP_M tile
+// rows, walked column by column inside a group, so that any 32 consecutive
+// indices cover 4 tile rows x 8 tile columns.  A bijection of
+// [0, tiles_m * tiles_n).
+constexpr int G_GROUP_M = 4;
+
+__device__ __forceinline__ void gemm_tile_at(int i, int tiles_m, int tiles_n,
                                              int& tm, int& tn) {
-  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
-  tm = pid / tiles_n;
-  tn = pid % tiles_n;
+  const int group = i / (G_GROUP_M * tiles_n);
+  const int first = group * G_GROUP_M;
+  const int rows = min(G_GROUP_M, tiles_m - first);
+  const int in = i - group * G_GROUP_M * tiles_n;
+  tm = first + in % rows;
+  tn = in / rows;
+}
+
+// The hardware deals workgroups round-robin over the 8 XCDs; workgroup pid
+// of the first `nwhole` takes tile index (pid % 8) * (nwhole / 8) + pid / 8,
+// so each XCD works through a contiguous run of indices: at any moment its
+// 32 CUs hold a 4 x 8 block of tiles, whose A row tiles and weight column
+// tiles its L2 shares.
+__device__ __forceinline__ int gemm_xcd_index(int pid, int nwhole) {
+  return (nwhole & 7) == 0 ? (pid & 7) * (nwhole >> 3) + (pid >> 3) : pid;
 }
 
 // Kernel-side view of a GemmSplit: workgroups [0, whole) take whole tiles,
@@ -385,17 +485,16 @@ __device__ __forceinline__ void gemm_add_partial(
 
 // One reduction step: MFMAs on (sAc, sWc) while the next A tile streams into
 // sAn and the weight tile held in Wc is dequantized into sWn.
-template <int BM, int BN, bool BWD>
+template <int BM, int BN, bool BWD, bool CHK>
 __device__ __forceinline__ void gemm_step(
     int st, char* sAc, uint16_t* sWc, char* sAn, uint16_t* sWn, WRegs& Wc,
-    rsrc_t ra, rsrc_t rp, rsrc_t rq, rsrc_t rd, int M, int N, int K, int KRED,
-    int m0, int c0, int wave, int wm, int wn, int tid, int lane,
+    const GemmLoader<BM, BN, BWD, CHK>& ld, int wm, int wn, int tid, int lane,
     const Codebook& cb,
     f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
   WRegs Wn;
   ARegs<BM, BN, BWD> An;
-  gemm_load_a<BM, BN, BWD>(An, ra, M, KRED, m0, (st + 1) * G_BK, tid);
-  gemm_load_w<BM, BN, BWD>(Wn, rp, rq, rd, N, K, c0, (st + 2) * G_BK, tid);
+  ld.load_a(An, (st + 1) * G_BK);
+  ld.load_w(Wn, (st + 2) * G_BK);
   gemm_mma_deq<BM, BN, BWD>(sAc, sWc, sWn, Wc, An, sAn, cb, wm, wn, tid, lane, acc);
   __builtin_amdgcn_s_waitcnt(0);   // all counters: loads and LDS writes done
   __syncthreads();
@@ -473,7 +572,7 @@ __device__ __forceinline__ void gemm_drop_acc(
 
 // SPLIT: the grid holds split pieces (SplitArgs); without it the kernel
 // has none of their code.
-template <int BM, int BN, bool BWD, bool DROP, bool SPLIT>
+template <int BM, int BN, bool BWD, bool DROP, bool SPLIT, bool CHK>
 __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
     const uint16_t* __restrict__ Aop, const uint8_t* __restrict__ packed,
     const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
@@ -495,26 +594,39 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int tiles_n = (NOUT + BN - 1) / BN;
   const int nsteps = (KRED + G_BK - 1) / G_BK;
+  const int tiles_m = (M + BM - 1) / BM;
   int tm, tn, s0 = 0, s1 = nsteps, split = -1;
   if (!SPLIT || (int)blockIdx.x < sp.whole) {
-    gemm_tile_of(blockIdx.x, SPLIT ? sp.whole : ((M + BM - 1) / BM) * tiles_n,
-                 tiles_n, tm, tn);
+    gemm_tile_at(gemm_xcd_index(blockIdx.x, SPLIT ? sp.whole : tiles_m * tiles_n),
+                 tiles_m, tiles_n, tm, tn);
   } else {
     const int q = blockIdx.x - sp.whole;
     const bool first = q < sp.rem;
     split = first ? q : q - sp.rem;
-    tm = (sp.whole + split) / tiles_n;
-    tn = (sp.whole + split) % tiles_n;
+    gemm_tile_at(sp.whole + split, tiles_m, tiles_n, tm, tn);
     s0 = first ? sp.ks : 0;
     s1 = first ? nsteps : sp.ks;
   }
   const int m0 = tm * BM, c0 = tn * BN;
 
   const int64_t numel = (int64_t)N * K;
-  const rsrc_t ra = make_rsrc(Aop, (uint32_t)((int64_t)M * KRED * 2));
-  const rsrc_t rp = make_rsrc(packed, (uint32_t)((numel + 1) >> 1));
-  const rsrc_t rq = make_rsrc(qabs, (uint32_t)((numel + 63) >> 6));
-  const rsrc_t rd = make_rsrc(gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
+  GemmLoader<BM, BN, BWD, CHK> ld;
+  ld.Aop = Aop;
+  ld.packed = packed;
+  ld.qabs = qabs;
+  ld.gscale = gscale;
+  ld.a_bytes = (uint32_t)((int64_t)M * KRED * 2);
+  ld.p_bytes = (uint32_t)((numel + 1) >> 1);
+  ld.q_bytes = (uint32_t)((numel + 63) >> 6);
+  ld.d_bytes = (uint32_t)(((numel + 16383) >> 14) << 2);
+  ld.M = M;
+  ld.N = N;
+  ld.K = K;
+  ld.KRED = KRED;
+  ld.m0 = m0;
+  ld.c0 = c0;
+  ld.tid = tid;
+  ld.init();
 
   f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -543,21 +655,19 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
     WRegs Wc;                                                                  \
     {                                                                          \
       ARegs<BM, BN, BWD> A0;                                                   \
-      gemm_load_a<BM, BN, BWD>(A0, ra, M, KRED, m0, r0_ * G_BK, tid);          \
+      ld.load_a(A0, r0_ * G_BK);                                               \
       gemm_store_a<BM, BN, BWD>(A0, sA0, tid);                                 \
     }                                                                          \
-    gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, r0_ * G_BK, tid);       \
+    ld.load_w(Wc, r0_ * G_BK);                                                 \
     gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);                             \
-    gemm_load_w<BM, BN, BWD>(Wc, rp, rq, rd, N, K, c0, (r0_ + 1) * G_BK, tid); \
+    ld.load_w(Wc, (r0_ + 1) * G_BK);                                           \
     __builtin_amdgcn_s_waitcnt(0); /* loads landed in LDS and registers */     \
     __syncthreads();                                                           \
     for (int st = r0_; st < r1_; st += 2) {                                    \
-      gemm_step<BM, BN, BWD>(st, sA0, sW0, sA1, sW1, Wc, ra, rp, rq, rd, M, N, \
-                             K, KRED, m0, c0, wave, wm, wn, tid, lane, cb,     \
-                             acc);                                             \
-      gemm_step<BM, BN, BWD>(st + 1, sA1, sW1, sA0, sW0, Wc, ra, rp, rq, rd,   \
-                             M, N, K, KRED, m0, c0, wave, wm, wn, tid, lane,   \
-                             cb, acc);                                         \
+      gemm_step<BM, BN, BWD, CHK>(st, sA0, sW0, sA1, sW1, Wc, ld, wm, wn, tid, \
+                                  lane, cb, acc);                              \
+      gemm_step<BM, BN, BWD, CHK>(st + 1, sA1, sW1, sA0, sW0, Wc, ld, wm, wn,  \
+                                  tid, lane, cb, acc);                         \
     }                                                                          \
   } while (0)
   GEMM_MAINLOOP(s0, s1);
@@ -699,7 +809,7 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
 
 namespace qn {
 
-template <int BM, int BN, bool BWD>
+template <int BM, int BN, bool BWD, bool CHK>
 void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                    const uint16_t* La_hi, const uint16_t* La_lo,
                    const uint16_t* Lb, int M, int rpad, void* out,
@@ -710,10 +820,10 @@ void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
   const unsigned grid = sp.rem == 0 ? tiles : (unsigned)(sp.whole + 2 * sp.rem);
   if constexpr (BWD) {
     if (drop != nullptr) {
-      QN_LAUNCH("k_bwd_dx_gemm", (k_gemm<BM, BN, BWD, true, false>), dim3(grid),
-                dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
-                w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
-                qn::codebook(), *drop, sp);
+      QN_LAUNCH("k_bwd_dx_gemm", (k_gemm<BM, BN, BWD, true, false, CHK>),
+                dim3(grid), dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed,
+                w->qabs, w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out,
+                out_bf16, qn::codebook(), *drop, sp);
       return;
     }
   }
@@ -721,17 +831,33 @@ void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
   if (sp.rem > 0) {
     if constexpr (BM == 256) {
       QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm",
-                (k_gemm<BM, BN, BWD, false, true>), dim3(grid),
+                (k_gemm<BM, BN, BWD, false, true, CHK>), dim3(grid),
                 dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
                 w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
                 qn::codebook(), none, sp);
       return;
     }
   }
-  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm", (k_gemm<BM, BN, BWD, false, false>),
-            dim3(grid), dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed,
-            w->qabs, w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
+  QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm",
+            (k_gemm<BM, BN, BWD, false, false, CHK>), dim3(grid),
+            dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
+            w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
             qn::codebook(), none, sp);
+}
+
+// Checked per-step addressing only where the reduction can end in a partial
+// step: the backward (reduction over N) when N % 64 != 0.
+template <int BM, int BN, bool BWD>
+void launch_gemm_c(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
+                   const uint16_t* La_hi, const uint16_t* La_lo,
+                   const uint16_t* Lb, int M, int rpad, void* out,
+                   int out_bf16, const DropArgs* drop, const SplitArgs& sp) {
+  if (BWD && w->rows % G_BK != 0)
+    launch_gemm_t<BM, BN, BWD, true>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
+                                     out_bf16, drop, sp);
+  else
+    launch_gemm_t<BM, BN, BWD, false>(st, Aop, w, La_hi, La_lo, Lb, M, rpad,
+                                      out, out_bf16, drop, sp);
 }
 
 template <bool BWD>
@@ -752,10 +878,10 @@ void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                      reinterpret_cast<int32_t*>(base)};
   }
   if (gemm_big_tiles(M, nout))
-    launch_gemm_t<256, 256, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
+    launch_gemm_c<256, 256, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
                                  out_bf16, drop, sa);
   else
-    launch_gemm_t<128, 128, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
+    launch_gemm_c<128, 128, BWD>(st, Aop, w, La_hi, La_lo, Lb, M, rpad, out,
                                  out_bf16, drop, sa);
 }
 
