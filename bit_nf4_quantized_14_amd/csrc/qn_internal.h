@@ -72,14 +72,20 @@ enum { RS_ROWS = 1, RS_COLS = 2 };
 
 // RM rows per workgroup, stages of 64 SUB columns, NBUF LDS buffers (NBUF - 1
 // stages in flight): about 32 KB of S per stage for r <= 32, less for the
-// wider adapters whose R and U tiles take more LDS.
+// wider adapters whose R and U tiles take more LDS.  The passes with column
+// sums write one fp32 partial [C][rpad] per RM rows, so they keep RM = 256
+// up to r = 64 (with two buffers at r = 64: 64 KB of S, 16 KB of R and
+// 67.6 KB of U).
 constexpr int rs_rm(int mode, int jt) {
-  return mode == RS_ROWS ? 64 : (jt <= 2 ? 256 : 64);
+  return mode == RS_ROWS ? 64 : (jt <= 4 ? 256 : 64);
 }
 constexpr int rs_sub(int mode, int jt) {
-  return jt >= 8 ? 1 : (jt == 4 ? 2 : (mode == RS_ROWS ? 4 : 1));
+  return jt >= 8 ? 1
+                 : (jt == 4 ? (mode == RS_ROWS ? 2 : 1) : (mode == RS_ROWS ? 4 : 1));
 }
-constexpr int rs_nbuf(int jt) { return jt >= 16 ? 2 : 3; }
+constexpr int rs_nbuf(int mode, int jt) {
+  return jt >= 16 || (jt == 4 && mode != RS_ROWS) ? 2 : 3;
+}
 
 struct StreamPlan {
   int rm, sub, mb, nb, cpb;   // rows per block, stage width (x64), row

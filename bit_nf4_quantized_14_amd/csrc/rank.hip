@@ -122,7 +122,7 @@ struct RsCfg {
   static constexpr bool ROWS = (MODE & RS_ROWS) != 0;
   static constexpr bool COLS = (MODE & RS_COLS) != 0;
   static constexpr int RM = rs_rm(MODE, JT), SUB = rs_sub(MODE, JT);
-  static constexpr int NBUF = rs_nbuf(JT);
+  static constexpr int NBUF = rs_nbuf(MODE, JT);
   static constexpr int RP = 16 * JT, PU = RM + 8, TR = RM / 64;
   static constexpr int S_BYTES = SUB * RM * 128;
   static constexpr int R_BYTES = ROWS ? SUB * RP * 128 : 16;

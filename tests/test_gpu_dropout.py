@@ -83,6 +83,7 @@ def test_tiny_workload_with_dropout(p):
     (8, 200, 320, 5, 3.0, 0.1),        # would be skinny without dropout
     (16, 64, 4160, 33, 64.0, 0.05),    # skinny-sized M, long K
     (130, 136, 320, 64, 16.0, 0.3),    # r = 64
+    (300, 264, 256, 64, 16.0, 0.1),    # r = 64 over two 256-row blocks
     (64, 128, 256, 256, 512.0, 0.1),   # maximum rank
     (257, 1024, 576, 16, 32.0, 0.05),  # M past a split
     (1024, 1024, 4096, 16, 32.0, 0.05),  # 256-wide GEMM tiles

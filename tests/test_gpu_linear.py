@@ -92,6 +92,8 @@ def test_tiny_workload_bf16_outputs():
     (1, 8, 64, 1, 1.0),          # smallest legal problem
     (130, 136, 320, 64, 16.0),   # r = 64, N and M just past a tile
     (300, 264, 128, 17, 3.0),    # rank just past a 16-wide tile
+    (300, 264, 256, 48, 3.0),    # r = 48: two 256-row blocks of the rank
+                                 # streams, the second ragged
     (64, 128, 256, 256, 512.0),  # maximum rank
     (257, 1024, 576, 16, 32.0),  # M spans two split-M chunks
     (8, 200, 320, 5, 3.0),       # skinny path: N % 16 != 0, K % 256 != 0
