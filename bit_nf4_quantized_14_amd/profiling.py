@@ -72,10 +72,12 @@ def _find(root: str, suffix: str) -> list[str]:
 
 
 def short_name(name: str) -> str:
-    """Kernel name without the anonymous-namespace prefix and argument
-    list: ``(anonymous namespace)::k_gemm<256, 256, ...>(...)`` ->
-    ``k_gemm<256, 256, ...>``."""
-    n = name.split("(anonymous namespace)::")[-1]
+    """Kernel name without the return type, the anonymous-namespace prefixes
+    and the argument list: ``void (anonymous namespace)::k_gemm<256, 256,
+    ...>(...)`` -> ``k_gemm<256, 256, ...>``."""
+    n = name.replace("(anonymous namespace)::", "").strip()
+    if n.startswith("void "):
+        n = n[5:]
     depth = 0
     for i, ch in enumerate(n):
         if ch == "<":
@@ -84,7 +86,7 @@ def short_name(name: str) -> str:
             depth -= 1
         elif ch == "(" and depth == 0:
             return n[:i].strip()
-    return n.strip()
+    return n
 
 
 def kernel_stats(root: str) -> list[dict]:
