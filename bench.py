@@ -439,20 +439,44 @@ def bench_70b(reps, do_train=True):
     def skinny():
         for pr in probs:
             pr.fwd()
-    sec = timed_graph(skinny, reps)
-    kp, _ = kernel_times_ms(capi, "k_skinny_partial", skinny, len(probs), reps)
-    kr, _ = kernel_times_ms(capi, "k_skinny_reduce", skinny, len(probs), reps)
-    ksum = (kp + kr) * len(probs) * 1e-3
+    # the same seven projections as one qlora_linear_fwd_batch call (one
+    # partial and one reduce launch for the whole layer)
+    batch = capi.FwdBatch([(pr.x, pr.w, pr.a, pr.b, pr.r, pr.alpha, pr.y,
+                            capi.QN_F32, pr.t) for pr in probs])
+
+    def skinny_batch():
+        capi.qlora_linear_fwd_batch(batch)
+    sec = timed_graph(skinny_batch, reps)
+    sec_calls = timed_graph(skinny, reps)
+    kp, _ = kernel_times_ms(capi, "k_skinny_partial", skinny_batch, 1, reps)
+    kr, _ = kernel_times_ms(capi, "k_skinny_reduce", skinny_batch, 1, reps)
+    kp1, _ = kernel_times_ms(capi, "k_skinny_partial", skinny, len(probs), reps)
+    kr1, _ = kernel_times_ms(capi, "k_skinny_reduce", skinny, len(probs), reps)
+    ksum = (kp + kr) * 1e-3
+    per = {}
+    for pr, (name, _, _) in zip(probs, wk.projections):
+        npk = pr.w.packed.numel() + pr.w.qabs.numel() + 4 * pr.w.gscale.numel()
+        b1 = npk + 2 * pr.r * (pr.n + pr.k) + 2 * pr.m * pr.k + 4 * pr.m * pr.n
+        s1 = timed_graph(pr.fwd, reps)
+        per[name] = {"bytes": b1, "ms": s1 * 1e3, "GB/s": b1 / s1 / 1e9}
     res["skinny70b"] = {"bytes_per_pass": nbytes, "ms_per_pass": sec * 1e3,
                         "GB/s": nbytes / sec / 1e9,
-                        "timing": "graph replay of the 7-projection pass",
+                        "timing": "graph replay of the 7-projection pass as one "
+                                  "qlora_linear_fwd_batch call",
                         "frac_hbm_peak": nbytes / sec / 1e9 / HBM_PEAK_GBS,
                         "kernel_ms_per_pass": ksum * 1e3,
-                        "k_skinny_partial_avg_ms": kp, "k_skinny_reduce_avg_ms": kr,
-                        "kernel_GB/s": nbytes / ksum / 1e9}
-    log(f"skinny70b: {res['skinny70b']['GB/s']:.0f} GB/s graph, "
+                        "k_skinny_partial_ms": kp, "k_skinny_reduce_ms": kr,
+                        "kernel_GB/s": nbytes / ksum / 1e9,
+                        "per_call_pass_ms": sec_calls * 1e3,
+                        "per_call_pass_GB/s": nbytes / sec_calls / 1e9,
+                        "per_call_partial_avg_ms": kp1,
+                        "per_call_reduce_avg_ms": kr1,
+                        "per_projection_single_call": per}
+    log(f"skinny70b: {res['skinny70b']['GB/s']:.0f} GB/s batched (graph), "
         f"{res['skinny70b']['kernel_GB/s']:.0f} GB/s kernels "
-        f"(partial {kp*1e3:.1f} us, reduce {kr*1e3:.1f} us avg)")
+        f"(partial {kp*1e3:.1f} us, reduce {kr*1e3:.1f} us); "
+        f"7 single calls {res['skinny70b']['per_call_pass_GB/s']:.0f} GB/s")
+    del batch
     del probs
     torch.cuda.empty_cache()
     if not do_train:

@@ -34,7 +34,9 @@ EXPORTS = ("nf4_codebook", "nf4_quantize", "nf4_dequantize",
            "qn_adamw8_step", "qn_adamw8_staging_bytes", "qn_adamw8_paged_step",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
            "qlora_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd",
-           "qn_strerror", "qn_profile_kernel", "qlora_linear_fwd_noalloc")
+           "qn_strerror", "qn_profile_kernel", "qlora_linear_fwd_noalloc",
+           "qlora_fwd_batch_workspace_bytes", "qlora_linear_fwd_batch")
+QN_FWD_BATCH_MAX = 8
 QN_DEQUANT_BATCH_MAX = 16
 QN_CODE_NF4, QN_CODE_FP4, QN_CODE_INT4 = 0, 1, 2
 QN_CONST_DQ8, QN_CONST_FP32, QN_CONST_CENTERED = 0, 1, 2
@@ -65,6 +67,14 @@ class _AdamHP(ctypes.Structure):
 class _Adam8State(ctypes.Structure):
     _fields_ = [("m_codes", ctypes.c_void_p), ("m_scale", ctypes.c_void_p),
                 ("r_codes", ctypes.c_void_p), ("r_scale", ctypes.c_void_p)]
+
+
+class _FwdJob(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("w", ctypes.POINTER(_NF4Struct)), ("A", ctypes.c_void_p),
+                ("B", ctypes.c_void_p), ("r", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("y", ctypes.c_void_p),
+                ("y_dtype", ctypes.c_int32), ("t_save", ctypes.c_void_p)]
 
 
 class _Dropout(ctypes.Structure):
@@ -149,6 +159,11 @@ def lib() -> ctypes.CDLL:
                                            vp, vp, i32, vp, vp, dp, vp,
                                            ctypes.c_size_t, vp]
     L.qlora_linear_bwd_dropout.restype = ctypes.c_int
+    jp = ctypes.POINTER(_FwdJob)
+    L.qlora_fwd_batch_workspace_bytes.argtypes = [jp, i32]
+    L.qlora_fwd_batch_workspace_bytes.restype = ctypes.c_size_t
+    L.qlora_linear_fwd_batch.argtypes = [jp, i32, vp, ctypes.c_size_t, vp]
+    L.qlora_linear_fwd_batch.restype = ctypes.c_int
     L.qlora_linear_fwd_noalloc.argtypes = [vp, i64, sp, vp, vp, i32, f32, vp,
                                            i32, vp, vp]
     L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
@@ -442,6 +457,46 @@ def qlora_linear_fwd(x, w: NF4Tensor, A, B, r: int, alpha: float, y=None,
         _ptr(y), y_dtype, _ptr(t_save), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
     return y, t_save
+
+
+class FwdBatch:
+    """Descriptors of a qlora_linear_fwd_batch call, kept alive with the
+    tensors they point to.  jobs: sequence of (x, w, A, B, r, alpha, y,
+    y_dtype, t_save) with y / t_save None to allocate them."""
+
+    def __init__(self, jobs):
+        import torch
+        self.keep, self.outs = [], []
+        arr = (_FwdJob * len(jobs))()
+        for i, (x, w, A, B, r, alpha, y, y_dtype, t_save) in enumerate(jobs):
+            M = x.shape[0]
+            if y is None:
+                y = torch.empty((M, w.rows), device=x.device,
+                                dtype=torch.float32 if y_dtype == QN_F32
+                                else torch.bfloat16)
+            if t_save is None:
+                t_save = torch.empty((M, r), device=x.device, dtype=torch.float32)
+            st = w.as_struct()
+            self.keep += [x, A, B, y, t_save, st]
+            self.outs.append((y, t_save))
+            arr[i] = _FwdJob(_ptr(x), M, ctypes.pointer(st), _ptr(A), _ptr(B), r,
+                             float(alpha), _ptr(y), y_dtype, _ptr(t_save))
+        self.arr, self.count = arr, len(jobs)
+        self.ws_bytes = lib().qlora_fwd_batch_workspace_bytes(arr, self.count)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8,
+                              device=jobs[0][0].device)
+
+
+def qlora_fwd_batch_workspace_bytes(batch: FwdBatch) -> int:
+    return int(lib().qlora_fwd_batch_workspace_bytes(batch.arr, batch.count))
+
+
+def qlora_linear_fwd_batch(batch: FwdBatch, stream=None):
+    """Batched skinny forward (every job M <= 16); returns [(y, t_save)]."""
+    _check("qlora_linear_fwd_batch", lib().qlora_linear_fwd_batch(
+        batch.arr, batch.count, _ptr(batch.ws),
+        batch.ws.numel() * batch.ws.element_size(), _stream(stream)))
+    return batch.outs
 
 
 def qlora_linear_fwd_noalloc(x, w: NF4Tensor, A, B, r: int, alpha: float,

@@ -136,8 +136,10 @@ int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K;
   hipStream_t st = (hipStream_t)stream;
   if (M <= qn::QN_SKINNY_M && !use_drop && drop == nullptr) {
-    launch_skinny(st, x, Mi, w, A, B, (int)r, L.rpad, s, t_save, y,
-                  (int)(y_dtype == QN_BF16), ws_at<float>(ws, L.part));
+    const SkinnyJob job{x, Mi, w, A, B, (int)r, s, t_save, y,
+                        (int)(y_dtype == QN_BF16)};
+    const SkinnyPlan plan = skinny_plan(M, N, K, r);
+    launch_skinny(st, &job, 1, &plan, ws_at<char>(ws, L.part));
     return check_launch();
   }
   uint16_t* Th = ws_at<uint16_t>(ws, L.th);
@@ -284,6 +286,57 @@ int qlora_linear_bwd_dropout(const uint16_t* dy, const uint16_t* x,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Batched skinny forward: up to QN_FWD_BATCH_MAX projections with M <= 16
+// in one launch pair.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Validates the jobs (each as qlora_linear_fwd would, and M <= 16) and
+// fills the internal jobs and plans; returns the workspace bytes, or 0.
+size_t fwd_batch_plan(const qlora_fwd_job* jobs, int32_t count,
+                      SkinnyJob* out, SkinnyPlan* plans) {
+  if (jobs == nullptr || count < 1 || count > QN_FWD_BATCH_MAX) return 0;
+  for (int i = 0; i < count; ++i) {
+    const qlora_fwd_job& J = jobs[i];
+    if (J.x == nullptr || J.A == nullptr || J.B == nullptr || J.y == nullptr ||
+        J.t_save == nullptr)
+      return 0;
+    if (!valid_linear(J.M, J.w, J.r) || J.M > QN_SKINNY_M) return 0;
+    if (J.y_dtype != QN_F32 && J.y_dtype != QN_BF16) return 0;
+    if (!aligned16(J.x) || !aligned16(J.A) || !aligned16(J.y) ||
+        !aligned16(J.t_save))
+      return 0;
+    out[i] = SkinnyJob{J.x, (int)J.M, J.w, J.A, J.B, J.r,
+                       J.alpha / (float)J.r, J.t_save, J.y,
+                       (int)(J.y_dtype == QN_BF16)};
+  }
+  skinny_plan_batch(out, count, plans);
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) total += align256(skinny_part_bytes(out[i].M, plans[i]));
+  return total;
+}
+
+}  // namespace
+
+extern "C" size_t qlora_fwd_batch_workspace_bytes(const qlora_fwd_job* jobs,
+                                                  int32_t count) {
+  SkinnyJob sj[QN_FWD_BATCH_MAX];
+  SkinnyPlan sp[QN_FWD_BATCH_MAX];
+  return fwd_batch_plan(jobs, count, sj, sp);
+}
+
+extern "C" int qlora_linear_fwd_batch(const qlora_fwd_job* jobs, int32_t count,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  SkinnyJob sj[QN_FWD_BATCH_MAX];
+  SkinnyPlan sp[QN_FWD_BATCH_MAX];
+  const size_t need = fwd_batch_plan(jobs, count, sj, sp);
+  if (need == 0) return QN_EINVAL;
+  if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return QN_EWORKSPACE;
+  launch_skinny((hipStream_t)stream, sj, count, sp, static_cast<char*>(ws));
+  return check_launch();
+}
 
 // ---------------------------------------------------------------------------
 // Allocation-free forward: the workspace is a file-scope device array, one

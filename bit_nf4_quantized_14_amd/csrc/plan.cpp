@@ -3,6 +3,7 @@
 // blocking, the skinny path's K slices, and the workspace layouts.  Plain
 // C++ with no HIP dependency, so the plans can be checked on the host.
 #include <algorithm>
+#include <vector>
 
 #include "qn_internal.h"
 
@@ -75,29 +76,68 @@ StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt) {
 }
 
 
-// Skinny path plan: K slices of ks columns (multiple of 256, short enough
-// that the X slice leaves LDS room for two workgroups per CU), and enough
-// slices for ~2 items per workgroup.  The grid is two workgroups per CU
-// whatever the item count; the items are split so that the CUs' shares
-// differ by at most one item (skinny_items).
-constexpr int64_t SK_LDS_PER_WG = 64 * 1024;   // X tile budget (bytes)
+// Skinny path plan (the rule is stated where SkinnyPlan is declared).
+// X tile budget (bytes); with two workgroups per CU the X tiles take at most
+// 128 KB of a CU's 160 KB of LDS.
+constexpr int64_t SK_LDS_PER_WG = 64 * 1024;
 
-SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r) {
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r,
+                       int64_t want_tiles) {
   SkinnyPlan P;
-  P.rows_total = (int)(((N + 15) & ~15LL) + 16 * rank_tiles(r));
-  P.wg_rows = (int)cdiv(P.rows_total, SK_ROWS);
+  P.wtiles = (int)cdiv(N, 16);
+  P.tps = P.wtiles + rank_tiles(r);
+  P.rows_total = 16 * P.tps;
   const int64_t kchunks = cdiv(K, 256);
-  // longest slice whose X tile ((M + 1) rows, zero row included) leaves room
-  // for two workgroups per CU, and enough slices for ~2 items per workgroup
   int64_t ks_max = (SK_LDS_PER_WG / (2 * (M + 1)) - 8) / 256 * 256;
   ks_max = std::max<int64_t>(256, std::min<int64_t>(ks_max, SK_KS_MAX));
-  int64_t slices = std::max<int64_t>(cdiv(K, ks_max),
-                                     cdiv((int64_t)G_CUS * SK_WGS_PER_CU * 2, P.wg_rows));
+  const int64_t grid_waves = int64_t(SK_WAVES) * SK_WGS_PER_CU * G_CUS;
+  const int64_t fewest = cdiv(K, ks_max);
+  const int64_t want = cdiv(std::max<int64_t>(want_tiles, 1), P.tps);
+  const int64_t cap = std::max(K / (cdiv(128 * M, 256) * 256), cdiv(grid_waves, P.tps));
+  int64_t slices = std::max(fewest, std::min(want, cap));
   slices = std::min<int64_t>(slices, kchunks);
   const int64_t ks = cdiv(kchunks, slices) * 256;
   P.ks = (int)ks;
   P.slices = (int)cdiv(K, ks);
   return P;
+}
+
+void skinny_plan_batch(const SkinnyJob* jobs, int count, SkinnyPlan* out) {
+  double total = 0;
+  for (int i = 0; i < count; ++i)
+    total += double(jobs[i].w->rows) * double(jobs[i].w->cols);
+  for (int i = 0; i < count; ++i) {
+    const double share = double(jobs[i].w->rows) * double(jobs[i].w->cols) / total;
+    const int64_t want = (int64_t)(share * SK_BATCH_TILES + 0.999);
+    out[i] = skinny_plan(jobs[i].M, jobs[i].w->rows, jobs[i].w->cols, jobs[i].r, want);
+  }
+}
+
+int skinny_bounds(const SkinnyPlan* plans, const int64_t* K, int count,
+                  int nslots, int32_t* bound) {
+  std::vector<int64_t> tile0(count + 1, 0), cost0(count + 1, 0);
+  for (int i = 0; i < count; ++i) {
+    tile0[i + 1] = tile0[i] + int64_t(plans[i].tps) * plans[i].slices;
+    cost0[i + 1] = cost0[i] + int64_t(plans[i].tps) * cdiv(K[i], 256);
+  }
+  const int64_t T = cost0[count];
+  // first tile whose cost starts at or after x
+  auto first_tile = [&](int64_t x) -> int64_t {
+    if (x >= T) return tile0[count];
+    int p = 0;
+    while (p + 1 < count && cost0[p + 1] <= x) ++p;
+    const SkinnyPlan& P = plans[p];
+    const int64_t kc = P.ks / 256, kchunks = cdiv(K[p], 256);
+    const int64_t full = int64_t(P.tps) * kc;              // cost of a slice
+    const int64_t local = x - cost0[p];
+    const int64_t s = std::min<int64_t>(local / full, P.slices - 1);
+    const int64_t c = s < P.slices - 1 ? kc : kchunks - (P.slices - 1) * kc;
+    const int64_t t = cdiv(local - s * full, c);
+    return tile0[p] + s * P.tps + std::min<int64_t>(t, P.tps);
+  };
+  for (int c = 0; c <= nslots; ++c)
+    bound[c] = (int32_t)first_tile(c * T / nslots);
+  return (int)tile0[count];
 }
 
 FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
@@ -109,7 +149,7 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
     L.slices = P.slices;
     L.ks = P.ks;
     L.part = 0;
-    L.total = align256(size_t(P.slices) * M * P.rows_total * 4);
+    L.total = align256(skinny_part_bytes(M, P));
     return L;
   }
   const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r));

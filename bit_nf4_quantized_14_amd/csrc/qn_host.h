@@ -131,10 +131,10 @@ struct FinishArgs {
 FinishArgs finish_args();
 void launch_finish(hipStream_t st, FinishArgs& a);
 
-// ---- skinny.hip: forward for M <= 16 tokens.
-void launch_skinny(hipStream_t st, const uint16_t* x, int M,
-                   const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
-                   int r, int rpad, float s, float* t_save, void* y,
-                   int y_bf16, float* part);
+// ---- skinny.hip: forward for M <= 16 tokens, a batch of up to
+// QN_FWD_BATCH_MAX projections in one launch pair; ws holds each
+// projection's partial sums (skinny_part_bytes, 256-byte aligned, in order).
+void launch_skinny(hipStream_t st, const SkinnyJob* jobs, int count,
+                   const SkinnyPlan* plans, char* ws);
 
 }  // namespace qn

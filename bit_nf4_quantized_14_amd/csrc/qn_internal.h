@@ -96,13 +96,54 @@ StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt);
 // ---- skinny forward (skinny.hip), M <= QN_SKINNY_M tokens.
 constexpr int64_t QN_SKINNY_M = 16;
 constexpr int SK_WAVES = 8;                  // waves per workgroup
-constexpr int SK_ROWS = 16 * SK_WAVES;       // rows per workgroup
 constexpr int SK_KS_MAX = 4096;              // longest K slice
 constexpr int SK_WGS_PER_CU = 2;             // resident workgroups per CU
+// tiles (16 rows x one K slice, one wave's work item) a call aims for:
+// about 4 per wave of the grid
+constexpr int SK_TARGET_TILES = 4 * SK_WAVES * SK_WGS_PER_CU * G_CUS;
 struct SkinnyPlan {
-  int slices, ks, rows_total, wg_rows;
+  int slices, ks;
+  int wtiles;       // tiles of weight rows per slice, cdiv(N, 16)
+  int tps;          // tiles per slice: wtiles, then rpad / 16 adapter tiles
+  int rows_total;   // 16 tps: rows of the partial sums
 };
-SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r);
+// One projection of a skinny (batched) forward.
+struct SkinnyJob {
+  const uint16_t* x;
+  int M;
+  const nf4_tensor* w;
+  const uint16_t* A;
+  const uint16_t* B;
+  int r;
+  float s;
+  float* t_save;
+  void* y;
+  int y_bf16;
+};
+// K slices of one projection: at least enough that the X slice ((M + 1)
+// rows, the zero row included) leaves LDS room for SK_WGS_PER_CU
+// workgroups per CU; more, up to about want_tiles tiles, as long as a slice
+// keeps >= 128 M columns (the fp32 partial sums then add at most 1/8 of the
+// packed weight bytes) or the projection has fewer tiles than the grid has
+// waves.
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int r,
+                       int64_t want_tiles = SK_TARGET_TILES);
+// Plans of a batch: each projection asks for its share (by weight count) of
+// SK_BATCH_TILES tiles.
+constexpr int SK_BATCH_TILES = 2 * SK_TARGET_TILES;
+void skinny_plan_batch(const SkinnyJob* jobs, int count, SkinnyPlan* out);
+// fp32 partial sums [slices][M][rows_total] of one projection
+inline size_t skinny_part_bytes(int64_t M, const SkinnyPlan& P) {
+  return size_t(P.slices) * size_t(M) * size_t(P.rows_total) * 4;
+}
+// Tiles of a batch, numbered projection by projection, slice-major inside a
+// projection; the cost of a tile is the number of 256-column chunks of its
+// slice.  bound[c] (c = 0 .. nslots) is the first tile whose cost starts at
+// or after floor(c T / nslots), T the batch's total cost, so slot c owns
+// tiles [bound[c], bound[c + 1]) and every slot's cost is within one tile of
+// T / nslots.  Returns the tile count.
+int skinny_bounds(const SkinnyPlan* plans, const int64_t* K, int count,
+                  int nslots, int32_t* bound);
 
 // Workspace layouts of the fused calls (byte offsets, 256-byte aligned).
 // rpad = r rounded up to 16, 32, 64, 128 or 256 (the adapter MFMA width).

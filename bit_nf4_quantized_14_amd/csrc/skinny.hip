@@ -1,7 +1,9 @@
 // Skinny forward of the QLoRA linear layer (M <= 16 tokens): an HBM-bound
 // GEMV over the NF4 weight with the adapter's T = X A^T in the same pass
 // ("QLoRA Guide", Forward pass diagram; "QLORA ... paper summary", Notes:
-// dequantize to BF16, multiply).
+// dequantize to BF16, multiply).  One launch pair serves a batch of up to
+// QN_FWD_BATCH_MAX projections (qlora_linear_fwd_batch; a single
+// qlora_linear_fwd with M <= 16 is a batch of one).
 #include "qn_host.h"
 
 namespace {
@@ -9,38 +11,83 @@ namespace {
 using namespace qn;
 
 // ---------------------------------------------------------------------------
-// K6: skinny forward (M <= 16 tokens): HBM-bound GEMV over the NF4 weight.
+// K6: skinny forward, partial sums.
 //
-// Workgroup = 8 waves; wave w owns 16 consecutive "rows" of the weight-like
-// operand: rows [0, N) are the NF4 weight W, rows [N, N + rpad) are the
-// adapter's A (bf16), so T = X A^T comes out of the same pass.  Grid.y
-// splits K into slices of KS columns; the workgroup stages its X slice
-// (M rows, zero above M) in LDS once.  Per 256-column chunk, lane
-// (n = l % 16, g = l / 16) loads the 32 packed bytes of block g of row n,
-// builds that block's 16-entry bf16 LUT and decodes 8 weights per
-// v_mfma_f32_16x16x32_bf16 step (t = 0..7 takes weights 8t..8t+7 of the
-// block); the matching A operand is X[m][64 g + 8 t ...] from LDS.  The
-// next chunk's weight bytes are loaded before the current chunk is decoded.
-// A persistent workgroup takes a contiguous run of work items ordered
-// slice-major, so its X slice stays in LDS across the row blocks of one
-// slice.  Partial sums go to part[slice][m][row] (fp32, m < M), combined by
-// k_skinny_reduce.
+// Tiles: 16 rows of one projection x one K slice of KS columns, numbered
+// projection by projection and, inside a projection, slice-major, one list
+// for the whole batch.  Rows [0, N) of a projection are its NF4 weight W;
+// its adapter A (bf16) takes rows [Nw, Nw + rpad), Nw = N rounded up to 16,
+// so T comes out of the same pass; a tile holds weight rows or adapter rows,
+// never both, and a slice's adapter tiles follow its weight tiles.
+//
+// The grid is SK_WGS_PER_CU = 2 workgroups of SK_WAVES = 8 waves per CU.
+// CU slot c owns a run of the list whose cost (in 256-column chunks) is
+// within one tile of an equal share (the host computes the runs); its two
+// workgroups split the run in halves, and inside a workgroup's half wave w
+// takes every eighth tile, starting with tile w.  Wherever the half changes
+// projection or slice, the workgroup stages that slice of X in LDS (M rows,
+// then an all-zero row M), each 8-element group permuted into the order
+// decode8p produces.
+//
+// A wave's weight tiles of one slice are one stream, chunk by chunk (256
+// columns): lane (n = l % 16, g = l / 16) loads the 32 packed bytes of
+// block g of row n, builds that block's 16-entry bf16 table and decodes 8
+// weights per v_mfma_f32_16x16x32_bf16 (t = 0..7 takes weights 8t..8t+7 of
+// the block); the matching A operand is X[m][64 g + 8 t ...] from LDS.  The
+// loads run two chunks ahead of the decode through three register sets,
+// also across tile boundaries, and a chunk's eight MFMAs alternate between
+// two accumulators.  Partial sums go to part[slice][m][row] (fp32, m < M).
 // ---------------------------------------------------------------------------
 
-// Items [ib, ie) of this workgroup.  The grid is two workgroups per CU;
-// workgroups b and b + gridDim.x / 2 (the same XCD, typically the same CU)
-// split one CU's share of the items, and the CU shares differ by at most
-// one item.
-__device__ __forceinline__ void skinny_items(int nitems, int& ib, int& ie) {
-  const int per = gridDim.x / 2;                 // CU slots
-  const int b = blockIdx.x;
-  const int c = b % per, h = b / per;
-  const int cb = (int)((int64_t)c * nitems / per);
-  const int ce = (int)((int64_t)(c + 1) * nitems / per);
-  const int mid = cb + (ce - cb + 1) / 2;
-  ib = h == 0 ? cb : mid;
-  ie = h == 0 ? mid : ce;
-}
+static_assert(SK_WGS_PER_CU == 2, "two workgroups per CU slot");
+
+struct SkProj {
+  const uint16_t* X;
+  const uint8_t* packed;
+  const uint8_t* qabs;
+  const float* gscale;
+  const uint16_t* A;
+  float* part;
+  int M, N, K, r, KS, wtiles, tps, tile0;
+};
+
+// bound[c]: first tile of CU slot c (skinny_bounds); slot c is served by
+// workgroups c and c + G_CUS.  wave_steps: the batch's chunk steps per wave
+// of the grid (total cost / waves), the yardstick of a wave's progress.
+struct SkArgs {
+  SkProj p[QN_FWD_BATCH_MAX];
+  int nproj, wave_steps;
+  int bound[G_CUS + 1];
+};
+
+// Issue priority by progress.  A SIMD's waves share its VALU, and at equal
+// priority the oldest wave issues first; left alone, the older workgroup's
+// waves run ahead and the younger ones finish the kernel by themselves,
+// with too few waves to cover the memory latency.  Each wave therefore
+// starts at priority 3 and steps down at 1/4, 1/2 and 3/4 of wave_steps
+// chunk steps, so that the waves behind issue first and the waves of a
+// SIMD stay within about a quarter of their work of each other.
+struct SkPrio {
+  int done = 0, band = 0, next = 0, quarter = 1;
+  __device__ void start(int wave_steps) {
+    quarter = max(1, wave_steps / 4);
+    next = quarter;
+    __builtin_amdgcn_s_setprio(3);
+  }
+  __device__ void advance(int steps) {
+    done += steps;
+    if (done >= next && band < 3) {
+      ++band;
+      next += quarter;
+      if (band == 1)
+        __builtin_amdgcn_s_setprio(2);
+      else if (band == 2)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
+  }
+};
 
 struct SkRegs {
   u32x4 w0, w1;
@@ -48,129 +95,261 @@ struct SkRegs {
   float d;
 };
 
-__global__ __launch_bounds__(512) void k_skinny_partial(
-    const uint16_t* __restrict__ X, int M, const uint8_t* __restrict__ packed,
-    const uint8_t* __restrict__ qabs, const float* __restrict__ gscale,
-    const uint16_t* __restrict__ A, int N, int K, int r, int rpad, int KS,
-    int wg_rows, int nitems, float* __restrict__ part, Codebook cb) {
-  // rows [0, N) weight, [N, Np16) zero padding, [Np16, Np16 + rpad) adapter
-  const int Np16 = (N + 15) & ~15;
-  const int rows_total = Np16 + rpad;
-  const int XP = KS + 8;                       // sX pitch (bf16)
-  extern __shared__ __attribute__((aligned(16))) uint16_t sX[];   // (M+1) x XP
+// The projection and K slice that a segment of tiles shares (uniform values,
+// copied from the kernel arguments once per segment).
+struct SkRun {
+  int M, N, K, KS, r, Nw, rows_total, k0, klen, slice;
+  const uint16_t* X;
+  const uint16_t* A;
+  float* part;
+  rsrc_t rp, rq, rd;
+};
+
+__device__ __forceinline__ void sk_run_of(const SkArgs& a, int p, int slice,
+                                          SkRun& R) {
+  const SkProj& P = a.p[p];
+  R.M = P.M;
+  R.N = P.N;
+  R.K = P.K;
+  R.KS = P.KS;
+  R.r = P.r;
+  R.Nw = 16 * P.wtiles;
+  R.rows_total = 16 * P.tps;
+  R.slice = slice;
+  R.k0 = slice * P.KS;
+  R.klen = min(P.KS, P.K - R.k0);
+  R.X = P.X;
+  R.A = P.A;
+  R.part = P.part;
+  const int64_t numel = (int64_t)P.N * P.K;
+  R.rp = make_rsrc(P.packed, (uint32_t)((numel + 1) >> 1));
+  R.rq = make_rsrc(P.qabs, (uint32_t)((numel + 63) >> 6));
+  R.rd = make_rsrc(P.gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
+}
+
+// X slice of the run -> LDS (M rows, columns >= klen zero, then the
+// all-zero row M), each 8-element group permuted into the order decode8p
+// produces.
+__device__ __forceinline__ void sk_stage_x(const SkRun& R, uint16_t* sX,
+                                           int tid) {
+  const int M = R.M, K = R.K, KS = R.KS, XP = KS + 8;
+  const rsrc_t rx = make_rsrc(R.X, (uint32_t)((int64_t)M * K * 2));
+  for (int c = tid; c < KS / 8; c += 512)
+    *reinterpret_cast<u32x4*>(sX + M * XP + 8 * c) = u32x4{0u, 0u, 0u, 0u};
+  const int groups = M * (KS / 8);
+  // batches of 4 loads per thread, all issued before their LDS writes
+  for (int i0 = 0; i0 < groups; i0 += 4 * 512) {
+    u32x4 xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = i0 + tid + 512 * i;
+      const int m = idx / (KS / 8), c = 8 * (idx % (KS / 8));
+      const bool ok = idx < groups && c < R.klen;
+      xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rx, ok ? (uint32_t)(((int64_t)m * K + R.k0 + c) * 2) : G_OOB, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = i0 + tid + 512 * i;
+      if (idx < groups) {
+        const int m = idx / (KS / 8), c = 8 * (idx % (KS / 8));
+        *reinterpret_cast<u32x4*>(sX + m * XP + c) = permute8(xv[i]);
+      }
+    }
+  }
+}
+
+// The eight A operands (X[m][64 g + 8 t ...], t = 0..7) of a chunk; lanes
+// whose row is >= M read the all-zero row M.
+__device__ __forceinline__ void sk_read_x(const SkRun& R, const uint16_t* sX,
+                                          int n, int g, int kc, u32x4 (&xa)[8]) {
+  const uint16_t* xrow = sX + (n < R.M ? n : R.M) * (R.KS + 8) + 64 * g + kc;
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8)
+    xa[s8] = *reinterpret_cast<const u32x4*>(xrow + 8 * s8);
+}
+
+// acc[v] = C[m = 4 g + v][row] -> part[slice][m][row] for the lanes whose
+// token m is < M (the others address past the range and are dropped).
+__device__ __forceinline__ void sk_store(const SkRun& R, int row, int g,
+                                         const f32x4& acc) {
+  const rsrc_t rpt = make_rsrc(
+      R.part, (uint32_t)((int64_t)(R.slice + 1) * R.M * R.rows_total * 4));
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = 4 * g + v;
+    const uint32_t off =
+        m < R.M ? (uint32_t)((((int64_t)R.slice * R.M + m) * R.rows_total + row) * 4)
+                : G_OOB;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v]), rpt, off, 0, 0);
+  }
+}
+
+// Weight bytes, block code and group scale of the lane's block whose first
+// element is 64 qb (qb = element index / 64, so the packed bytes start at
+// 32 qb, the code at qb and the group scale at 4 (qb / 256)).  `skip`
+// (qb = ~0) addresses past every range: the block's constant loads as 0,
+// which makes all 64 weights +-0.  `oob` (0 or G_OOB) drops the packed
+// loads of positions past the run.  Rows past N address past the ranges by
+// themselves.  Every step of the stream issues these same four loads, so
+// the wait before a chunk's decode leaves the next two chunks in flight.
+__device__ __forceinline__ void sk_load(const SkRun& R, uint32_t qb, bool skip,
+                                        uint32_t oob, SkRegs& W) {
+  const uint32_t qm = skip ? ~0u : qb;
+  const uint32_t op = (qb << 5) | oob;
+  W.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.rp, op, 0, 0));
+  W.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.rp, op, 16, 0));
+  W.q = __builtin_amdgcn_raw_buffer_load_b8(R.rq, qm, 0, 0);
+  W.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+      R.rd, (qm >> 6) & ~3u, 0, 0));
+}
+
+__device__ __forceinline__ void sk_decode_chunk(const u32x4 (&xa)[8],
+                                                const SkRegs& W,
+                                                const Codebook& cb, f32x4& acc0,
+                                                f32x4& acc1) {
+  const Lut t = make_lut(cb, static_cast<float>(W.q) * W.d);
+  const uint32_t wd[8] = {W.w0.x, W.w0.y, W.w0.z, W.w0.w,
+                          W.w1.x, W.w1.y, W.w1.z, W.w1.w};
+#pragma unroll
+  for (int s8 = 0; s8 < 8; s8 += 2) {
+    acc0 = mfma16(xa[s8], decode8p(wd[s8], t), acc0);
+    acc1 = mfma16(xa[s8 + 1], decode8p(wd[s8 + 1], t), acc1);
+  }
+}
+
+__global__ __launch_bounds__(512) void k_skinny_partial(SkArgs args,
+                                                        Codebook cb) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t sX[];   // (M+1) x (KS+8)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int64_t numel = (int64_t)N * K;
-  const rsrc_t rp = make_rsrc(packed, (uint32_t)((numel + 1) >> 1));
-  const rsrc_t rq = make_rsrc(qabs, (uint32_t)((numel + 63) >> 6));
-  const rsrc_t rd = make_rsrc(gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
-  const rsrc_t ra = make_rsrc(A, (uint32_t)((int64_t)r * K * 2));
-  const rsrc_t rx = make_rsrc(X, (uint32_t)((int64_t)M * K * 2));
 
-  // work items (block of SK_ROWS rows, K slice), item = slice * wg_rows +
-  // row block; this workgroup takes items [ib, ie)
-  int ib, ie;
-  skinny_items(nitems, ib, ie);
-  for (int c = tid; c < KS / 8; c += 512)
-    *reinterpret_cast<u32x4*>(sX + M * XP + 8 * c) = u32x4{0u, 0u, 0u, 0u};
-  int staged = -1;                               // slice held in sX
-  for (int item = ib; item < ie; ++item) {
-    const int rb = item % wg_rows, slice = item / wg_rows;
-    const int k0 = slice * KS;
-    const int klen = min(KS, K - k0);
-    const int row0 = rb * SK_ROWS + wave * 16;   // first row of the wave
-    const int row = row0 + n;
+  // this workgroup's half of its CU slot's tiles
+  const int slot = blockIdx.x % G_CUS, half = blockIdx.x / G_CUS;
+  const int cb0 = args.bound[slot], ce0 = args.bound[slot + 1];
+  const int mid = cb0 + (ce0 - cb0 + 1) / 2;
+  const int ib = half == 0 ? cb0 : mid, ie = half == 0 ? mid : ce0;
 
-    // X slice -> LDS (M rows, columns >= klen zero), each 8-element group
-    // permuted into the order decode8p produces; loads issued before use.
-    if (slice != staged) {
-      if (staged >= 0) __syncthreads();          // sX still being read
-      staged = slice;
-      const int groups = M * (KS / 8);
-      // batches of 4 loads per thread, all issued before their LDS writes
-      for (int i0 = 0; i0 < groups; i0 += 4 * 512) {
-        u32x4 xv[4];
+  SkPrio prio;
+  prio.start(args.wave_steps);
+  int p = 0, staged_p = -1, staged_slice = -1;
+  int tile = ib;
+  while (tile < ie) {
+    // segment: the tiles of one projection and slice, [tile, seg_end)
+    while (p + 1 < args.nproj && tile >= args.p[p + 1].tile0) ++p;
+    const int tps = args.p[p].tps, wtiles = args.p[p].wtiles;
+    const int local = tile - args.p[p].tile0;
+    const int slice = local / tps, t_seg = local % tps;
+    const int seg_end = min(ie, tile + (tps - t_seg));
+    SkRun R;
+    sk_run_of(args, p, slice, R);
+    const bool restage = p != staged_p || slice != staged_slice;
+    // this wave's first tile of the segment (slice-local index): every
+    // eighth tile of the half, counted from ib
+    const int first = t_seg + ((wave - (tile - ib)) % SK_WAVES + SK_WAVES) % SK_WAVES;
+    const int t_end = t_seg + (seg_end - tile);          // slice-local end
+    const int w_end = min(t_end, wtiles);                // end of weight tiles
+    const int nw = first < w_end ? (w_end - first + SK_WAVES - 1) / SK_WAVES : 0;
+
+    // Weight tiles first, tile first + 8 i for i < nw: one stream of
+    // nw * nch chunk steps.  The lane's load address is one running block
+    // index qb, moved by a uniform step: 4 blocks to the next chunk, 128
+    // rows down and back to the slice's first chunk at a tile boundary.
+    const int nch = (R.klen + 255) / 256;          // chunks per tile
+    const int steps = nw * nch;
+    const uint32_t K64 = (uint32_t)R.K / 64;
+    const uint32_t wrap = (uint32_t)(16 * SK_WAVES) * K64 - 4u * (uint32_t)(nch - 1);
+    // On a tile's last chunk, lanes whose 64 columns lie past the slice
+    // load a zero block constant (only when the slice is not a whole number
+    // of chunks).
+    const bool tail_dead = 64 * g >= R.klen - 256 * (nch - 1);
+    uint32_t qb = (uint32_t)(first * 16 + n) * K64 + (uint32_t)(R.k0 / 64 + g);
+    int pc = 0;                                    // chunk being loaded
+    int cc = 0, ctile = first;                     // chunk being decoded
+    auto load_next = [&](int s_load, SkRegs& W) {
+      sk_load(R, qb, pc == nch - 1 && tail_dead, s_load < steps ? 0u : G_OOB, W);
+      const bool wrapped = pc == nch - 1;
+      qb += wrapped ? wrap : 4u;
+      pc = wrapped ? 0 : pc + 1;
+    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc0 = zero4, acc1 = zero4;
+    const uint16_t* xb = sX + (n < R.M ? n : R.M) * (R.KS + 8) + 64 * g;
+    auto decode_step = [&](const SkRegs& W) {
+      u32x4 xa[8];
+      const uint16_t* xr = xb + 256 * cc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int idx = i0 + tid + 512 * i;
-          const int m = idx / (KS / 8), c = 8 * (idx % (KS / 8));
-          const bool ok = idx < groups && c < klen;
-          xv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-              rx, ok ? (uint32_t)(((int64_t)m * K + k0 + c) * 2) : G_OOB, 0, 0));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int idx = i0 + tid + 512 * i;
-          if (idx < groups) {
-            const int m = idx / (KS / 8), c = 8 * (idx % (KS / 8));
-            *reinterpret_cast<u32x4*>(sX + m * XP + c) = permute8(xv[i]);
-          }
-        }
+      for (int s8 = 0; s8 < 8; ++s8)
+        xa[s8] = *reinterpret_cast<const u32x4*>(xr + 8 * s8);
+      sk_decode_chunk(xa, W, cb, acc0, acc1);
+      const bool tile_end = cc == nch - 1;
+      if (tile_end) {
+        sk_store(R, ctile * 16 + n, g, acc0 + acc1);
+        acc0 = zero4;
+        acc1 = zero4;
       }
+      ctile += tile_end ? SK_WAVES : 0;
+      cc = tile_end ? 0 : cc + 1;
+    };
+    // Three steps per iteration, the register sets rotating; the number of
+    // vector memory instructions between a chunk's loads and its decode is
+    // the same on every path through the loop, so the waits keep two chunks
+    // in flight.  The last one or two steps follow the loop.
+    SkRegs W0, W1, W2;
+    // (the scheduler must not interleave the two chunks' loads: the waits in
+    // the loop count on W0's loads being issued before W1's)
+    load_next(0, W0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_next(1, W1);
+    __builtin_amdgcn_sched_barrier(0);
+    // the first two chunks are in flight while the X slice is staged
+    if (restage) {
+      if (staged_p >= 0) __syncthreads();        // sX still being read
+      staged_p = p;
+      staged_slice = slice;
+      sk_stage_x(R, sX, tid);
       __syncthreads();
     }
+    int s0 = 0;
+    for (; s0 + 3 <= steps; s0 += 3) {
+      prio.advance(3);
+      load_next(s0 + 2, W2);
+      decode_step(W0);
+      load_next(s0 + 3, W0);
+      decode_step(W1);
+      load_next(s0 + 4, W1);
+      decode_step(W2);
+    }
+    if (s0 < steps) decode_step(W0);
+    if (s0 + 1 < steps) decode_step(W1);
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (row0 < rows_total) {
-      const bool is_w = row0 < Np16;             // wave-uniform
-      // lanes whose A-operand row is >= M read the all-zero row M of sX
-      const uint16_t* xrow = sX + (n < M ? n : M) * XP + 64 * g;
-      auto load = [&](SkRegs& R, int kc) {
-        const int k = k0 + kc + 64 * g;
-        const int64_t e = (int64_t)row * K + k;
-        const bool okw = is_w && kc + 64 * g < klen && row < N;
-        const uint32_t op = okw ? (uint32_t)(e >> 1) : G_OOB;
-        R.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op, 0, 0));
-        R.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, op + 16, 0, 0));
-        R.q = __builtin_amdgcn_raw_buffer_load_b8(rq, okw ? (uint32_t)(e >> 6) : G_OOB, 0, 0);
-        R.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-            rd, okw ? (uint32_t)((e >> 14) << 2) : G_OOB, 0, 0));
-      };
-      auto chunk = [&](const SkRegs& R, int kc) {
-        u32x4 a[8];
+    // Adapter tiles (T = X A^T, A bf16): the wave's tiles at or past
+    // wtiles, plain loads of A, chunk by chunk.
+    const rsrc_t ra = make_rsrc(R.A, (uint32_t)((int64_t)R.r * R.K * 2));
+    for (int t = first + nw * SK_WAVES; t < t_end; t += SK_WAVES) {
+      const int j = (t - wtiles) * 16 + n;
+      f32x4 a0 = zero4, a1 = zero4;
+      for (int kc = 0; kc < R.klen; kc += 256) {
+        u32x4 xa[8];
+        sk_read_x(R, sX, n, g, kc, xa);
+        const int k = R.k0 + kc + 64 * g;
+        const bool ok = kc + 64 * g < R.klen && j < R.r;
+        const uint32_t o = ok ? (uint32_t)(((int64_t)j * R.K + k) * 2) : G_OOB;
+        u32x4 b[8];
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8)
-          a[s8] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * s8);
-        if (is_w) {
-          const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
-          const uint32_t wd[8] = {R.w0.x, R.w0.y, R.w0.z, R.w0.w,
-                                  R.w1.x, R.w1.y, R.w1.z, R.w1.w};
+          b[s8] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+              ra, o, 16 * s8, 0));
 #pragma unroll
-          for (int s8 = 0; s8 < 8; ++s8) acc = mfma16(a[s8], decode8p(wd[s8], t), acc);
-        } else {
-          const int j = row - Np16;
-          const int k = k0 + kc + 64 * g;
-          const bool ok = kc + 64 * g < klen && j < r;
-#pragma unroll
-          for (int s8 = 0; s8 < 8; ++s8) {
-            const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                ra, ok ? (uint32_t)(((int64_t)j * K + k + 8 * s8) * 2) : G_OOB, 0, 0));
-            acc = mfma16(a[s8], permute8(b), acc);
-          }
+        for (int s8 = 0; s8 < 8; s8 += 2) {
+          a0 = mfma16(xa[s8], permute8(b[s8]), a0);
+          a1 = mfma16(xa[s8 + 1], permute8(b[s8 + 1]), a1);
         }
-      };
-      // two register sets, loaded one chunk ahead, no copies between them
-      // (the loop is VALU-bound on the decode; deeper prefetch measured no
-      // faster)
-      SkRegs ra0, ra1;
-      load(ra0, 0);
-      for (int kc = 0; kc < klen; kc += 512) {
-        load(ra1, kc + 256);
-        chunk(ra0, kc);
-        if (kc + 256 >= klen) break;
-        load(ra0, kc + 512);
-        chunk(ra1, kc + 256);
       }
+      sk_store(R, R.Nw + j, g, a0 + a1);
     }
-    // acc[v] = C[m = 4 g + v][row n]
-    if (row < rows_total) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * g + v;
-        if (m < M) part[((int64_t)slice * M + m) * rows_total + row] = acc[v];
-      }
-    }
+    tile = seg_end;
   }
 }
 
@@ -190,36 +369,62 @@ __device__ __forceinline__ float sum_slices(const float* __restrict__ p,
   return acc;
 }
 
-// Y[m][n] = sum_slices part[.][m][n] + s * sum_j T[m][j] B[n][j], and
-// T[m][j] = sum_slices part[.][m][Np16 + j] (written to t_save by the
-// blocks with blockIdx.x == 0).  Workgroup (bx, by) covers columns
-// [64 bx, 64 bx + 64) of tokens [4 by, 4 by + 4), one output per thread.
-__global__ __launch_bounds__(256) void k_skinny_reduce(
-    const float* __restrict__ part, int slices, int M, int N, int r, int rpad,
-    const uint16_t* __restrict__ B, float s, float* __restrict__ t_save,
-    void* __restrict__ Y, int y_bf16) {
+// ---------------------------------------------------------------------------
+// Reduce: Y[m][n] = sum_slices part[.][m][n] + s * sum_j T[m][j] B[n][j],
+// and T[m][j] = sum_slices part[.][m][Nw + j] (written to t_save by the
+// blocks of the first column block).  The blocks of all projections form one
+// grid; block b of projection p covers columns [64 bx, 64 bx + 64) of tokens
+// [4 by, 4 by + 4), one output per thread.
+// ---------------------------------------------------------------------------
+struct SkRProj {
+  const float* part;
+  const uint16_t* B;
+  float* t_save;
+  void* Y;
+  float s;
+  int slices, M, N, r, rpad, y_bf16, blk0;
+};
+
+struct SkRArgs {
+  SkRProj p[QN_FWD_BATCH_MAX];
+  int nproj;
+};
+
+__global__ __launch_bounds__(256) void k_skinny_reduce(SkRArgs args) {
   __shared__ float sT[4 * QN_MAX_RANK];
-  const int Np16 = (N + 15) & ~15;
-  const int64_t rows_total = Np16 + rpad;
+  int p = 0;
+  while (p + 1 < args.nproj && (int)blockIdx.x >= args.p[p + 1].blk0) ++p;
+  const SkRProj& P = args.p[p];
+  const int M = P.M, N = P.N, r = P.r;
+  const int Nw = (N + 15) / 16 * 16;
+  const int64_t rows_total = Nw + P.rpad;
   const int64_t stride = (int64_t)M * rows_total;      // between slices
-  const int mb = 4 * blockIdx.y;
+  const int nbx = (N + 63) / 64;
+  const int local = blockIdx.x - P.blk0;
+  const int bx = local % nbx, by = local / nbx;
+  const int mb = 4 * by;
   const int mrows = min(4, M - mb);
+  const int n = bx * 64 + (threadIdx.x & 63);
+  const int mi = threadIdx.x >> 6;
+  const bool live = n < N && mi < mrows;
+  const int m = mb + mi;
+  // this thread's weight partials first: their loads are in flight while T
+  // is summed
+  const float y =
+      live ? sum_slices(P.part + (int64_t)m * rows_total + n, stride, P.slices) : 0.f;
   for (int idx = threadIdx.x; idx < mrows * r; idx += 256) {
     const int m = mb + idx / r, j = idx % r;
-    const float v = sum_slices(part + (int64_t)m * rows_total + Np16 + j, stride, slices);
+    const float v = sum_slices(P.part + (int64_t)m * rows_total + Nw + j, stride,
+                               P.slices);
     sT[idx] = v;
-    if (blockIdx.x == 0) t_save[(int64_t)m * r + j] = v;
+    if (bx == 0) P.t_save[(int64_t)m * r + j] = v;
   }
   __syncthreads();
-  const int n = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int mi = threadIdx.x >> 6;
-  if (n >= N || mi >= mrows) return;
-  const int m = mb + mi;
-  const float y = sum_slices(part + (int64_t)m * rows_total + n, stride, slices);
+  if (!live) return;
   const float* t = sT + mi * r;
-  const uint16_t* b = B + (int64_t)n * r;
+  const uint16_t* b = P.B + (int64_t)n * r;
   float lora = 0.f;
-  if ((r & 7) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0) {
+  if ((r & 7) == 0 && (reinterpret_cast<uintptr_t>(P.B) & 15) == 0) {
     // 16-byte aligned rows of B: 8 weights per load
     for (int j0 = 0; j0 < r; j0 += 8) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(b + j0);
@@ -233,30 +438,46 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(
   } else {
     for (int jj = 0; jj < r; ++jj) lora += t[jj] * bf16_to_f32(b[jj]);
   }
-  store_out(Y, y_bf16, (int64_t)m * N + n, y + s * lora);
+  store_out(P.Y, P.y_bf16, (int64_t)m * N + n, y + P.s * lora);
 }
 
 }  // namespace
 
 namespace qn {
 
-void launch_skinny(hipStream_t st, const uint16_t* x, int M,
-                   const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
-                   int r, int rpad, float s, float* t_save, void* y,
-                   int y_bf16, float* part) {
-  const int64_t N = w->rows, K = w->cols;
-  const SkinnyPlan P = skinny_plan(M, N, K, r);
-  const int nitems = P.wg_rows * P.slices;
-  const size_t shm = size_t(M + 1) * (P.ks + 8) * 2;
+void launch_skinny(hipStream_t st, const SkinnyJob* jobs, int count,
+                   const SkinnyPlan* plans, char* ws) {
+  static_assert(sizeof(SkArgs) + sizeof(Codebook) <= 4096, "kernel arguments");
+  SkArgs a{};
+  SkRArgs ra{};
+  a.nproj = ra.nproj = count;
+  int64_t K[QN_FWD_BATCH_MAX];
+  int tiles = 0, blocks = 0;
+  size_t shm = 16, off = 0;                 // X tile bytes, partials offset
+  for (int i = 0; i < count; ++i) {
+    const SkinnyJob& J = jobs[i];
+    const SkinnyPlan& P = plans[i];
+    float* part = reinterpret_cast<float*>(ws + off);
+    off += align256(skinny_part_bytes(J.M, P));
+    a.p[i] = SkProj{J.x, J.w->packed, J.w->qabs, J.w->gscale, J.A, part,
+                    J.M, (int)J.w->rows, (int)J.w->cols, J.r,
+                    P.ks, P.wtiles, P.tps, tiles};
+    tiles += P.tps * P.slices;
+    K[i] = J.w->cols;
+    shm = std::max(shm, size_t(J.M + 1) * (P.ks + 8) * 2);
+    ra.p[i] = SkRProj{part, J.B, J.t_save, J.y, J.s, P.slices, J.M,
+                      (int)J.w->rows, J.r, 16 * rank_tiles(J.r), J.y_bf16, blocks};
+    blocks += (int)(cdiv(J.w->rows, 64) * cdiv(J.M, 4));
+  }
+  skinny_bounds(plans, K, count, G_CUS, a.bound);
+  int64_t cost = 0;
+  for (int i = 0; i < count; ++i) cost += int64_t(plans[i].tps) * cdiv(K[i], 256);
+  a.wave_steps = (int)(cost / (G_CUS * SK_WGS_PER_CU * SK_WAVES));
   QN_LAUNCH_SHM("k_skinny_partial", k_skinny_partial,
-                dim3((unsigned)(G_CUS * SK_WGS_PER_CU)),
-                dim3(512), shm, st, x, M, w->packed, w->qabs, w->gscale, A,
-                (int)N, (int)K, r, rpad, P.ks, P.wg_rows, nitems, part,
+                dim3((unsigned)(G_CUS * SK_WGS_PER_CU)), dim3(512), shm, st, a,
                 qn::codebook());
-  QN_LAUNCH("k_skinny_reduce", k_skinny_reduce,
-            dim3((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 4)), dim3(256), st,
-            part, P.slices, M,
-            (int)N, r, rpad, B, s, t_save, y, y_bf16);
+  QN_LAUNCH("k_skinny_reduce", k_skinny_reduce, dim3((unsigned)blocks),
+            dim3(256), st, ra);
 }
 
 }  // namespace qn

@@ -440,6 +440,54 @@ int qlora_linear_bwd_dropout(const uint16_t* dy, const uint16_t* x,
                              size_t ws_bytes, void* stream);
 
 /*
+ * qlora_linear_fwd_batch -- qlora_linear_fwd for up to QN_FWD_BATCH_MAX
+ * projections with few tokens (M <= 16 each), as one pair of launches
+ * (device).
+ *
+ * "QLoRA Guide", How QLoRA Works / Forward pass, for each job: T = X A^T
+ * (fp32, to t_save) and Y = X W'^T + (alpha / r) T B^T; decoding through a
+ * QLoRA model runs every projection of a layer at a handful of tokens,
+ * where the pass is bound by streaming the 4-bit weights.  The kernels are
+ * those of qlora_linear_fwd at M <= 16; the split of each reduction into K
+ * slices (and with it the order of the fp32 sums) is chosen for the whole
+ * batch, so a job agrees with its single call up to fp32 rounding, and a
+ * batch of one gives qlora_linear_fwd's bits.  Jobs are independent: each has its
+ * own x, weight, adapters and outputs, and no output may overlap another
+ * job's inputs or outputs.  The work of all jobs is dealt to the CUs as one
+ * list, so small projections (the k / v of grouped-query attention) do
+ * not leave the GPU idle and a layer costs two launches, not two per
+ * projection.
+ * jobs : host array of `count` descriptors (1 <= count <= QN_FWD_BATCH_MAX),
+ *        fields as the qlora_linear_fwd arguments of the same names;
+ *        1 <= M <= 16 for every job.
+ * ws   : device workspace, ws_bytes >= qlora_fwd_batch_workspace_bytes(jobs,
+ *        count) (fp32 K-slice partial sums of every job), 16-byte aligned.
+ * Errors: QN_EINVAL (a job qlora_linear_fwd would reject, M > 16, count out
+ * of range), QN_EWORKSPACE, QN_EHIP.
+ */
+#define QN_FWD_BATCH_MAX 8
+
+typedef struct {
+  const uint16_t* x;      /* device bf16 [M, K] */
+  int64_t M;              /* 1 .. 16 */
+  const nf4_tensor* w;    /* host descriptor: rows = N, cols = K */
+  const uint16_t* A;      /* device bf16 [r, K] */
+  const uint16_t* B;      /* device bf16 [N, r] */
+  int32_t r;
+  float alpha;
+  void* y;                /* device [M, N] of y_dtype */
+  int32_t y_dtype;        /* QN_F32 or QN_BF16 */
+  float* t_save;          /* device fp32 [M, r] */
+} qlora_fwd_job;
+
+/* Workspace for qlora_linear_fwd_batch (host); 0 for an invalid batch. */
+size_t qlora_fwd_batch_workspace_bytes(const qlora_fwd_job* jobs,
+                                       int32_t count);
+
+int qlora_linear_fwd_batch(const qlora_fwd_job* jobs, int32_t count,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * qlora_linear_fwd_noalloc -- qlora_linear_fwd without a workspace argument
  * (device), for callers that cannot allocate device memory: code being
  * captured into a HIP graph, tight serving loops, harnesses that forbid

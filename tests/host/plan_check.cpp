@@ -12,6 +12,9 @@
 //   split area at offset 0.
 // * stream_plan and skinny_plan cover every row and column, and the skinny X
 //   slice fits its LDS budget.
+// * skinny_bounds: the slots' tile runs are contiguous, cover every tile, and
+//   each slot starts at the first tile whose cost starts at or after its
+//   share of the total (checked against a walk over every tile).
 #include <cstdio>
 #include <vector>
 
@@ -115,7 +118,9 @@ static void layouts() {
           check((long long)P.slices * P.ks >= K && (long long)(P.slices - 1) * P.ks < K,
                 "skinny slices cover K", M, N, K);
           check((M + 1) * (P.ks + 8) * 2 <= 64 * 1024, "skinny X tile fits LDS", M, N, K);
-          check(P.rows_total >= N + r && (long long)P.wg_rows * SK_ROWS >= P.rows_total,
+          check(P.wtiles * 16 >= N && P.wtiles * 16 < N + 16 &&
+                    P.tps == P.wtiles + rank_tiles(r) && P.rows_total == 16 * P.tps &&
+                    P.rows_total >= N + r,
                 "skinny rows", M, N, K);
           check(f.total >= size_t(P.slices) * M * P.rows_total * 4, "skinny partials",
                 M, N, K);
@@ -157,6 +162,69 @@ static void layouts() {
     }
 }
 
+static void skinny_bounds_sweep() {
+  // batches: single projections and the seven projections of two layers
+  const long long shapes[][3] = {{8, 1024, 8192},  {8, 8192, 8192},   {8, 28672, 8192},
+                                 {8, 8192, 28672}, {16, 4096, 11008}, {1, 8, 64},
+                                 {3, 136, 192},    {16, 264, 4160},   {5, 11008, 4096}};
+  std::vector<std::vector<int>> batches;
+  for (int i = 0; i < 9; ++i) batches.push_back({i});
+  batches.push_back({1, 0, 0, 1, 2, 2, 3});
+  batches.push_back({4, 4, 4, 4, 4, 4, 4, 5});
+  batches.push_back({5, 6, 7, 8});
+  const int ranks[] = {1, 16, 64, 256};
+  for (auto& b : batches)
+    for (int r : ranks) {
+      const int n = (int)b.size();
+      std::vector<SkinnyPlan> P(n);
+      std::vector<int64_t> K(n);
+      std::vector<nf4_tensor> w(n);
+      std::vector<SkinnyJob> J(n);
+      for (int i = 0; i < n; ++i) {
+        const long long* sh = shapes[b[i]];
+        w[i].rows = sh[1];
+        w[i].cols = sh[2];
+        J[i] = SkinnyJob{nullptr, (int)sh[0], &w[i], nullptr, nullptr, r, 1.f,
+                         nullptr, nullptr, 0};
+        K[i] = sh[2];
+      }
+      if (n == 1)
+        P[0] = skinny_plan(J[0].M, w[0].rows, w[0].cols, r);
+      else
+        skinny_plan_batch(J.data(), n, P.data());
+      // every tile's cost start, by walking the list
+      std::vector<int64_t> start;
+      int64_t T = 0;
+      for (int i = 0; i < n; ++i) {
+        const int64_t kch = cdiv(K[i], 256), kc = P[i].ks / 256;
+        for (int s = 0; s < P[i].slices; ++s) {
+          const int64_t c = s < P[i].slices - 1 ? kc : kch - (P[i].slices - 1) * kc;
+          check(c >= 1 && c <= kc, "slice chunks", b[i], s, c);
+          for (int t = 0; t < P[i].tps; ++t) {
+            start.push_back(T);
+            T += c;
+          }
+        }
+      }
+      std::vector<int32_t> bound(G_CUS + 1);
+      const int tiles = skinny_bounds(P.data(), K.data(), n, G_CUS, bound.data());
+      check(tiles == (int)start.size(), "tile count", tiles, (long long)start.size());
+      check(bound[0] == 0 && bound[G_CUS] == tiles, "bounds cover the tiles", bound[0],
+            bound[G_CUS], tiles);
+      for (int c = 0; c <= G_CUS; ++c) {
+        const int64_t x = int64_t(c) * T / G_CUS;
+        int64_t want = (int64_t)start.size();
+        for (size_t i = 0; i < start.size(); ++i)
+          if (start[i] >= x) {
+            want = (int64_t)i;
+            break;
+          }
+        check(bound[c] == want, "slot bound", c, bound[c], want);
+        if (c > 0) check(bound[c] >= bound[c - 1], "bounds not monotone", c);
+      }
+    }
+}
+
 static void shape_rules() {
   nf4_tensor w{reinterpret_cast<uint8_t*>(0x1000), reinterpret_cast<uint8_t*>(0x2000),
                reinterpret_cast<float*>(0x3000), 256, 512};
@@ -181,6 +249,7 @@ static void shape_rules() {
 int main() {
   split_plan_sweep();
   layouts();
+  skinny_bounds_sweep();
   shape_rules();
   if (!bad) std::printf("ok\n");
   return bad;

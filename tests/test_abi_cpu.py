@@ -257,3 +257,28 @@ def test_noalloc_forward_rejects_shapes_beyond_its_scratch():
                                       p, capi.QN_F32, p, None) == capi.QN_EWORKSPACE
     assert L.qlora_linear_fwd_noalloc(p, 16, ctypes.byref(st), p, p, 0, 1.0,
                                       p, capi.QN_F32, p, None) == capi.QN_EINVAL
+
+
+def test_fwd_batch_validation():
+    """qlora_linear_fwd_batch rejects, before any launch: an empty or
+    oversized batch, a job with M > 16, a job qlora_linear_fwd would reject;
+    and asks for at least the workspace it reports."""
+    L = capi.lib()
+    p = 0x10000
+    st = _fake_tensor(256, 512)
+
+    def job(M=8, r=8, y_dtype=capi.QN_F32, x=p, w=None):
+        return capi._FwdJob(x, M, ctypes.pointer(w or st), p, p, r, 16.0, p,
+                            y_dtype, p)
+    one = (capi._FwdJob * 1)(job())
+    need = L.qlora_fwd_batch_workspace_bytes(one, 1)
+    assert need > 0
+    assert L.qlora_linear_fwd_batch(one, 1, p, need - 16, None) == capi.QN_EWORKSPACE
+    assert L.qlora_linear_fwd_batch(one, 0, p, need, None) == capi.QN_EINVAL
+    nine = (capi._FwdJob * 9)(*[job() for _ in range(9)])
+    assert L.qlora_linear_fwd_batch(nine, 9, p, 1 << 30, None) == capi.QN_EINVAL
+    for bad in (job(M=17), job(M=0), job(r=0), job(r=257), job(y_dtype=7),
+                job(x=p + 2), job(w=_fake_tensor(256, 500))):
+        arr = (capi._FwdJob * 2)(job(), bad)
+        assert L.qlora_fwd_batch_workspace_bytes(arr, 2) == 0
+        assert L.qlora_linear_fwd_batch(arr, 2, p, 1 << 30, None) == capi.QN_EINVAL
