@@ -416,11 +416,12 @@ __device__ __forceinline__ int gemm_xcd_index(int pid, int nwhole) {
   return (nwhole & 7) == 0 ? (pid & 7) * (nwhole >> 3) + (pid >> 3) : pid;
 }
 
-// Kernel-side view of a GemmSplit: workgroups [0, whole) take whole tiles,
-// [whole, whole + rem) the first piece of split tile b - whole (reduction
-// steps [ks, end)), [whole + rem, whole + 2 rem) its second piece ([0, ks)).
+// Kernel-side view of a GemmSplit: workgroups [0, whole) take whole tiles;
+// workgroup whole + i rem + t is piece i (0 or 1) of split tile t, over
+// reduction steps [0, h) or [h, nsteps), h = nsteps / 2 rounded down to
+// even (the pieces of a tile lie on one XCD when rem is a multiple of 8).
 struct SplitArgs {
-  int whole, rem, ks;
+  int whole, rem;
   float* part;       // [rem][TM TN 4][NT] float4: one partial tile each
   uint32_t* cnt;     // [rem][2]: arrivals, partial-ready flag
   int32_t* status;   // QN_ESYNC when a partial never became ready
@@ -570,6 +571,62 @@ __device__ __forceinline__ void gemm_drop_acc(
     }
 }
 
+// The exchange of split tile t.  Returns false for the piece that arrives
+// first (its partial is stored and the flag raised: the workgroup exits);
+// true for the second, with rpart set to the partial to add (a zero-sized
+// range, and acc NaN, if the partial never became ready).
+template <int BM, int BN, bool BWD>
+__device__ __forceinline__ bool gemm_split_exchange(
+    const SplitArgs& sp, int t, int tid,
+    f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN],
+    rsrc_t& rpart) {
+  using C = GemmCfg<BM, BN, BWD>;
+  __shared__ uint32_t s_arrived, s_ready;
+  uint32_t* cnt = sp.cnt + 2 * t;
+  rpart = make_rsrc(sp.part + (int64_t)t * BM * BN, (uint32_t)(BM * BN * 4));
+  if (tid == 0)
+    s_arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_arrived == 0) {
+    gemm_put_partial<BM, BN, BWD>(rpart, tid, acc);
+    __syncthreads();   // every wave's stores precede the release below
+    if (tid == 0)
+      __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  // The other piece is past its arrival and only has stores left, so this
+  // wait is short; the bound only guards against a hang.
+  if (tid == 0) {
+    int it = 0;
+    while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               0u &&
+           ++it < G_SPLIT_SPIN)
+      __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_ready = it < G_SPLIT_SPIN;
+    if (it >= G_SPLIT_SPIN)
+      __hip_atomic_store(sp.status, (int32_t)QN_ESYNC, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    // back to zero for the next launch (a kernel boundary orders these
+    // stores before it)
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (s_ready == 0) {
+    // an unready partial is never added: the tile becomes NaN
+    rpart = make_rsrc(sp.part, 0u);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
+  }
+  return true;
+}
+
 // SPLIT: the grid holds split pieces (SplitArgs); without it the kernel
 // has none of their code.
 template <int BM, int BN, bool BWD, bool DROP, bool SPLIT, bool CHK>
@@ -601,11 +658,12 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
                  tiles_m, tiles_n, tm, tn);
   } else {
     const int q = blockIdx.x - sp.whole;
-    const bool first = q < sp.rem;
-    split = first ? q : q - sp.rem;
+    const bool second = q >= sp.rem;
+    split = second ? q - sp.rem : q;
     gemm_tile_at(sp.whole + split, tiles_m, tiles_n, tm, tn);
-    s0 = first ? sp.ks : 0;
-    s1 = first ? nsteps : sp.ks;
+    const int h = (nsteps / 2) & ~1;
+    s0 = second ? h : 0;
+    s1 = second ? nsteps : h;
   }
   const int m0 = tm * BM, c0 = tn * BN;
 
@@ -673,67 +731,21 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
   GEMM_MAINLOOP(s0, s1);
 #undef GEMM_MAINLOOP
 
-  // With SPLIT, the adapter term and the partial sum of a split tile's other
-  // piece are added by code that every tile runs, with zero-sized buffer
-  // ranges (reads return zeros, no memory traffic) where they do not apply:
-  // with one path for acc the accumulators stay in registers.  The adapter
-  // goes with the piece that starts at step 0.
+  // The adapter term goes with the piece that starts at step 0; in a split
+  // launch every tile runs its code, with a zero-sized buffer range (reads
+  // return zeros, no memory traffic) where it does not apply, so that acc has
+  // one path and stays in registers.
   if constexpr (!DROP)
     gemm_adapter<BM, BN, BWD>(La_hi, La_lo, Lb,
                               (!SPLIT || split < 0 || s0 == 0) ? M : 0, NOUT,
                               rpad, m0, c0, wm, wn, lane, acc);
 
   if constexpr (SPLIT) {
+    // Every tile runs the add (a zero-sized range where there is no partial)
+    // so that acc has one path and stays in registers.
     rsrc_t rpart = make_rsrc(sp.part, 0u);
-    if (split >= 0) {
-      // The first piece of a split tile to get here leaves its partial and
-      // exits; the second adds it and finishes the tile.
-      __shared__ uint32_t s_arrived, s_ready;
-      uint32_t* cnt = sp.cnt + 2 * split;
-      rpart = make_rsrc(sp.part + (int64_t)split * BM * BN,
-                        (uint32_t)(BM * BN * 4));
-      if (tid == 0)
-        s_arrived = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      if (s_arrived == 0) {
-        gemm_put_partial<BM, BN, BWD>(rpart, tid, acc);
-        __syncthreads();   // every wave's stores precede the release below
-        if (tid == 0)
-          __hip_atomic_store(cnt + 1, 1u, __ATOMIC_RELEASE,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        return;
-      }
-      // The other piece is past its arrival and only has stores left, so this
-      // wait is short; the bound only guards against a hang.
-      if (tid == 0) {
-        int it = 0;
-        while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT) == 0u &&
-               ++it < G_SPLIT_SPIN)
-          __builtin_amdgcn_s_sleep(2);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_ready = it < G_SPLIT_SPIN;
-        if (it >= G_SPLIT_SPIN)
-          __hip_atomic_store(sp.status, (int32_t)QN_ESYNC, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        // back to zero for the next launch (a kernel boundary orders these
-        // stores before it)
-        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
-      if (s_ready == 0) {
-        // an unready partial is never added: the tile becomes NaN
-        rpart = make_rsrc(sp.part, 0u);
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_nanf("");
-      }
-    }
+    if (split >= 0 && !gemm_split_exchange<BM, BN, BWD>(sp, split, tid, acc, rpart))
+      return;
     gemm_add_partial<BM, BN, BWD>(rpart, tid, acc);
     // Keep those loads out of the stores below: a wait for a load would also
     // wait for every store issued before it (one counter, in order).
@@ -829,14 +841,12 @@ void launch_gemm_t(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
   }
   const DropArgs none{};
   if (sp.rem > 0) {
-    if constexpr (BM == 256) {
-      QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm",
-                (k_gemm<BM, BN, BWD, false, true, CHK>), dim3(grid),
-                dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
-                w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
-                qn::codebook(), none, sp);
-      return;
-    }
+    QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm",
+              (k_gemm<BM, BN, BWD, false, true, CHK>), dim3(grid),
+              dim3(GemmCfg<BM, BN, BWD>::NT), st, Aop, w->packed, w->qabs,
+              w->gscale, La_hi, La_lo, Lb, M, N, K, rpad, out, out_bf16,
+              qn::codebook(), none, sp);
+    return;
   }
   QN_LAUNCH(BWD ? "k_bwd_dx_gemm" : "k_fwd_gemm",
             (k_gemm<BM, BN, BWD, false, false, CHK>), dim3(grid),
@@ -867,12 +877,13 @@ void launch_gemm(hipStream_t st, const uint16_t* Aop, const nf4_tensor* w,
                  int out_bf16, const DropArgs* drop, void* split_ws) {
   const int64_t nout = BWD ? w->cols : w->rows;
   const int64_t kred = BWD ? w->rows : w->cols;
-  SplitArgs sa{0, 0, 0, nullptr, nullptr, nullptr};
+  SplitArgs sa{0, 0, nullptr, nullptr, nullptr};
   if (split_ws != nullptr) {
     const GemmSplit sp = gemm_split_plan(M, nout, kred, drop != nullptr);
     char* base = static_cast<char*>(split_ws);
+    // (the plan's tile edge is the one chosen below: gemm_big_tiles decides both)
     if (sp.rem > 0)
-      sa = SplitArgs{sp.whole, sp.rem, sp.ks,
+      sa = SplitArgs{sp.whole, sp.rem,
                      reinterpret_cast<float*>(base + gemm_split_part_offset(sp)),
                      reinterpret_cast<uint32_t*>(base + G_SPLIT_HDR),
                      reinterpret_cast<int32_t*>(base)};

@@ -37,21 +37,24 @@ bool gemm_big_tiles(int64_t M, int64_t nout) {
 // that leaves CUs idle runs its tiles at a higher clock (the package is
 // power-limited), and splitting 174-176 of 256 into a 3/4 and a 1/4 piece
 // measured 3-5% slower than leaving them whole, against 6-13% faster for
-// halves of 2-90 tiles.  No split with dropout either (its adapter term is
-// masked before the main loop).
+// halves of 2-90 tiles.  A grid of 128 x 128 tiles (fewer than 192 big
+// tiles) with at most G_CUS tiles has every tile split, two such
+// workgroups fitting on a CU (the 70B k/v forward, 128 tiles: 104 -> 71 us;
+// four pieces per tile, a tree of exchanges, measured 75-78 us).  No split
+// with dropout (its adapter term is masked before the main loop), and none
+// for a reduction shorter than 8 steps.
 GemmSplit gemm_split_plan(int64_t M, int64_t nout, int64_t kred, bool drop) {
   GemmSplit sp{0, 0, 0};
-  if (drop || !gemm_big_tiles(M, nout)) return sp;
-  const int64_t tiles = cdiv(M, 256) * cdiv(nout, 256);
-  const int64_t rem = tiles % G_CUS;
-  if (rem == 0 || 2 * rem > G_CUS) return sp;
-  const int64_t nsteps = cdiv(kred, G_BK);
-  const int64_t ks = (nsteps / 2) & ~int64_t(1);
-  if (ks < 2 || nsteps - ks < 2) return sp;
-  sp.whole = (int)(tiles - rem);
-  sp.rem = (int)rem;
-  sp.ks = (int)ks;
-  return sp;
+  if (drop || cdiv(kred, G_BK) < 8) return sp;
+  if (gemm_big_tiles(M, nout)) {
+    const int64_t tiles = cdiv(M, 256) * cdiv(nout, 256);
+    const int64_t rem = tiles % G_CUS;
+    if (rem == 0 || 2 * rem > G_CUS) return sp;
+    return GemmSplit{(int)(tiles - rem), (int)rem, 256};
+  }
+  const int64_t tiles = cdiv(M, 128) * cdiv(nout, 128);
+  if (tiles > G_CUS) return sp;
+  return GemmSplit{0, (int)tiles, 128};
 }
 
 size_t gemm_split_part_offset(const GemmSplit& sp) {
@@ -59,7 +62,7 @@ size_t gemm_split_part_offset(const GemmSplit& sp) {
 }
 
 size_t gemm_split_bytes(const GemmSplit& sp) {
-  return gemm_split_part_offset(sp) + size_t(sp.rem) * 256 * 256 * 4;
+  return gemm_split_part_offset(sp) + size_t(sp.rem) * sp.tile * sp.tile * 4;
 }
 
 StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt) {

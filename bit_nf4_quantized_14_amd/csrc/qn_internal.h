@@ -47,19 +47,22 @@ constexpr int G_CUS = 256;     // MI355X compute units
 constexpr int G_BK = 64;       // reduction step
 bool gemm_big_tiles(int64_t M, int64_t nout);
 
-// Ragged last wave: when the 256 x 256 tiles leave a last wave that fills
-// at most half of the GPU, each of its tiles is computed as two pieces over
-// the two halves of the reduction (GemmSplit; no split with dropout).  The
-// first piece to finish leaves its fp32 partial tile in the split area, the
-// second adds it and stores the tile.  Split area (the first bytes of a
-// general-path workspace): int32 status word (QN_OK, or QN_ESYNC if a
-// partial never became ready), 4 bytes of padding, 2 * rem counter words,
-// then at gemm_split_part_offset rem partial tiles of 256 * 256 floats.
-// The status word and the counters must be zero at launch (the second piece
-// of each tile sets its counters back to zero).
+// Split reduction (GemmSplit; no split with dropout): a tile computed as
+// two workgroups over the two halves of the reduction.  The piece that
+// finishes first leaves its fp32 partial tile in the split area and exits,
+// the second adds it (two fp32 terms, so the result does not depend on which
+// finishes first) and stores the tile.  With 256 x 256 tiles, the tiles of
+// a ragged last wave that fills at most half of the GPU; with 128 x 128
+// tiles (a small grid), every tile of a grid of at most G_CUS tiles.  Split
+// area (the first bytes of a general-path workspace): int32 status word
+// (QN_OK, or QN_ESYNC if a partial never became ready), 4 bytes of padding,
+// 2 counter words per split tile, then at gemm_split_part_offset one partial
+// tile of tile * tile floats per split tile.  The status word and the
+// counters must be zero at launch (the second piece of each tile sets its
+// counters back to zero).
 struct GemmSplit {
-  int whole, rem, ks;   // whole tiles, split tiles, reduction steps of the
-                        // second piece (the first takes the rest)
+  int whole, rem;       // whole tiles, split tiles
+  int tile;             // tile edge of the split tiles (256 or 128)
 };
 constexpr size_t G_SPLIT_HDR = 8;   // status word + padding before the counters
 GemmSplit gemm_split_plan(int64_t M, int64_t nout, int64_t kred, bool drop);

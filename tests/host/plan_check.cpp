@@ -1,10 +1,11 @@
 // Host check of the library's planning code (csrc/plan.cpp), built with
 // address and undefined-behaviour sanitizers by tests/test_host_sanitizers.py.
 //
-// * gemm_split_plan: a split happens only for 256 x 256 tiles without
-//   dropout, when the last wave holds 1..128 tiles; whole + rem is the tile
-//   count, whole is a multiple of 256, both pieces get an even number (>= 2)
-//   of 64-wide reduction steps; known shapes give the documented plans.
+// * gemm_split_plan: no split with dropout or under 8 reduction steps; with
+//   256 x 256 tiles the tiles of a last wave of 1..128 tiles (whole + rem
+//   is the tile count, whole a multiple of 256); with 128 x 128 tiles every
+//   tile of a grid of at most 256; both pieces get an even number (>= 4) of
+//   64-wide reduction steps; known shapes give the documented plans.
 // * the split area: status word, 8-byte padding, 2 counter words per split
 //   tile, partial tiles 256-byte aligned after them.
 // * workspace layouts: every region 256-byte aligned, inside the total, no
@@ -58,30 +59,38 @@ static void split_plan_sweep() {
       for (long long k : Ks) {
         for (int drop = 0; drop < 2; ++drop) {
           const GemmSplit sp = gemm_split_plan(M, n, k, drop != 0);
-          const long long tiles = cdiv(M, 256) * cdiv(n, 256);
+          const bool big = gemm_big_tiles(M, n);
+          const long long tiles = big ? cdiv(M, 256) * cdiv(n, 256)
+                                      : cdiv(M, 128) * cdiv(n, 128);
           const long long nsteps = cdiv(k, G_BK);
           if (sp.rem == 0) {
-            check(sp.whole == 0 && sp.ks == 0, "no-split plan not empty", M, n, k);
+            check(sp.whole == 0, "no-split plan not empty", M, n, k);
             // when a split would apply it is taken
             const long long rem = tiles % G_CUS;
-            const bool could = !drop && gemm_big_tiles(M, n) && rem > 0 &&
-                               2 * rem <= G_CUS &&
-                               ((nsteps / 2) & ~1LL) >= 2 &&
-                               nsteps - ((nsteps / 2) & ~1LL) >= 2;
+            const bool could = !drop && nsteps >= 8 &&
+                               (big ? rem > 0 && 2 * rem <= G_CUS : tiles <= G_CUS);
             check(!could, "split not taken", M, n, k);
             continue;
           }
-          check(!drop, "split with dropout", M, n, k);
-          check(gemm_big_tiles(M, n), "split with small tiles", M, n, k);
-          check(sp.whole + sp.rem == tiles, "whole + rem != tiles", M, n, k);
-          check(sp.whole % G_CUS == 0, "whole not a multiple of the CUs", M, n, k);
-          check(sp.rem >= 1 && 2 * sp.rem <= G_CUS, "rem out of range", M, n, k);
-          check(sp.ks >= 2 && sp.ks % 2 == 0, "first piece steps", M, n, k);
-          check(nsteps - sp.ks >= 2, "second piece steps", M, n, k);
+          check(!drop && nsteps >= 8, "split with dropout or a short reduction", M, n, k);
+          if (big) {
+            check(sp.tile == 256, "big-tile split edge", M, n, k);
+            check(sp.whole + sp.rem == tiles, "whole + rem != tiles", M, n, k);
+            check(sp.whole % G_CUS == 0, "whole not a multiple of the CUs", M, n, k);
+            check(sp.rem >= 1 && 2 * sp.rem <= G_CUS, "rem out of range", M, n, k);
+          } else {
+            check(sp.tile == 128, "small-tile split edge", M, n, k);
+            check(sp.whole == 0 && sp.rem == tiles && tiles <= G_CUS,
+                  "small grid not split whole", M, n, k);
+          }
+          // the two pieces: [0, h) and [h, nsteps), h even, both >= 4 steps
+          const long long h = (nsteps / 2) & ~1LL;
+          check(h >= 4 && nsteps - h >= 4, "piece shorter than four steps", M, n, k);
           const size_t part = gemm_split_part_offset(sp);
           check(part % 256 == 0 && part >= G_SPLIT_HDR + 8 * size_t(sp.rem),
                 "partials overlap the counters", M, n, k);
-          check(gemm_split_bytes(sp) == part + size_t(sp.rem) * 256 * 256 * 4,
+          check(gemm_split_bytes(sp) ==
+                    part + size_t(sp.rem) * sp.tile * sp.tile * 4,
                 "split area size", M, n, k);
         }
       }
@@ -89,13 +98,16 @@ static void split_plan_sweep() {
   GemmSplit sp = gemm_split_plan(4096, 11008, 4096, false);   // 688 tiles
   check(sp.rem == 0, "gate7b forward must not split (176 left)", sp.rem);
   sp = gemm_split_plan(2048, 8448, 1024, false);              // 264 tiles
-  check(sp.whole == 256 && sp.rem == 8 && sp.ks == 8, "2048x8448x1024 plan",
-        sp.whole, sp.rem, sp.ks);
+  check(sp.whole == 256 && sp.rem == 8 && sp.tile == 256, "2048x8448x1024 plan",
+        sp.whole, sp.rem, sp.tile);
   sp = gemm_split_plan(2048, 28672, 8192, false);             // 896 tiles
-  check(sp.whole == 768 && sp.rem == 128 && sp.ks == 64, "70B gate forward plan",
-        sp.whole, sp.rem, sp.ks);
+  check(sp.whole == 768 && sp.rem == 128 && sp.tile == 256, "70B gate forward plan",
+        sp.whole, sp.rem, sp.tile);
   sp = gemm_split_plan(4096, 4096, 11008, false);             // 256 tiles
   check(sp.rem == 0, "gate7b dX must not split", sp.rem);
+  sp = gemm_split_plan(2048, 1024, 8192, false);              // 70B k/v forward
+  check(sp.whole == 0 && sp.rem == 128 && sp.tile == 128, "70B k forward plan",
+        sp.whole, sp.rem, sp.tile);
   check(gemm_split_bytes(GemmSplit{0, 0, 0}) == 256, "status word area");
 }
 
