@@ -5,15 +5,17 @@
 // Implementation Details (2025 Edition)", Step 7 (Merge & Save).  s = alpha/r
 // as in the linear layer ("QLoRA Implementation Details", Step 4).
 //
-// One workgroup per 64 x 64 tile of W (256 threads; about 30 KB of LDS, so
-// five workgroups share a CU and their phases overlap):
-//  * each thread owns 16 consecutive weights of one row (a quarter of a
-//    64-weight block): one 8-byte load of packed codes, its block code and
-//    group scale, the block's bf16 LUT and two decode8;
-//  * the rank-r product P = B_tile A_tile runs on v_mfma_f32_32x32x16_bf16:
-//    the A tile (r x 128, zero past r) and the B tile (64 x r) are staged in
-//    LDS, A read column-wise with ds_read_b64_tr_b16 (rows 16 banks apart);
-//  * P goes through LDS into row order, and each thread forms
+// Tiles of 64 x 64 weights, numbered row block by row block; each of a
+// fixed grid of workgroups (256 threads, four per CU) takes a contiguous
+// run of them and loads the codes, constants and A tile of the tile two
+// ahead into registers while it works on the current one.  Per tile:
+//  * the rank-r product runs on v_mfma_f32_32x32x16_bf16 as P^T = A^T B^T,
+//    the A tile (r x 64, zero past r) read column-wise from LDS with
+//    ds_read_b64_tr_b16, the B tile (64 x r, reloaded only when the row
+//    block changes) row-wise; lane l of wave (wn, wk) ends up with P at row
+//    32 wn + l % 32, columns 32 wk + 8 m + 4 h + 0..3 (m = 0..3, h = l / 32);
+//  * the thread dequantizes exactly those 16 weights (half of each packed
+//    dword of its row's 32-weight run, one block LUT, two decode8), forms
 //    fma(s, P, W') in fp32 and rounds to bf16 (RNE) into an LDS output
 //    tile, which is written out so that every store instruction covers
 //    whole 128-byte row runs (non-temporal stores).
@@ -26,6 +28,8 @@ namespace {
 using namespace qn;
 
 constexpr int MG_ROWS = 64, MG_COLS = 64, MG_THREADS = 256;
+constexpr int MG_WGS_PER_CU = 4;     // grid: this many workgroups per CU
+constexpr int MG_NT = 2;             // cache policy of the output stores: non-temporal
 constexpr int MG_EPT = MG_ROWS * MG_COLS / MG_THREADS;   // weights per thread
 static_assert(MG_EPT == 16, "two packed dwords per thread");
 
@@ -64,114 +68,171 @@ __device__ __forceinline__ u32x4 mg_read_colT(const uint16_t* t, int pitch,
   return v;
 }
 
+// Global loads of one tile that do not depend on the previous one: this
+// thread's 16 packed codes, its block code and group scale, and its chunks
+// of the A tile [RP][MG_COLS] (rows j < r of A [r][K], zero past r).
+// Global loads of one tile that do not depend on the previous one: the 16
+// packed bytes of this thread's row half-block (it decodes half of them),
+// its block code and group scale, and its chunks of the A tile [RP][MG_COLS]
+// (rows j < r of A [r][K], zero past r).
+template <int JT>
+struct MgLoads {
+  static constexpr int ACH = MG_COLS / 8;                 // 16-byte chunks per row
+  static constexpr int NA = (16 * JT * ACH + MG_THREADS - 1) / MG_THREADS;
+  u32x4 w;
+  uint32_t q;
+  float d;
+  u32x4 a[NA];
+};
+
 template <int JT>
 __global__ __launch_bounds__(MG_THREADS) void k_merge(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qabs,
     const float* __restrict__ gscale, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ B, int N, int K, int r, float s,
-    uint16_t* __restrict__ out, Codebook cb) {
+    const uint16_t* __restrict__ B, int N, int K, int r, float s, int tiles_k,
+    int ntiles, uint16_t* __restrict__ out, Codebook cb) {
   using G = MgCfg<JT>;
-  // the output tile reuses the A tile's storage: A is last read by the
-  // MFMAs, which every wave has finished at the barrier after the P writes
-  constexpr int AO = G::RP * G::AP > MG_ROWS * G::OP ? G::RP * G::AP
-                                                      : MG_ROWS * G::OP;
-  __shared__ __attribute__((aligned(16))) uint16_t sAO[AO];
+  using L = MgLoads<JT>;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[G::RP * G::AP];
   __shared__ __attribute__((aligned(16))) uint16_t sB[MG_ROWS * G::BP];
-  __shared__ __attribute__((aligned(16))) float sP[MG_ROWS * G::PP];
-  uint16_t* const sA = sAO;
-  uint16_t* const sO = sAO;
+  __shared__ __attribute__((aligned(16))) uint16_t sO[MG_ROWS * G::OP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wk = wave & 1;
-  const int n0 = blockIdx.x * MG_ROWS, k0 = blockIdx.y * MG_COLS;
   const int64_t numel = (int64_t)N * K;
-
-  // this thread's 16 weights: row n0 + rn, columns k0 + rc .. + 15
-  const int rn = tid >> 2, rc = MG_EPT * (tid & 3);
-  const bool mine = n0 + rn < N && k0 + rc < K;
-  const int64_t e = (int64_t)(n0 + rn) * K + k0 + rc;
   const rsrc_t rp = make_rsrc(packed, (uint32_t)((numel + 1) >> 1));
   const rsrc_t rq = make_rsrc(qabs, (uint32_t)((numel + 63) >> 6));
   const rsrc_t rd = make_rsrc(gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 wv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-      rp, mine ? (uint32_t)(e >> 1) : G_OOB, 0, 0));
-  const uint32_t qv = __builtin_amdgcn_raw_buffer_load_b8(
-      rq, mine ? (uint32_t)(e >> 6) : G_OOB, 0, 0);
-  const float dv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-      rd, mine ? (uint32_t)((e >> 14) << 2) : G_OOB, 0, 0));
-
-  // A tile [RP][MG_COLS]: rows j < r of A [r][K], zero past r and past K
   const rsrc_t ra = make_rsrc(A, (uint32_t)((int64_t)r * K * 2));
-  constexpr int ACH = MG_COLS / 8;                  // 16-byte chunks per row
-  static_assert((G::RP * ACH) % MG_THREADS == 0 || G::RP * ACH < MG_THREADS,
-                "A tile loads");
-#pragma unroll
-  for (int i0 = 0; i0 < G::RP * ACH; i0 += MG_THREADS) {
-    const int i = i0 + tid, j = i / ACH, c = 8 * (i % ACH);
-    if (j >= G::RP) break;
-    const uint32_t off = (j < r && k0 + c < K)
-                             ? (uint32_t)(((int64_t)j * K + k0 + c) * 2) : G_OOB;
-    *reinterpret_cast<u32x4*>(sA + j * G::AP + c) = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
-  }
-  // B tile [64][RP]: rows n0.. of B [N][r], zero past r and past N
-#pragma unroll
-  for (int i0 = 0; i0 < MG_ROWS * G::RP; i0 += MG_THREADS) {
-    const int i = i0 + tid, n = i / G::RP, j = i % G::RP;
-    sB[n * G::BP + j] = (n0 + n < N && j < r) ? B[(int64_t)(n0 + n) * r + j]
-                                              : (uint16_t)0;
-  }
-  __syncthreads();
+  const rsrc_t rb = make_rsrc(B, (uint32_t)((int64_t)N * r * 2));
+  // The MFMA gives lane l the products of row 32 wn + l % 32 of the tile at
+  // columns 32 wk + 8 m + 4 h + t (m, t = 0..3, h = l / 32): this thread
+  // dequantizes and writes exactly those 16 weights.
+  const int rn = 32 * wn + (lane & 31), h = lane >> 5;
+  constexpr int ACH = L::ACH;
 
-  // P = B_tile A_tile: wave (wn, wk) owns rows 32 wn .., columns 32 wk ..
-  f32x16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-#pragma unroll
-  for (int sj = 0; sj < JT; ++sj) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(
-        sB + (32 * wn + (lane & 31)) * G::BP + 16 * sj + 8 * (lane >> 5));
-    acc = mfma32(a, mg_read_colT(sA, G::AP, 16 * sj, 32 * wk, lane), acc);
-  }
-  // acc[v] = P[row 32 wn + 8 (v / 4) + 4 (l / 32) + v % 4][col 32 wk + l % 32]
-#pragma unroll
-  for (int v = 0; v < 16; ++v)
-    sP[(32 * wn + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * G::PP +
-       32 * wk + (lane & 31)] = acc[v];
-  __syncthreads();
+  // this workgroup's run of tiles
+  const int tb = (int)((int64_t)blockIdx.x * ntiles / gridDim.x);
+  const int te = (int)((int64_t)(blockIdx.x + 1) * ntiles / gridDim.x);
 
-  if (mine) {
-    const Lut lut = make_lut(cb, static_cast<float>(qv) * dv);
-    const uint32_t wd[2] = {wv.x, wv.y};
-    const float* prow = sP + rn * G::PP + rc;
+  // Loads of tile t; past the run every offset is out of range (no memory
+  // access), so each step issues the same vector memory instructions.
+  auto load = [&](L& ld, int t) {
+    const bool live = t < te;
+    const int n0 = (t / tiles_k) * MG_ROWS, k0 = (t % tiles_k) * MG_COLS;
+    const bool mine = live && n0 + rn < N;
+    // elements 32 wk .. 32 wk + 31 of the row's block
+    const int64_t e = (int64_t)(n0 + rn) * K + k0 + 32 * wk;
+    ld.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        rp, mine ? (uint32_t)(e >> 1) : G_OOB, 0, 0));
+    ld.q = __builtin_amdgcn_raw_buffer_load_b8(rq, mine ? (uint32_t)(e >> 6) : G_OOB,
+                                               0, 0);
+    ld.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        rd, mine ? (uint32_t)((e >> 14) << 2) : G_OOB, 0, 0));
+#pragma unroll
+    for (int u = 0; u < L::NA; ++u) {
+      const int i = tid + MG_THREADS * u, j = i / ACH, c = 8 * (i % ACH);
+      const uint32_t off = (live && j < r && i < G::RP * ACH)
+                               ? (uint32_t)(((int64_t)j * K + k0 + c) * 2) : G_OOB;
+      ld.a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          ra, off, 0, 0));
+    }
+  };
+
+  int b_n0 = -1;                                  // row block of the B tile in LDS
+  // Tile t from the loads in `cur`; the loads of tile t + 2 go into `ahead`.
+  auto step = [&](int t, const L& cur, L& ahead) {
+    const int n0 = (t / tiles_k) * MG_ROWS, k0 = (t % tiles_k) * MG_COLS;
+    if (n0 != b_n0) {
+      // B tile [64][RP]: rows n0.. of B [N][r], zero past r and past N
+      // (once per row block of the run)
+      b_n0 = n0;
+      constexpr int NB = MG_ROWS * G::RP / MG_THREADS;
+      uint16_t bv[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = tid + MG_THREADS * u, n = i / G::RP, j = i % G::RP;
+        bv[u] = __builtin_amdgcn_raw_buffer_load_b16(
+            rb, (n0 + n < N && j < r) ? (uint32_t)(((int64_t)(n0 + n) * r + j) * 2)
+                                      : G_OOB, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = tid + MG_THREADS * u, n = i / G::RP, j = i % G::RP;
+        sB[n * G::BP + j] = bv[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < L::NA; ++u) {
+      const int i = tid + MG_THREADS * u, j = i / ACH, c = 8 * (i % ACH);
+      if (i < G::RP * ACH) *reinterpret_cast<u32x4*>(sA + j * G::AP + c) = cur.a[u];
+    }
+    __syncthreads();   // A and B tiles written; the last tile's sO read out
+    load(ahead, t + 2);
+
+    // P^T = A_tile^T B_tile^T: acc[v] = P[row rn][col 32 wk + 8 (v / 4) +
+    // 4 h + v % 4]
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+    for (int sj = 0; sj < JT; ++sj) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(
+          sB + (32 * wn + (lane & 31)) * G::BP + 16 * sj + 8 * h);
+      acc = mfma32(mg_read_colT(sA, G::AP, 16 * sj, 32 * wk, lane), b, acc);
+    }
+
+    // codes of columns 32 wk + 8 m + 4 h .. + 3: half h of packed dword m
+    const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+    const uint32_t wd[2] = {__builtin_amdgcn_perm(cur.w.y, cur.w.x, sel),
+                            __builtin_amdgcn_perm(cur.w.w, cur.w.z, sel)};
+    const Lut lut = make_lut(cb, static_cast<float>(cur.q) * cur.d);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const u32x4 wb = decode8(wd[g], lut);    // 8 dequantized bf16 weights
+      // 8 dequantized bf16: columns 8 (2 g) + 4 h + 0..3, then 8 (2 g + 1) + ...
+      const u32x4 wb = decode8(wd[g], lut);
       const uint32_t wp[4] = {wb.x, wb.y, wb.z, wb.w};
-      u32x4 res;
+      uint32_t res[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float p0 = prow[8 * g + 2 * h], p1 = prow[8 * g + 2 * h + 1];
-        const float v0 = fmaf(s, p0, bf16_to_f32(wp[h] & 0xFFFFu));
-        const float v1 = fmaf(s, p1, bf16_to_f32(wp[h] >> 16));
-        res[h] = pack_bf16x2(v0, v1);
+      for (int i = 0; i < 4; ++i) {
+        const int v = 8 * g + 2 * i;             // acc index of the pair
+        const float v0 = fmaf(s, acc[v], bf16_to_f32(wp[i] & 0xFFFFu));
+        const float v1 = fmaf(s, acc[v + 1], bf16_to_f32(wp[i] >> 16));
+        res[i] = pack_bf16x2(v0, v1);
       }
-      *reinterpret_cast<u32x4*>(sO + rn * G::OP + rc + 8 * g) = res;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      uint16_t* o = sO + rn * G::OP + 32 * wk + 16 * g + 4 * h;
+      *reinterpret_cast<u32x2*>(o) = u32x2{res[0], res[1]};
+      *reinterpret_cast<u32x2*>(o + 8) = u32x2{res[2], res[3]};
     }
-  }
-  __syncthreads();
-  // write-out in store order: each wave instruction covers 8 rows x 128
-  // contiguous bytes (16-byte chunk q of the tile is row q / ACH, column
-  // chunk q % ACH), non-temporal
+    __syncthreads();   // the output tile is complete
+    // write-out in store order: each wave instruction covers 8 rows x 128
+    // contiguous bytes (16-byte chunk q of the tile is row q / ACH, column
+    // chunk q % ACH), non-temporal; rows past N address out of range
+    const rsrc_t ro = make_rsrc(out + (int64_t)n0 * K + k0,
+                                (uint32_t)(((int64_t)(MG_ROWS - 1) * K + MG_COLS) * 2));
 #pragma unroll
-  for (int i = 0; i < MG_ROWS * ACH / MG_THREADS; ++i) {
-    const int q = tid + MG_THREADS * i, row = q / ACH, c = 8 * (q % ACH);
-    if (n0 + row < N && k0 + c < K)
-      __builtin_nontemporal_store(
-          *reinterpret_cast<const u32x4*>(sO + row * G::OP + c),
-          reinterpret_cast<u32x4*>(out + (int64_t)(n0 + row) * K + k0 + c));
+    for (int i = 0; i < MG_ROWS * ACH / MG_THREADS; ++i) {
+      const int q = tid + MG_THREADS * i, row = q / ACH, c = 8 * (q % ACH);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          *reinterpret_cast<const u32x4*>(sO + row * G::OP + c), ro,
+          n0 + row < N ? (uint32_t)((row * K + c) * 2) : G_OOB, 0, MG_NT);
+    }
+  };
+
+  // Three register sets in rotation (no copies between them, so the waits
+  // before a tile's first use of its loads leave the next tile's in flight).
+  L L0, L1, L2;
+  load(L0, tb);
+  load(L1, tb + 1);
+  int t = tb;
+  for (; t + 3 <= te; t += 3) {
+    step(t, L0, L2);
+    step(t + 1, L1, L0);
+    step(t + 2, L2, L1);
   }
+  if (t < te) step(t, L0, L2);
+  if (t + 1 < te) step(t + 1, L1, L0);
 }
 
 }  // namespace
@@ -192,11 +253,13 @@ int nf4_merge(const nf4_tensor* w, const uint16_t* A, const uint16_t* B,
     return QN_EINVAL;
   const float s = alpha / (float)r;
   hipStream_t st = (hipStream_t)stream;
-  if (cdiv(K, MG_COLS) > 65535) return QN_EINVAL;      // grid.y limit
-  const dim3 grid((unsigned)cdiv(N, MG_ROWS), (unsigned)cdiv(K, MG_COLS));
-  QN_RANK_DISPATCH(r, QN_LAUNCH("k_merge", k_merge<JT>, grid, dim3(MG_THREADS),
+  const int64_t tiles_k = K / MG_COLS, ntiles = cdiv(N, MG_ROWS) * tiles_k;
+  if (ntiles > 0x7FFFFFFFLL) return QN_EINVAL;
+  const unsigned grid = (unsigned)std::min<int64_t>(ntiles, MG_WGS_PER_CU * G_CUS);
+  QN_RANK_DISPATCH(r, QN_LAUNCH("k_merge", k_merge<JT>, dim3(grid), dim3(MG_THREADS),
                                 st, w->packed, w->qabs, w->gscale, A, B, (int)N,
-                                (int)K, (int)r, s, w_merged, codebook()));
+                                (int)K, (int)r, s, (int)tiles_k, (int)ntiles,
+                                w_merged, codebook()));
   return check_launch();
 }
 
