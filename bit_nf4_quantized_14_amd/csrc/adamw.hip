@@ -24,7 +24,7 @@ namespace {
 using namespace qn;
 
 constexpr int AW_BLOCK = QN_ADAMW_BLOCK;     // elements per state block
-constexpr int AW_THREADS = 256;              // 4 waves, one block per wave
+constexpr int AW_THREADS = 256;              // 4 waves, 4 blocks per wave step
 constexpr float AW_E4M3_MAX = 448.0f;
 
 struct AdamConsts {
@@ -73,134 +73,256 @@ __device__ __forceinline__ Elem adam_elem(float g, float mo, float ro,
   return r;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
+// Maximum over the 16 lanes that hold one block (lanes 16 j .. 16 j + 15).
+__device__ __forceinline__ float group_max16(float x) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  for (int off = 8; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
   return x;
 }
 
-// Operands of one lane for one block: 4 gradients, 4 bf16 parameters, 4
-// codes of each moment, the block's two scales.
+// x_i / s for the 16 values of a block whose absolute maximum is amax, as
+// the correctly rounded fp32 quotient wherever it can decide an E4M3 code.
+// The block is scaled by 2^k, k = 64 - exponent(amax) (clamped to the
+// normal exponents): power-of-two scalings are exact, and then every value
+// whose quotient reaches 2^-10 (the smallest magnitude with a nonzero code)
+// is large enough that the fma residuals below stay normal.  With y the
+// correctly rounded reciprocal of the scaled divisor, q = x y refined twice
+// by r = x - q s (one fma, exact) and q + r y is RN(x / s) (Markstein's
+// correction, which holds without underflow).  Smaller quotients may differ
+// from RN in their last bit; all of them encode to code 0.  A block maximum
+// that is not finite takes the IEEE division.
+__device__ __forceinline__ void block_quot16(const float (&x)[16], float amax,
+                                             float s, float (&q)[16]) {
+#pragma clang fp contract(off)
+  if (!__builtin_isfinite(amax)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = x[i] / s;
+    return;
+  }
+  int k = 64 - __builtin_amdgcn_frexp_expf(amax);
+  k = k > 127 ? 127 : (k < -126 ? -126 : k);
+  const float sc = __builtin_ldexpf(1.0f, k);
+  const float s2 = s * sc;
+  const float y = 1.0f / s2;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = x[i] * sc;
+    const float q0 = a * y;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s2, a), y, q0);
+    q[i] = __builtin_fmaf(__builtin_fmaf(-q1, s2, a), y, q1);
+  }
+}
+
+__device__ __forceinline__ void e4m3_decode4(uint32_t w, float s, float* out) {
+  out[0] = e4m3_value<0>(w) * s;
+  out[1] = e4m3_value<1>(w) * s;
+  out[2] = e4m3_value<2>(w) * s;
+  out[3] = e4m3_value<3>(w) * s;
+}
+
+// Operands of one lane: 16 consecutive elements of one block (gradients,
+// bf16 parameters as 8 words, the codes of each moment as 4 words) and the
+// block's two scales.
 struct AwLoads {
-  float g[4];
-  uint32_t p01, p23, mc, rc;
+  f32x4 g[4];
+  u32x4 p[2];
+  u32x4 mc, rc;
   float sm, sr;
 };
 
-// One block's step for one lane; `n_here` elements of the lane's four are
-// real (4 for whole blocks).  Returns the outputs packed for storing.
 struct AwOut {
-  uint32_t p01, p23, mc, rc;
+  u32x4 p[2];
+  u32x4 mc, rc;
   float sm, sr;
 };
 
+// One block's step for the 16 lanes that hold it (16 elements per lane).
 __device__ __forceinline__ AwOut adam_block(const AwLoads& L,
                                             const AdamConsts& k) {
-  const float pv[4] = {bf16_to_f32(L.p01 & 0xFFFFu), bf16_to_f32(L.p01 >> 16),
-                       bf16_to_f32(L.p23 & 0xFFFFu), bf16_to_f32(L.p23 >> 16)};
-  const float mo[4] = {e4m3_value<0>(L.mc) * L.sm, e4m3_value<1>(L.mc) * L.sm,
-                       e4m3_value<2>(L.mc) * L.sm, e4m3_value<3>(L.mc) * L.sm};
-  const float ro[4] = {e4m3_value<0>(L.rc) * L.sr, e4m3_value<1>(L.rc) * L.sr,
-                       e4m3_value<2>(L.rc) * L.sr, e4m3_value<3>(L.rc) * L.sr};
-  Elem el[4];
+  const float g[16] = {L.g[0].x, L.g[0].y, L.g[0].z, L.g[0].w,
+                       L.g[1].x, L.g[1].y, L.g[1].z, L.g[1].w,
+                       L.g[2].x, L.g[2].y, L.g[2].z, L.g[2].w,
+                       L.g[3].x, L.g[3].y, L.g[3].z, L.g[3].w};
+  const uint32_t pw[8] = {L.p[0].x, L.p[0].y, L.p[0].z, L.p[0].w,
+                          L.p[1].x, L.p[1].y, L.p[1].z, L.p[1].w};
+  const uint32_t mw[4] = {L.mc.x, L.mc.y, L.mc.z, L.mc.w};
+  const uint32_t rw[4] = {L.rc.x, L.rc.y, L.rc.z, L.rc.w};
+  float mo[16], ro[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    e4m3_decode4(mw[j], L.sm, mo + 4 * j);
+    e4m3_decode4(rw[j], L.sr, ro + 4 * j);
+  }
+  float m[16], r[16], pn[16];
   float am = 0.0f, ar = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    el[i] = adam_elem(L.g[i], mo[i], ro[i], pv[i], k);
-    el[i].v = sqrtf(el[i].v);      // r = sqrt(v), the stored quantity
-    am = fmaxf(am, fabsf(el[i].m));
-    ar = fmaxf(ar, el[i].v);
+  for (int i = 0; i < 16; ++i) {
+    const float pv = bf16_to_f32(i & 1 ? pw[i >> 1] >> 16 : pw[i >> 1] & 0xFFFFu);
+    const Elem el = adam_elem(g[i], mo[i], ro[i], pv, k);
+    m[i] = el.m;
+    r[i] = sqrtf(el.v);            // r = sqrt(v), the stored quantity
+    pn[i] = el.p;
+    am = fmaxf(am, fabsf(m[i]));
+    ar = fmaxf(ar, r[i]);
   }
-  am = wave_max(am);
-  ar = wave_max(ar);
+  am = group_max16(am);
+  ar = group_max16(ar);
   const float sm = am / AW_E4M3_MAX;
   const float sr = ar / AW_E4M3_MAX;
+  float qm[16], qr[16];
+  block_quot16(m, am, sm, qm);
+  block_quot16(r, ar, sr, qr);
   AwOut o;
-  o.mc = am == 0.0f ? 0u
-                    : e4m3_encode4(el[0].m / sm, el[1].m / sm, el[2].m / sm,
-                                   el[3].m / sm);
-  o.rc = ar == 0.0f ? 0u
-                    : e4m3_encode4(el[0].v / sr, el[1].v / sr, el[2].v / sr,
-                                   el[3].v / sr);
-  o.p01 = pack_bf16x2(el[0].p, el[1].p);
-  o.p23 = pack_bf16x2(el[2].p, el[3].p);
+  uint32_t mcw[4], rcw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mcw[j] = am == 0.0f ? 0u
+                        : e4m3_encode4(qm[4 * j], qm[4 * j + 1], qm[4 * j + 2],
+                                       qm[4 * j + 3]);
+    rcw[j] = ar == 0.0f ? 0u
+                        : e4m3_encode4(qr[4 * j], qr[4 * j + 1], qr[4 * j + 2],
+                                       qr[4 * j + 3]);
+  }
+  o.mc = u32x4{mcw[0], mcw[1], mcw[2], mcw[3]};
+  o.rc = u32x4{rcw[0], rcw[1], rcw[2], rcw[3]};
+  uint32_t po[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) po[j] = pack_bf16x2(pn[2 * j], pn[2 * j + 1]);
+  o.p[0] = u32x4{po[0], po[1], po[2], po[3]};
+  o.p[1] = u32x4{po[4], po[5], po[6], po[7]};
   o.sm = am == 0.0f ? 0.0f : sm;
   o.sr = ar == 0.0f ? 0.0f : sr;
   return o;
 }
 
-// A wave owns one 256-element block per iteration (lane l: elements
-// 4l .. 4l+3) and issues the loads of its next block before stepping the
-// current one.  The whole blocks run in the loop; a short last block is
-// done afterwards by one wave with per-element guards (its missing
-// elements count as zero for the block maxima and are not stored).
+// A wave steps 4 whole blocks (1024 consecutive elements, lane l holding
+// elements 16 l .. 16 l + 15 of them) per iteration, the loads of its next
+// 4 blocks in flight; two register sets alternate, every iteration issues
+// the same loads and stores (out of range for blocks past the whole ones),
+// so the compiler's waits leave the next loads in flight.  A short last
+// block is done afterwards by lanes 0..15 of one wave with per-element
+// guards (its missing elements count as zero for the block maxima and are
+// not stored).
 __global__ __launch_bounds__(AW_THREADS) void k_adamw8(
     uint16_t* __restrict__ p, const float* __restrict__ g, int64_t n,
     uint8_t* __restrict__ mc, float* __restrict__ ms,
     uint8_t* __restrict__ rc, float* __restrict__ rs, AdamConsts k) {
   const int lane = threadIdx.x & 63;
   const int64_t nwhole = n / AW_BLOCK;
-  const int64_t wave0 = ((int64_t)blockIdx.x * AW_THREADS + threadIdx.x) >> 6;
+  const int64_t nquad = (nwhole + 3) / 4;          // groups of 4 blocks
+  const int64_t wave0 = __builtin_amdgcn_readfirstlane(
+      (int)(((int64_t)blockIdx.x * AW_THREADS + threadIdx.x) >> 6));
   const int64_t nwaves = ((int64_t)gridDim.x * AW_THREADS) >> 6;
-  auto load = [&](AwLoads& L, int64_t b) {
-    const int64_t bb = b < nwhole ? b : 0;     // keep loads in range
-    const int64_t e0 = bb * AW_BLOCK + 4 * lane;
-    const f32x4 g4 = *reinterpret_cast<const f32x4*>(g + e0);
-    const uint2 p4 = *reinterpret_cast<const uint2*>(p + e0);
-    L.g[0] = g4.x; L.g[1] = g4.y; L.g[2] = g4.z; L.g[3] = g4.w;
-    L.p01 = p4.x;
-    L.p23 = p4.y;
-    L.mc = *reinterpret_cast<const uint32_t*>(mc + e0);
-    L.rc = *reinterpret_cast<const uint32_t*>(rc + e0);
-    L.sm = ms[bb];
-    L.sr = rs[bb];
+  const int blk = lane >> 4;                       // block of the quad
+  // per-quad buffer resources: offsets stay small whatever n is
+  auto loadq = [&](AwLoads& L, int64_t qd) {
+    const int64_t b = 4 * qd + blk;
+    const bool ok = qd < nquad && b < nwhole;
+    const int64_t e0 = qd < nquad ? 4 * qd * AW_BLOCK : 0;
+    const rsrc_t rg = make_rsrc(g + e0, 4 * AW_BLOCK * 4);
+    const rsrc_t rp = make_rsrc(p + e0, 4 * AW_BLOCK * 2);
+    const rsrc_t rm = make_rsrc(mc + e0, 4 * AW_BLOCK);
+    const rsrc_t rr = make_rsrc(rc + e0, 4 * AW_BLOCK);
+    const rsrc_t rsm = make_rsrc(ms + (qd < nquad ? 4 * qd : 0), 16);
+    const rsrc_t rsr = make_rsrc(rs + (qd < nquad ? 4 * qd : 0), 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      L.g[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rg, ok ? (uint32_t)(64 * lane + 16 * j) : G_OOB, 0, 0));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      L.p[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rp, ok ? (uint32_t)(32 * lane + 16 * j) : G_OOB, 0, 0));
+    L.mc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        rm, ok ? (uint32_t)(16 * lane) : G_OOB, 0, 0));
+    L.rc = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+        rr, ok ? (uint32_t)(16 * lane) : G_OOB, 0, 0));
+    L.sm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        rsm, ok ? (uint32_t)(4 * blk) : G_OOB, 0, 0));
+    L.sr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+        rsr, ok ? (uint32_t)(4 * blk) : G_OOB, 0, 0));
   };
-  if (nwhole > 0) {
-    AwLoads cur;
-    int64_t b = wave0;
-    if (b < nwhole) load(cur, b);
-    for (; b < nwhole; b += nwaves) {
-      AwLoads nxt;
-      if (b + nwaves < nwhole) load(nxt, b + nwaves);
-      const AwOut o = adam_block(cur, k);
-      const int64_t e0 = b * AW_BLOCK + 4 * lane;
-      *reinterpret_cast<uint2*>(p + e0) = make_uint2(o.p01, o.p23);
-      *reinterpret_cast<uint32_t*>(mc + e0) = o.mc;
-      *reinterpret_cast<uint32_t*>(rc + e0) = o.rc;
-      if (lane == 0) {
-        ms[b] = o.sm;
-        rs[b] = o.sr;
-      }
-      cur = nxt;
+  auto stepq = [&](const AwLoads& L, int64_t qd) {
+    const AwOut o = adam_block(L, k);
+    const int64_t b = 4 * qd + blk;
+    const bool ok = b < nwhole;
+    const int64_t e0 = 4 * qd * AW_BLOCK;
+    const rsrc_t rp = make_rsrc(p + e0, 4 * AW_BLOCK * 2);
+    const rsrc_t rm = make_rsrc(mc + e0, 4 * AW_BLOCK);
+    const rsrc_t rr = make_rsrc(rc + e0, 4 * AW_BLOCK);
+    const rsrc_t rsm = make_rsrc(ms + 4 * qd, 16);
+    const rsrc_t rsr = make_rsrc(rs + 4 * qd, 16);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          o.p[j], rp, ok ? (uint32_t)(32 * lane + 16 * j) : G_OOB, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(o.mc, rm, ok ? (uint32_t)(16 * lane) : G_OOB,
+                                           0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(o.rc, rr, ok ? (uint32_t)(16 * lane) : G_OOB,
+                                           0, 0);
+    const bool lead = ok && (lane & 15) == 0;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.sm), rsm,
+                                          lead ? (uint32_t)(4 * blk) : G_OOB, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o.sr), rsr,
+                                          lead ? (uint32_t)(4 * blk) : G_OOB, 0, 0);
+  };
+  if (nquad > 0) {
+    AwLoads A, B;
+    int64_t qd = wave0;
+    loadq(A, qd);
+    for (; qd + nwaves < nquad; qd += 2 * nwaves) {
+      loadq(B, qd + nwaves);
+      stepq(A, qd);
+      loadq(A, qd + 2 * nwaves);
+      stepq(B, qd + nwaves);
     }
+    if (qd < nquad) stepq(A, qd);
   }
   if (n % AW_BLOCK != 0 && wave0 == 0) {
+    // the short last block: lanes 0..15, guarded per element
     const int64_t b = nwhole;
-    const int64_t e0 = b * AW_BLOCK + 4 * lane;
+    const int64_t e0 = b * AW_BLOCK + 16 * (lane & 15);
     AwLoads L;
-    L.mc = L.rc = 0;
-    uint32_t pb[4];
+    float gv[16];
+    uint32_t pb[16], mb[16], rb[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = e0 + i < n;
-      L.g[i] = in ? g[e0 + i] : 0.0f;
+    for (int i = 0; i < 16; ++i) {
+      const bool in = lane < 16 && e0 + i < n;
+      gv[i] = in ? g[e0 + i] : 0.0f;
       pb[i] = in ? static_cast<uint32_t>(p[e0 + i]) : 0u;
-      L.mc |= (in ? static_cast<uint32_t>(mc[e0 + i]) : 0u) << (8 * i);
-      L.rc |= (in ? static_cast<uint32_t>(rc[e0 + i]) : 0u) << (8 * i);
+      mb[i] = in ? static_cast<uint32_t>(mc[e0 + i]) : 0u;
+      rb[i] = in ? static_cast<uint32_t>(rc[e0 + i]) : 0u;
     }
-    L.p01 = pb[0] | (pb[1] << 16);
-    L.p23 = pb[2] | (pb[3] << 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      L.g[j] = f32x4{gv[4 * j], gv[4 * j + 1], gv[4 * j + 2], gv[4 * j + 3]};
+      const uint32_t m4 = mb[4 * j] | (mb[4 * j + 1] << 8) | (mb[4 * j + 2] << 16) |
+                          (mb[4 * j + 3] << 24);
+      const uint32_t r4 = rb[4 * j] | (rb[4 * j + 1] << 8) | (rb[4 * j + 2] << 16) |
+                          (rb[4 * j + 3] << 24);
+      if (j == 0) { L.mc.x = m4; L.rc.x = r4; }
+      if (j == 1) { L.mc.y = m4; L.rc.y = r4; }
+      if (j == 2) { L.mc.z = m4; L.rc.z = r4; }
+      if (j == 3) { L.mc.w = m4; L.rc.w = r4; }
+    }
+    uint32_t pw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pw[j] = pb[2 * j] | (pb[2 * j + 1] << 16);
+    L.p[0] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+    L.p[1] = u32x4{pw[4], pw[5], pw[6], pw[7]};
     L.sm = ms[b];
     L.sr = rs[b];
     const AwOut o = adam_block(L, k);
-    const uint32_t po[4] = {o.p01 & 0xFFFFu, o.p01 >> 16, o.p23 & 0xFFFFu,
-                            o.p23 >> 16};
+    const uint32_t po[8] = {o.p[0].x, o.p[0].y, o.p[0].z, o.p[0].w,
+                            o.p[1].x, o.p[1].y, o.p[1].z, o.p[1].w};
+    const uint32_t mo[4] = {o.mc.x, o.mc.y, o.mc.z, o.mc.w};
+    const uint32_t ro[4] = {o.rc.x, o.rc.y, o.rc.z, o.rc.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (e0 + i < n) {
-        p[e0 + i] = static_cast<uint16_t>(po[i]);
-        mc[e0 + i] = static_cast<uint8_t>(o.mc >> (8 * i));
-        rc[e0 + i] = static_cast<uint8_t>(o.rc >> (8 * i));
+    for (int i = 0; i < 16; ++i) {
+      if (lane < 16 && e0 + i < n) {
+        p[e0 + i] = static_cast<uint16_t>(i & 1 ? po[i >> 1] >> 16 : po[i >> 1] & 0xFFFFu);
+        mc[e0 + i] = static_cast<uint8_t>(mo[i >> 2] >> (8 * (i & 3)));
+        rc[e0 + i] = static_cast<uint8_t>(ro[i >> 2] >> (8 * (i & 3)));
       }
     }
     if (lane == 0) {
@@ -242,8 +364,9 @@ bool valid_state(const qn_adamw8_state* st) {
 int launch_adamw8(uint16_t* p, const float* g, int64_t n, uint8_t* mc,
                   float* ms, uint8_t* rc, float* rs, const AdamConsts& k,
                   hipStream_t st) {
-  const int64_t nb = cdiv(n, AW_BLOCK);
-  const int64_t grid = std::min<int64_t>(cdiv(nb, AW_THREADS / 64), 8192);
+  const int64_t nquad = cdiv(n / AW_BLOCK, 4);     // 4 blocks per wave step
+  const int64_t grid = std::max<int64_t>(
+      1, std::min<int64_t>(cdiv(nquad, AW_THREADS / 64), 8192));
   QN_LAUNCH("k_adamw8", k_adamw8, dim3((unsigned)grid), dim3(AW_THREADS), st,
             p, g, n, mc, ms, rc, rs, k);
   return check_launch();
