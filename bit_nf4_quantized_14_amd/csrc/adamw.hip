@@ -426,9 +426,10 @@ int qn_adamw8_paged_step(uint16_t* p, const float* g, int64_t n,
   hipStream_t ds = d2h_stream ? (hipStream_t)d2h_stream : cs;
   const int64_t nch = cdiv(n, chunk);
 
-  // events: start (on the compute stream), and per chunk H2D done, step
-  // done, D2H done; destroyed at the end (released once they complete)
-  std::vector<hipEvent_t> ev(3 * nch + 1, nullptr);
+  // events: per chunk H2D done, step done, D2H done; then the start (on the
+  // compute stream) and the two copy streams' tails for an error exit;
+  // destroyed at the end (released once they complete)
+  std::vector<hipEvent_t> ev(3 * nch + 3, nullptr);
   int rc_all = QN_OK;
   auto mk = [&](hipEvent_t* e) {
     if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess)
@@ -438,6 +439,7 @@ int qn_adamw8_paged_step(uint16_t* p, const float* g, int64_t n,
   auto ok = [&](hipError_t r) {
     if (r != hipSuccess) rc_all = QN_EHIP;
   };
+  bool queued = false;           // copies may be in flight on hs / ds
   if (rc_all == QN_OK) {
     hipEvent_t start = ev[3 * nch];
     // nothing earlier on the compute stream (a previous step's write-back
@@ -446,6 +448,7 @@ int qn_adamw8_paged_step(uint16_t* p, const float* g, int64_t n,
     ok(hipStreamWaitEvent(hs, start, 0));
     ok(hipStreamWaitEvent(ds, start, 0));
     char* base = static_cast<char*>(staging);
+    queued = true;
     for (int64_t i = 0; i < nch && rc_all == QN_OK; ++i) {
       const int64_t e0 = i * chunk;
       const int64_t len = std::min<int64_t>(chunk, n - e0);
@@ -478,6 +481,22 @@ int qn_adamw8_paged_step(uint16_t* p, const float* g, int64_t n,
     // the compute stream reaches the end of the call only after the last
     // write-back (the copy streams run in order)
     if (rc_all == QN_OK) ok(hipStreamWaitEvent(cs, ev[3 * (nch - 1) + 2], 0));
+  }
+  if (rc_all != QN_OK && queued) {
+    // An error after copies were queued: the compute stream still waits for
+    // everything queued on the copy streams, so the host state and the
+    // staging area are not in use once the stream reaches this point; if
+    // that cannot be arranged, the copy streams are drained before return.
+    hipEvent_t th = ev[3 * nch + 1], td = ev[3 * nch + 2];
+    const bool waited =
+        th != nullptr && td != nullptr && hipEventRecord(th, hs) == hipSuccess &&
+        hipEventRecord(td, ds) == hipSuccess &&
+        hipStreamWaitEvent(cs, th, 0) == hipSuccess &&
+        hipStreamWaitEvent(cs, td, 0) == hipSuccess;
+    if (!waited) {
+      (void)hipStreamSynchronize(hs);
+      (void)hipStreamSynchronize(ds);
+    }
   }
   for (auto& e : ev)
     if (e != nullptr) hipEventDestroy(e);

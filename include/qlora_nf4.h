@@ -320,7 +320,12 @@ size_t qn_adamw8_staging_bytes(int64_t chunk);
  * `stream` reaches the end of the call only after the last page is back in
  * host memory.  The copy streams must have the default priority.
  * Errors: QN_EINVAL, QN_EWORKSPACE (staging smaller than
- * qn_adamw8_staging_bytes(chunk)), QN_EHIP. */
+ * qn_adamw8_staging_bytes(chunk)), both before anything is queued; QN_EHIP,
+ * possibly after some pages were queued: then `stream` still waits for
+ * every copy already queued (or, if that cannot be arranged, the copy
+ * streams are drained before the call returns), so the host state and the
+ * staging buffer are free once `stream` gets past the call, but the state
+ * may hold a mix of stepped and unstepped pages. */
 int qn_adamw8_paged_step(uint16_t* p, const float* g, int64_t n,
                          const qn_adamw8_state* host_st, void* staging,
                          size_t staging_bytes, int64_t chunk,
