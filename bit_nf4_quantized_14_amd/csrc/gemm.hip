@@ -143,10 +143,11 @@ __device__ __forceinline__ void gemm_load_w(WRegs& R, rsrc_t rp, rsrc_t rq,
 
 template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_dequant_w(const WRegs& R, uint16_t* sW,
-                                               const Codebook& cb, int tid) {
+                                               const LutHalf& lh, int tid) {
   const WDst dst = gemm_wdst<BM, BN, BWD>(sW, tid);
-  const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
-  const uint32_t wd[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+  const Lut t = make_lut_pair(lh, static_cast<float>(R.q) * R.d);
+  const uint32_t wd[4] = {R.w.x ^ lh.flip, R.w.y ^ lh.flip, R.w.z ^ lh.flip,
+                          R.w.w ^ lh.flip};
 #pragma unroll
   for (int d = 0; d < 4; ++d)
     *reinterpret_cast<u32x4*>(dst.base + 8 * (d ^ dst.x)) = gemm_decode<BWD>(wd[d], t);
@@ -350,7 +351,7 @@ template <int BM, int BN, bool BWD>
 __device__ __forceinline__ void gemm_mma_deq(
     const char* sA, const uint16_t* sW, uint16_t* sWn, const WRegs& R,
     const ARegs<BM, BN, BWD>& An, char* sAn,
-    const Codebook& cb, int wm, int wn, int tid, int lane,
+    const LutHalf& lh, int wm, int wn, int tid, int lane,
     f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
   using C = GemmCfg<BM, BN, BWD>;
   constexpr int MPK = C::TM * C::TN;     // MFMAs per k16 slice
@@ -358,8 +359,9 @@ __device__ __forceinline__ void gemm_mma_deq(
   constexpr int MPD = MPK / DPK;         // MFMAs per decode8
   static_assert(C::WDW % 4 == 0 && MPK % DPK == 0, "decode split");
   const WDst dst = gemm_wdst<BM, BN, BWD>(sWn, tid);
-  const Lut t = make_lut(cb, static_cast<float>(R.q) * R.d);
-  const uint32_t wd[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+  const Lut t = make_lut_pair(lh, static_cast<float>(R.q) * R.d);
+  const uint32_t wd[4] = {R.w.x ^ lh.flip, R.w.y ^ lh.flip, R.w.z ^ lh.flip,
+                          R.w.w ^ lh.flip};
   u32x4 a[2][C::TM], b[2][C::TN];
   gemm_frags<BM, BN, BWD>(sA, sW, wm, wn, lane, 0, a[0], b[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -490,13 +492,13 @@ template <int BM, int BN, bool BWD, bool CHK>
 __device__ __forceinline__ void gemm_step(
     int st, char* sAc, uint16_t* sWc, char* sAn, uint16_t* sWn, WRegs& Wc,
     const GemmLoader<BM, BN, BWD, CHK>& ld, int wm, int wn, int tid, int lane,
-    const Codebook& cb,
+    const LutHalf& lh,
     f32x16 (&acc)[GemmCfg<BM, BN, BWD>::TM][GemmCfg<BM, BN, BWD>::TN]) {
   WRegs Wn;
   ARegs<BM, BN, BWD> An;
   ld.load_a(An, (st + 1) * G_BK);
   ld.load_w(Wn, (st + 2) * G_BK);
-  gemm_mma_deq<BM, BN, BWD>(sAc, sWc, sWn, Wc, An, sAn, cb, wm, wn, tid, lane, acc);
+  gemm_mma_deq<BM, BN, BWD>(sAc, sWc, sWn, Wc, An, sAn, lh, wm, wn, tid, lane, acc);
   __builtin_amdgcn_s_waitcnt(0);   // all counters: loads and LDS writes done
   __syncthreads();
   Wc = Wn;
@@ -686,6 +688,10 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
   ld.tid = tid;
   ld.init();
 
+  // lanes 2i and 2i+1 hold weights of the same 64-weight block (32 each)
+  // and build its table together
+  const LutHalf lh = lut_half(cb, lane);
+
   f32x16 acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
@@ -717,15 +723,15 @@ __global__ __launch_bounds__((BN == 256 ? 512 : 256), 1) void k_gemm(
       gemm_store_a<BM, BN, BWD>(A0, sA0, tid);                                 \
     }                                                                          \
     ld.load_w(Wc, r0_ * G_BK);                                                 \
-    gemm_dequant_w<BM, BN, BWD>(Wc, sW0, cb, tid);                             \
+    gemm_dequant_w<BM, BN, BWD>(Wc, sW0, lh, tid);                             \
     ld.load_w(Wc, (r0_ + 1) * G_BK);                                           \
     __builtin_amdgcn_s_waitcnt(0); /* loads landed in LDS and registers */     \
     __syncthreads();                                                           \
     for (int st = r0_; st < r1_; st += 2) {                                    \
       gemm_step<BM, BN, BWD, CHK>(st, sA0, sW0, sA1, sW1, Wc, ld, wm, wn, tid, \
-                                  lane, cb, acc);                              \
+                                  lane, lh, acc);                              \
       gemm_step<BM, BN, BWD, CHK>(st + 1, sA1, sW1, sA0, sW0, Wc, ld, wm, wn,  \
-                                  tid, lane, cb, acc);                         \
+                                  tid, lane, lh, acc);                         \
     }                                                                          \
   } while (0)
   GEMM_MAINLOOP(s0, s1);

@@ -87,6 +87,57 @@ __device__ __forceinline__ Lut make_lut(const Codebook& cb, float cp) {
   return t;
 }
 
+// The same table built by two adjacent lanes (2i, 2i+1) that decode the same
+// block: each lane forms the products of one half of the levels (entries
+// 0-7 on the even lane, 8-15 on the odd one) and takes the other half from
+// its neighbour with a DPP swap, so each lane does half the multiplies,
+// conversions and byte splits.  The odd lane ends up with the two halves in
+// swapped slots; it decodes codes whose bit 3 is flipped (`flip`, XORed
+// into each packed dword), which selects the right slot.  The entries are
+// the same fp32 products as make_lut's, so the decoded weights are
+// bit-identical.
+struct LutHalf {
+  float L[8];      // levels 8 (lane & 1) .. + 7
+  uint32_t flip;   // 0 on the even lane, 0x88888888 on the odd lane
+};
+
+__device__ __forceinline__ LutHalf lut_half(const Codebook& cb, int lane) {
+  LutHalf h;
+  const bool odd = (lane & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h.L[i] = odd ? cb.L[8 + i] : cb.L[i];
+  h.flip = odd ? 0x88888888u : 0u;
+  return h;
+}
+
+// v_mov_b32 with DPP quad_perm [1, 0, 3, 2]: the value of the other lane of
+// the pair.
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ Lut make_lut_pair(const LutHalf& h, float cp) {
+  uint32_t P[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    P[k] = pack_bf16x2(h.L[2 * k] * cp, h.L[2 * k + 1] * cp);
+  // low and high bytes of this lane's entries 0-3 and 4-7 of its half
+  const uint32_t l0 = perm(P[1], P[0], 0x06040200u);
+  const uint32_t h0 = perm(P[1], P[0], 0x07050301u);
+  const uint32_t l1 = perm(P[3], P[2], 0x06040200u);
+  const uint32_t h1 = perm(P[3], P[2], 0x07050301u);
+  Lut t;
+  t.ll0 = l0;
+  t.hl0 = h0;
+  t.ll1 = l1;
+  t.hl1 = h1;
+  t.lh0 = pair_swap(l0);
+  t.hh0 = pair_swap(h0);
+  t.lh1 = pair_swap(l1);
+  t.hh1 = pair_swap(h1);
+  return t;
+}
+
 // 8 codes (one packed dword, element i in bits 4i..4i+3) -> 8 bf16 in
 // natural order (out[i] holds elements 2i, 2i+1, low half first).
 __device__ __forceinline__ u32x4 decode8(uint32_t p, const Lut& t) {
