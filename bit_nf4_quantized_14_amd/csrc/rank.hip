@@ -314,24 +314,31 @@ __global__ __launch_bounds__(256) void k_rank_stream(
   wg_barrier();
 
   // One stage: store the previous stage's column sums, compute on buffer
-  // `cur`, start the stage NBUF - 1 ahead into buffer `far`, then wait until
-  // the next stage has landed (with three buffers the newest one stays in
-  // flight; its loads are the last ones issued, and loads complete in order).
+  // `cur` while the stage NBUF - 1 ahead streams into buffer `far` (the
+  // buffer of the stage before, which every wave has left at the last
+  // barrier), then wait until the next stage has landed.  With three buffers
+  // the loads start after the compute and the newest stage stays in flight
+  // across the barrier (its loads are the last ones issued, and loads
+  // complete in order); with two, they start before the compute, so that
+  // their latency runs under it.
 #define RS_BODY(I, CS, CR, FS, FR)                                            \
   do {                                                                        \
     if (G::COLS && (I) > sb)                                                  \
       rs_store_cols<MODE, JT>(rc, (I) - 1, C, wave, lane, accC);              \
+    const bool ahead_ = (I) + G::NBUF - 1 < se;                               \
+    if (G::NBUF == 2 && ahead_)                                               \
+      rs_stage_dma<MODE, JT>(rs, rr, FS, FR, C, nvalid, r, (I) + 1, wave,     \
+                             lane);                                           \
     rs_stage_compute<MODE, JT, DROP>(CS, CR, sUh, sUl, wave, lane, accR,      \
                                      accC, (I), m0, dp);                      \
-    if ((I) + G::NBUF - 1 < se) {                                             \
-      rs_stage_dma<MODE, JT>(rs, rr, FS, FR, C, nvalid, r, (I) + G::NBUF - 1, \
-                             wave, lane);                                     \
-      if (G::NBUF == 3) RS_WAIT_VM(G::DMA);                                   \
-      else RS_WAIT_VM(0);                                                     \
+    if (G::NBUF == 3 && ahead_) {                                             \
+      rs_stage_dma<MODE, JT>(rs, rr, FS, FR, C, nvalid, r, (I) + 2, wave,     \
+                             lane);                                           \
+      RS_WAIT_VM(G::DMA);                                                     \
     } else {                                                                  \
       RS_WAIT_VM(0);                                                          \
     }                                                                         \
-    wg_barrier();                                                          \
+    wg_barrier();                                                             \
   } while (0)
 
   if constexpr (G::NBUF == 3) {

@@ -95,6 +95,9 @@ def test_tiny_workload_bf16_outputs():
     (300, 264, 256, 48, 3.0),    # r = 48: two 256-row blocks of the rank
                                  # streams, the second ragged
     (64, 128, 256, 256, 512.0),  # maximum rank
+    (1024, 2048, 2112, 256, 64.0),  # maximum rank, two or three stages per
+                                    # rank-stream workgroup (two-buffer
+                                    # pipeline), a ragged last one
     (257, 1024, 576, 16, 32.0),  # M spans two split-M chunks
     (8, 200, 320, 5, 3.0),       # skinny path: N % 16 != 0, K % 256 != 0
     (13, 1032, 2368, 33, 8.0),   # skinny path: several K slices, r > 32
