@@ -373,8 +373,12 @@ __device__ __forceinline__ float sum_slices(const float* __restrict__ p,
 // Reduce: Y[m][n] = sum_slices part[.][m][n] + s * sum_j T[m][j] B[n][j],
 // and T[m][j] = sum_slices part[.][m][Nw + j] (written to t_save by the
 // blocks of the first column block).  The blocks of all projections form one
-// grid; block b of projection p covers columns [64 bx, 64 bx + 64) of tokens
-// [4 by, 4 by + 4), one output per thread.
+// grid; block b of projection p covers columns [256 bx, 256 bx + 256) of
+// tokens [4 by, 4 by + 4), four adjacent outputs per thread (16-byte partial
+// loads; N % 8 == 0, so a thread's four columns are all in range or all
+// out).  Every load a thread needs goes out before the first is waited for:
+// its rows of B (r <= 16), then SKR_SL slices of its outputs and of its T
+// element (r <= 64) at a time.
 // ---------------------------------------------------------------------------
 struct SkRProj {
   const float* part;
@@ -390,6 +394,20 @@ struct SkRArgs {
   int nproj;
 };
 
+constexpr int SKR_SL = 16;    // slice loads in flight per summed element
+constexpr int SKR_COLS = 256; // columns per block
+
+// sum_j t[j] * B row j (16-byte rows of eight bf16), j in order
+__device__ __forceinline__ float skr_dot8(const float* t, const u32x4& w, float acc) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    acc += t[2 * h] * __uint_as_float(ww[h] << 16);
+    acc += t[2 * h + 1] * __uint_as_float(ww[h] & 0xFFFF0000u);
+  }
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void k_skinny_reduce(SkRArgs args) {
   __shared__ float sT[4 * QN_MAX_RANK];
   int p = 0;
@@ -399,46 +417,94 @@ __global__ __launch_bounds__(256) void k_skinny_reduce(SkRArgs args) {
   const int Nw = (N + 15) / 16 * 16;
   const int64_t rows_total = Nw + P.rpad;
   const int64_t stride = (int64_t)M * rows_total;      // between slices
-  const int nbx = (N + 63) / 64;
+  const int nbx = (N + SKR_COLS - 1) / SKR_COLS;
   const int local = blockIdx.x - P.blk0;
   const int bx = local % nbx, by = local / nbx;
   const int mb = 4 * by;
   const int mrows = min(4, M - mb);
-  const int n = bx * 64 + (threadIdx.x & 63);
+  const int n0 = bx * SKR_COLS + 4 * (threadIdx.x & 63);
   const int mi = threadIdx.x >> 6;
-  const bool live = n < N && mi < mrows;
+  const bool live = n0 < N && mi < mrows;
   const int m = mb + mi;
-  // this thread's weight partials first: their loads are in flight while T
-  // is summed
-  const float y =
-      live ? sum_slices(P.part + (int64_t)m * rows_total + n, stride, P.slices) : 0.f;
-  for (int idx = threadIdx.x; idx < mrows * r; idx += 256) {
-    const int m = mb + idx / r, j = idx % r;
-    const float v = sum_slices(P.part + (int64_t)m * rows_total + Nw + j, stride,
-                               P.slices);
-    sT[idx] = v;
-    if (bx == 0) P.t_save[(int64_t)m * r + j] = v;
+  const bool b16 = (r & 7) == 0 && (reinterpret_cast<uintptr_t>(P.B) & 15) == 0;
+  // (lanes without outputs read valid addresses, row 0 and slice 0, and drop
+  // what they read, so that no load sits behind a branch)
+  const uint16_t* b = P.B + (live ? (int64_t)n0 * r : 0);
+  u32x4 brow[4][2];
+  if (b16 && r <= 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        brow[i][q] = 8 * q < r ? *reinterpret_cast<const u32x4*>(b + i * r + 8 * q)
+                               : u32x4{0u, 0u, 0u, 0u};
+  }
+  const int tidx = threadIdx.x;
+  const bool tl = r <= 64 && tidx < mrows * r;
+  const int tm = mb + (tl ? tidx / r : 0), tj = tl ? tidx % r : 0;
+  const float* py = P.part + (live ? (int64_t)m * rows_total + n0 : 0);
+  const float* pt = P.part + (tl ? (int64_t)tm * rows_total + Nw + tj : 0);
+  float y[4] = {0.f, 0.f, 0.f, 0.f}, tsum = 0.f;
+  for (int sl = 0; sl < P.slices; sl += SKR_SL) {
+    f32x4 yv[SKR_SL];
+    float tv[SKR_SL];
+#pragma unroll
+    for (int u = 0; u < SKR_SL; ++u) {
+      const bool in = sl + u < P.slices;
+      const int64_t o = (int64_t)(in ? sl + u : 0) * stride;
+      yv[u] = *reinterpret_cast<const f32x4*>(py + o);
+      tv[u] = pt[o];
+      if (!(live && in)) yv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!(tl && in)) tv[u] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SKR_SL; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] += yv[u][i];
+#pragma unroll
+    for (int u = 0; u < SKR_SL; ++u) tsum += tv[u];
+  }
+  if (tl) {
+    sT[tidx] = tsum;
+    if (bx == 0) P.t_save[(int64_t)tm * r + tj] = tsum;
+  }
+  if (r > 64) {
+    for (int idx = threadIdx.x; idx < mrows * r; idx += 256) {
+      const int mm = mb + idx / r, j = idx % r;
+      const float v = sum_slices(P.part + (int64_t)mm * rows_total + Nw + j, stride,
+                                 P.slices);
+      sT[idx] = v;
+      if (bx == 0) P.t_save[(int64_t)mm * r + j] = v;
+    }
   }
   __syncthreads();
   if (!live) return;
   const float* t = sT + mi * r;
-  const uint16_t* b = P.B + (int64_t)n * r;
-  float lora = 0.f;
-  if ((r & 7) == 0 && (reinterpret_cast<uintptr_t>(P.B) & 15) == 0) {
-    // 16-byte aligned rows of B: 8 weights per load
-    for (int j0 = 0; j0 < r; j0 += 8) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(b + j0);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  float lora[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        lora += t[j0 + 2 * h] * __uint_as_float(ww[h] << 16);
-        lora += t[j0 + 2 * h + 1] * __uint_as_float(ww[h] & 0xFFFF0000u);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t* bi = b + i * r;
+    if (b16 && r <= 16) {
+      lora[i] = skr_dot8(t, brow[i][0], lora[i]);
+      if (r > 8) lora[i] = skr_dot8(t + 8, brow[i][1], lora[i]);
+    } else if (b16) {
+      for (int j0 = 0; j0 < r; j0 += 8)
+        lora[i] = skr_dot8(t + j0, *reinterpret_cast<const u32x4*>(bi + j0), lora[i]);
+    } else {
+      for (int jj = 0; jj < r; ++jj) lora[i] += t[jj] * bf16_to_f32(bi[jj]);
     }
-  } else {
-    for (int jj = 0; jj < r; ++jj) lora += t[jj] * bf16_to_f32(b[jj]);
   }
-  store_out(P.Y, P.y_bf16, (int64_t)m * N + n, y + P.s * lora);
+  const int64_t o = (int64_t)m * N + n0;
+  if (P.y_bf16) {
+    uint2 v;
+    v.x = pack_bf16x2(y[0] + P.s * lora[0], y[1] + P.s * lora[1]);
+    v.y = pack_bf16x2(y[2] + P.s * lora[2], y[3] + P.s * lora[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(P.Y) + o) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(P.Y) + o) =
+        f32x4{y[0] + P.s * lora[0], y[1] + P.s * lora[1], y[2] + P.s * lora[2],
+              y[3] + P.s * lora[3]};
+  }
 }
 
 }  // namespace
@@ -467,7 +533,7 @@ void launch_skinny(hipStream_t st, const SkinnyJob* jobs, int count,
     shm = std::max(shm, size_t(J.M + 1) * (P.ks + 8) * 2);
     ra.p[i] = SkRProj{part, J.B, J.t_save, J.y, J.s, P.slices, J.M,
                       (int)J.w->rows, J.r, 16 * rank_tiles(J.r), J.y_bf16, blocks};
-    blocks += (int)(cdiv(J.w->rows, 64) * cdiv(J.M, 4));
+    blocks += (int)(cdiv(J.w->rows, SKR_COLS) * cdiv(J.M, 4));
   }
   skinny_bounds(plans, K, count, G_CUS, a.bound);
   int64_t cost = 0;
