@@ -21,13 +21,17 @@ using namespace qn;
 // never both, and a slice's adapter tiles follow its weight tiles.
 //
 // The grid is SK_WGS_PER_CU = 2 workgroups of SK_WAVES = 8 waves per CU.
-// CU slot c owns a run of the list whose cost (in 256-column chunks) is
-// within one tile of an equal share (the host computes the runs); its two
-// workgroups split the run in halves, and inside a workgroup's half wave w
-// takes every eighth tile, starting with tile w.  Wherever the half changes
-// projection or slice, the workgroup stages that slice of X in LDS (M rows,
-// then an all-zero row M), each 8-element group permuted into the order
-// decode8p produces.
+// The host cuts the list into 2 G_CUS runs whose costs (in 256-column
+// chunks) are within one tile of an equal share.  Workgroups c and
+// c + G_CUS take runs 2c and 2c + 1: adjacent tiles, and the same XCD (the
+// hardware deals workgroups to the XCDs by index mod 8), so the two share
+// L2 lines of X and of the adapter rows.  Inside a workgroup's run wave w
+// takes every eighth tile, starting with tile w.  (Cutting G_CUS runs in
+// halves by tile count instead left one workgroup with 3x the work of
+// another where the cheap tiles of a short last slice met full ones.)
+// Wherever the run changes projection or slice, the workgroup stages that
+// slice of X in LDS (M rows, then an all-zero row M), each 8-element group
+// permuted into the order decode8p produces.
 //
 // A wave's weight tiles of one slice are one stream, chunk by chunk (256
 // columns): lane (n = l % 16, g = l / 16) loads the 32 packed bytes of
@@ -39,7 +43,7 @@ using namespace qn;
 // two accumulators.  Partial sums go to part[slice][m][row] (fp32, m < M).
 // ---------------------------------------------------------------------------
 
-static_assert(SK_WGS_PER_CU == 2, "two workgroups per CU slot");
+static_assert(SK_WGS_PER_CU == 2, "two workgroups per CU");
 
 struct SkProj {
   const uint16_t* X;
@@ -51,13 +55,14 @@ struct SkProj {
   int M, N, K, r, KS, wtiles, tps, tile0;
 };
 
-// bound[c]: first tile of CU slot c (skinny_bounds); slot c is served by
-// workgroups c and c + G_CUS.  wave_steps: the batch's chunk steps per wave
-// of the grid (total cost / waves), the yardstick of a wave's progress.
+// bound[j]: first tile of run j (skinny_bounds over 2 G_CUS runs); run 2c
+// belongs to workgroup c, run 2c + 1 to workgroup c + G_CUS.
+// wave_steps: the batch's chunk steps per wave of the grid (total cost /
+// waves), the yardstick of a wave's progress.
 struct SkArgs {
   SkProj p[QN_FWD_BATCH_MAX];
   int nproj, wave_steps;
-  int bound[G_CUS + 1];
+  int bound[SK_WGS_PER_CU * G_CUS + 1];
 };
 
 // Issue priority by progress.  A SIMD's waves share its VALU, and at equal
@@ -225,11 +230,9 @@ __global__ __launch_bounds__(512) void k_skinny_partial(SkArgs args,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  // this workgroup's half of its CU slot's tiles
-  const int slot = blockIdx.x % G_CUS, half = blockIdx.x / G_CUS;
-  const int cb0 = args.bound[slot], ce0 = args.bound[slot + 1];
-  const int mid = cb0 + (ce0 - cb0 + 1) / 2;
-  const int ib = half == 0 ? cb0 : mid, ie = half == 0 ? mid : ce0;
+  // this workgroup's run of tiles
+  const int run = SK_WGS_PER_CU * (blockIdx.x % G_CUS) + blockIdx.x / G_CUS;
+  const int ib = args.bound[run], ie = args.bound[run + 1];
 
   SkPrio prio;
   prio.start(args.wave_steps);
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(512) void k_skinny_partial(SkArgs args,
     sk_run_of(args, p, slice, R);
     const bool restage = p != staged_p || slice != staged_slice;
     // this wave's first tile of the segment (slice-local index): every
-    // eighth tile of the half, counted from ib
+    // eighth tile of the run, counted from ib
     const int first = t_seg + ((wave - (tile - ib)) % SK_WAVES + SK_WAVES) % SK_WAVES;
     const int t_end = t_seg + (seg_end - tile);          // slice-local end
     const int w_end = min(t_end, wtiles);                // end of weight tiles
@@ -535,7 +538,7 @@ void launch_skinny(hipStream_t st, const SkinnyJob* jobs, int count,
                       (int)J.w->rows, J.r, 16 * rank_tiles(J.r), J.y_bf16, blocks};
     blocks += (int)(cdiv(J.w->rows, SKR_COLS) * cdiv(J.M, 4));
   }
-  skinny_bounds(plans, K, count, G_CUS, a.bound);
+  skinny_bounds(plans, K, count, SK_WGS_PER_CU * G_CUS, a.bound);
   int64_t cost = 0;
   for (int i = 0; i < count; ++i) cost += int64_t(plans[i].tps) * cdiv(K[i], 256);
   a.wave_steps = (int)(cost / (G_CUS * SK_WGS_PER_CU * SK_WAVES));

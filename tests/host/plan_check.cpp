@@ -218,21 +218,24 @@ static void skinny_bounds_sweep() {
           }
         }
       }
-      std::vector<int32_t> bound(G_CUS + 1);
-      const int tiles = skinny_bounds(P.data(), K.data(), n, G_CUS, bound.data());
-      check(tiles == (int)start.size(), "tile count", tiles, (long long)start.size());
-      check(bound[0] == 0 && bound[G_CUS] == tiles, "bounds cover the tiles", bound[0],
-            bound[G_CUS], tiles);
-      for (int c = 0; c <= G_CUS; ++c) {
-        const int64_t x = int64_t(c) * T / G_CUS;
-        int64_t want = (int64_t)start.size();
-        for (size_t i = 0; i < start.size(); ++i)
-          if (start[i] >= x) {
-            want = (int64_t)i;
-            break;
-          }
-        check(bound[c] == want, "slot bound", c, bound[c], want);
-        if (c > 0) check(bound[c] >= bound[c - 1], "bounds not monotone", c);
+      // one run per CU, and one per workgroup (two per CU, as launched)
+      for (const int ns : {G_CUS, SK_WGS_PER_CU * G_CUS}) {
+        std::vector<int32_t> bound(ns + 1);
+        const int tiles = skinny_bounds(P.data(), K.data(), n, ns, bound.data());
+        check(tiles == (int)start.size(), "tile count", tiles, (long long)start.size());
+        check(bound[0] == 0 && bound[ns] == tiles, "bounds cover the tiles", bound[0],
+              bound[ns], tiles);
+        for (int c = 0; c <= ns; ++c) {
+          const int64_t x = int64_t(c) * T / ns;
+          int64_t want = (int64_t)start.size();
+          for (size_t i = 0; i < start.size(); ++i)
+            if (start[i] >= x) {
+              want = (int64_t)i;
+              break;
+            }
+          check(bound[c] == want, "slot bound", c, bound[c], want);
+          if (c > 0) check(bound[c] >= bound[c - 1], "bounds not monotone", c);
+        }
       }
     }
 }
