@@ -68,9 +68,29 @@ __device__ __forceinline__ u32x4 mg_read_colT(const uint16_t* t, int pitch,
   return v;
 }
 
-// Global loads of one tile that do not depend on the previous one: this
-// thread's 16 packed codes, its block code and group scale, and its chunks
-// of the A tile [RP][MG_COLS] (rows j < r of A [r][K], zero past r).
+// 8 codes (one packed dword, element i in bits 4i..4i+3) -> the fp32 values
+// of their 8 bf16 table entries, in natural order.  The same table lookups
+// as decode8; each fp32 word is then one v_perm of the entry's two bytes
+// over two zero bytes, instead of interleaving bf16 pairs and widening them.
+__device__ __forceinline__ void decode8_f32(uint32_t p, const Lut& t, float (&f)[8]) {
+  const uint32_t se = p & 0x07070707u;
+  const uint32_t so = (p >> 4) & 0x07070707u;
+  const uint32_t me = perm(p << 4, p << 12, 0x0B090A08u);
+  const uint32_t mo = perm(p, p << 8, 0x0B090A08u);
+  // byte k: low / high byte of element 2k (e) or 2k + 1 (o)
+  const uint32_t le = bfi(me, perm(t.lh1, t.lh0, se), perm(t.ll1, t.ll0, se));
+  const uint32_t he = bfi(me, perm(t.hh1, t.hh0, se), perm(t.hl1, t.hl0, se));
+  const uint32_t lo = bfi(mo, perm(t.lh1, t.lh0, so), perm(t.ll1, t.ll0, so));
+  const uint32_t ho = bfi(mo, perm(t.hh1, t.hh0, so), perm(t.hl1, t.hl0, so));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    // bytes: zero, zero, low byte k of src1, high byte k of src0 (4 + k)
+    const uint32_t sel = 0x0C0Cu | ((uint32_t)k << 16) | ((uint32_t)(4 + k) << 24);
+    f[2 * k] = __uint_as_float(perm(he, le, sel));
+    f[2 * k + 1] = __uint_as_float(perm(ho, lo, sel));
+  }
+}
+
 // Global loads of one tile that do not depend on the previous one: the 16
 // packed bytes of this thread's row half-block (it decodes half of them),
 // its block code and group scale, and its chunks of the A tile [RP][MG_COLS]
@@ -100,10 +120,7 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave >> 1, wk = wave & 1;
   const int64_t numel = (int64_t)N * K;
-  const rsrc_t rp = make_rsrc(packed, (uint32_t)((numel + 1) >> 1));
-  const rsrc_t rq = make_rsrc(qabs, (uint32_t)((numel + 63) >> 6));
   const rsrc_t rd = make_rsrc(gscale, (uint32_t)(((numel + 16383) >> 14) << 2));
-  const rsrc_t ra = make_rsrc(A, (uint32_t)((int64_t)r * K * 2));
   const rsrc_t rb = make_rsrc(B, (uint32_t)((int64_t)N * r * 2));
   // The MFMA gives lane l the products of row 32 wn + l % 32 of the tile at
   // columns 32 wk + 8 m + 4 h + t (m, t = 0..3, h = l / 32): this thread
@@ -115,28 +132,42 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge(
   const int tb = (int)((int64_t)blockIdx.x * ntiles / gridDim.x);
   const int te = (int)((int64_t)(blockIdx.x + 1) * ntiles / gridDim.x);
 
-  // Loads of tile t; past the run every offset is out of range (no memory
-  // access), so each step issues the same vector memory instructions.
+  // Offsets inside a tile, the same for every tile: each tile's loads go
+  // through resources based at the tile's first row and column whose range
+  // ends after its last row below N (rows past N read zeros), and past the
+  // run through zero-sized ones, so a lane's offsets are constants.
+  const uint32_t ow = (uint32_t)rn * (uint32_t)(K / 2) + 16u * (uint32_t)wk;
+  const uint32_t oq = (uint32_t)rn * (uint32_t)(K / 64);
+  const uint32_t oe = (uint32_t)rn * (uint32_t)K;    // element index of the row
+  uint32_t oa[L::NA];
+#pragma unroll
+  for (int u = 0; u < L::NA; ++u) {
+    const int i = tid + MG_THREADS * u, j = i / ACH, c = 8 * (i % ACH);
+    oa[u] = (j < r && i < G::RP * ACH) ? (uint32_t)((j * K + c) * 2) : G_OOB;
+  }
+  // lanes l and l + 32 dequantize the same block and build its table together
+  const LutHalf lh = lut_half32(cb, lane);
+
+  // Loads of tile t (every tile issues the same vector memory instructions).
   auto load = [&](L& ld, int t) {
     const bool live = t < te;
     const int n0 = (t / tiles_k) * MG_ROWS, k0 = (t % tiles_k) * MG_COLS;
-    const bool mine = live && n0 + rn < N;
-    // elements 32 wk .. 32 wk + 31 of the row's block
-    const int64_t e = (int64_t)(n0 + rn) * K + k0 + 32 * wk;
-    ld.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        rp, mine ? (uint32_t)(e >> 1) : G_OOB, 0, 0));
-    ld.q = __builtin_amdgcn_raw_buffer_load_b8(rq, mine ? (uint32_t)(e >> 6) : G_OOB,
-                                               0, 0);
+    const int rows = min(MG_ROWS, N - n0);
+    const uint32_t e0 = (uint32_t)n0 * (uint32_t)K + (uint32_t)k0;
+    const rsrc_t tp = make_rsrc(packed + e0 / 2,
+                                live ? ((uint32_t)(rows - 1) * (uint32_t)K + 64u) / 2 : 0u);
+    const rsrc_t tq = make_rsrc(qabs + e0 / 64,
+                                live ? (uint32_t)(rows - 1) * (uint32_t)(K / 64) + 1u : 0u);
+    const rsrc_t ta = make_rsrc(A + k0, live ? (uint32_t)(((r - 1) * K + MG_COLS) * 2) : 0u);
+    ld.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tp, ow, 0, 0));
+    ld.q = __builtin_amdgcn_raw_buffer_load_b8(tq, oq, 0, 0);
+    // group scale: the groups of 16384 weights do not follow the tiles
     ld.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-        rd, mine ? (uint32_t)((e >> 14) << 2) : G_OOB, 0, 0));
+        live ? rd : make_rsrc(gscale, 0u), ((oe + e0) >> 14) << 2, 0, 0));
 #pragma unroll
-    for (int u = 0; u < L::NA; ++u) {
-      const int i = tid + MG_THREADS * u, j = i / ACH, c = 8 * (i % ACH);
-      const uint32_t off = (live && j < r && i < G::RP * ACH)
-                               ? (uint32_t)(((int64_t)j * K + k0 + c) * 2) : G_OOB;
+    for (int u = 0; u < L::NA; ++u)
       ld.a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          ra, off, 0, 0));
-    }
+          ta, oa[u], 0, 0));
   };
 
   int b_n0 = -1;                                  // row block of the B tile in LDS
@@ -186,18 +217,18 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge(
     const uint32_t sel = h ? 0x07060302u : 0x05040100u;
     const uint32_t wd[2] = {__builtin_amdgcn_perm(cur.w.y, cur.w.x, sel),
                             __builtin_amdgcn_perm(cur.w.w, cur.w.z, sel)};
-    const Lut lut = make_lut(cb, static_cast<float>(cur.q) * cur.d);
+    const Lut lut = make_lut_swap32(lh, static_cast<float>(cur.q) * cur.d);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      // 8 dequantized bf16: columns 8 (2 g) + 4 h + 0..3, then 8 (2 g + 1) + ...
-      const u32x4 wb = decode8(wd[g], lut);
-      const uint32_t wp[4] = {wb.x, wb.y, wb.z, wb.w};
+      // 8 dequantized weights: columns 8 (2 g) + 4 h + 0..3, then 8 (2 g + 1) + ...
+      float wf[8];
+      decode8_f32(wd[g], lut, wf);
       uint32_t res[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int v = 8 * g + 2 * i;             // acc index of the pair
-        const float v0 = fmaf(s, acc[v], bf16_to_f32(wp[i] & 0xFFFFu));
-        const float v1 = fmaf(s, acc[v + 1], bf16_to_f32(wp[i] >> 16));
+        const float v0 = fmaf(s, acc[v], wf[2 * i]);
+        const float v1 = fmaf(s, acc[v + 1], wf[2 * i + 1]);
         res[i] = pack_bf16x2(v0, v1);
       }
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -208,15 +239,17 @@ __global__ __launch_bounds__(MG_THREADS) void k_merge(
     __syncthreads();   // the output tile is complete
     // write-out in store order: each wave instruction covers 8 rows x 128
     // contiguous bytes (16-byte chunk q of the tile is row q / ACH, column
-    // chunk q % ACH), non-temporal; rows past N address out of range
+    // chunk q % ACH), non-temporal; the resource ends after the tile's last
+    // row below N, so rows past N fall out of range
+    const int rows = min(MG_ROWS, N - n0);
     const rsrc_t ro = make_rsrc(out + (int64_t)n0 * K + k0,
-                                (uint32_t)(((int64_t)(MG_ROWS - 1) * K + MG_COLS) * 2));
+                                (uint32_t)(((rows - 1) * K + MG_COLS) * 2));
 #pragma unroll
     for (int i = 0; i < MG_ROWS * ACH / MG_THREADS; ++i) {
       const int q = tid + MG_THREADS * i, row = q / ACH, c = 8 * (q % ACH);
       __builtin_amdgcn_raw_buffer_store_b128(
           *reinterpret_cast<const u32x4*>(sO + row * G::OP + c), ro,
-          n0 + row < N ? (uint32_t)((row * K + c) * 2) : G_OOB, 0, MG_NT);
+          (uint32_t)((row * K + c) * 2), 0, MG_NT);
     }
   };
 

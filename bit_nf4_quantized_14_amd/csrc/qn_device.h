@@ -138,6 +138,45 @@ __device__ __forceinline__ Lut make_lut_pair(const LutHalf& h, float cp) {
   return t;
 }
 
+// The same table built by lanes l and l + 32 of a wave that decode the same
+// block: the lower lane forms the byte planes of entries 0-7, the upper
+// lane those of entries 8-15, and v_permlane32_swap of each plane with
+// itself hands every lane both (its first result is the lower lane's value,
+// its second the upper lane's), so no lane needs a flip.
+__device__ __forceinline__ LutHalf lut_half32(const Codebook& cb, int lane) {
+  LutHalf h;
+  const bool up = lane >= 32;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h.L[i] = up ? cb.L[8 + i] : cb.L[i];
+  h.flip = 0u;
+  return h;
+}
+
+__device__ __forceinline__ Lut make_lut_swap32(const LutHalf& h, float cp) {
+  uint32_t P[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    P[k] = pack_bf16x2(h.L[2 * k] * cp, h.L[2 * k + 1] * cp);
+  const uint32_t l0 = perm(P[1], P[0], 0x06040200u);
+  const uint32_t h0 = perm(P[1], P[0], 0x07050301u);
+  const uint32_t l1 = perm(P[3], P[2], 0x06040200u);
+  const uint32_t h1 = perm(P[3], P[2], 0x07050301u);
+  const auto s0 = __builtin_amdgcn_permlane32_swap(l0, l0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(h0, h0, false, false);
+  const auto s2 = __builtin_amdgcn_permlane32_swap(l1, l1, false, false);
+  const auto s3 = __builtin_amdgcn_permlane32_swap(h1, h1, false, false);
+  Lut t;
+  t.ll0 = s0[0];
+  t.lh0 = s0[1];
+  t.hl0 = s1[0];
+  t.hh0 = s1[1];
+  t.ll1 = s2[0];
+  t.lh1 = s2[1];
+  t.hl1 = s3[0];
+  t.hh1 = s3[1];
+  return t;
+}
+
 // 8 codes (one packed dword, element i in bits 4i..4i+3) -> 8 bf16 in
 // natural order (out[i] holds elements 2i, 2i+1, low half first).
 __device__ __forceinline__ u32x4 decode8(uint32_t p, const Lut& t) {
