@@ -262,8 +262,12 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
   uint32_t x0 = c0, x1 = c1, x2 = 0, x3 = 0;
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
-    const uint32_t hi0 = __umulhi(M0, x0), lo0 = M0 * x0;
-    const uint32_t hi1 = __umulhi(M1, x2), lo1 = M1 * x2;
+    // one 32 x 32 -> 64-bit product each (v_mad_u64_u32), rather than
+    // separate high and low multiplies
+    const uint64_t p0 = static_cast<uint64_t>(M0) * x0;
+    const uint64_t p1 = static_cast<uint64_t>(M1) * x2;
+    const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+    const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
     x0 = hi1 ^ x1 ^ k0;
     x1 = lo1;
     x2 = hi0 ^ x3 ^ k1;
@@ -277,6 +281,15 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
   r.z = x2;
   r.w = x3;
   return r;
+}
+
+// The value of lane (lane ^ dd) of this lane's quad, dd = 1..3: a DPP
+// quad_perm move, no LDS round trip.
+__device__ __forceinline__ uint32_t quad_xor(uint32_t v, int dd) {
+  return static_cast<uint32_t>(
+      dd == 1 ? __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)
+      : dd == 2 ? __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)
+                : __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x1B, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ uint32_t pick4(const u32x4& w, int sel) {
@@ -308,8 +321,8 @@ __device__ __forceinline__ u32x4 drop_row8(const u32x4& a, int m, int k0,
 #pragma unroll
   for (int dd = 0; dd < 4; ++dd) {
     const uint32_t s0 = pick4(p0, j ^ dd), s1 = pick4(p1, j ^ dd);
-    recv0[dd] = dd == 0 ? s0 : static_cast<uint32_t>(__shfl_xor(static_cast<int>(s0), dd));
-    recv1[dd] = dd == 0 ? s1 : static_cast<uint32_t>(__shfl_xor(static_cast<int>(s1), dd));
+    recv0[dd] = dd == 0 ? s0 : quad_xor(s0, dd);
+    recv1[dd] = dd == 0 ? s1 : quad_xor(s1, dd);
   }
   u32x4 v0, v1;
   v0.x = recv0[0]; v0.y = recv0[1]; v0.z = recv0[2]; v0.w = recv0[3];
