@@ -148,7 +148,7 @@ int linear_fwd(const uint16_t* x, int64_t M, const nf4_tensor* w,
   float* prow = ws_at<float>(ws, L.prow);
   const int jt = rank_tiles(r);
   // T = X A^T: partials over column blocks of X
-  const StreamPlan P = stream_plan(RS_ROWS, M, K, jt);
+  const StreamPlan P = stream_plan(RS_ROWS, M, K, jt, use_drop);
   launch_rank_stream<RS_ROWS>(st, "k_rank_stream_t", P, x, Mi, Ki, A, (int)r,
                               nullptr, nullptr, 0, prow, nullptr,
                               use_drop ? &da : nullptr);
@@ -230,7 +230,7 @@ int linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t M,
                     (int)(dx_dtype == QN_BF16), use_drop ? &da : nullptr,
                     split_ws);
   // dA = (s G)^T X: row-block partials of out[k][j] -> dA[j][k]
-  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
+  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt, use_drop);
   launch_rank_stream<RS_COLS>(st, "k_rank_stream_da", Pa, x, Mi, Ki, nullptr,
                               (int)r, UGh, UGl, Mp, nullptr, pcol,
                               use_drop ? &da : nullptr);

@@ -65,13 +65,14 @@ size_t gemm_split_bytes(const GemmSplit& sp) {
   return gemm_split_part_offset(sp) + size_t(sp.rem) * sp.tile * sp.tile * 4;
 }
 
-StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt) {
+StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt, bool drop) {
   StreamPlan P;
-  P.rm = rs_rm(mode, jt);
-  P.sub = rs_sub(mode, jt);
+  P.rm = rs_rm(mode, jt, drop);
+  P.sub = rs_sub(mode, jt, drop);
   P.mb = (int)cdiv(M, P.rm);
   const int64_t nst = cdiv(C, 64 * P.sub);
-  const int64_t want = std::max<int64_t>(1, cdiv(256, P.mb));
+  const int64_t want =
+      std::max<int64_t>(1, cdiv(int64_t(G_CUS) * rs_wgs_per_cu(mode, jt, drop), P.mb));
   const int64_t nb = std::min(nst, want);
   P.cpb = (int)cdiv(nst, nb);
   P.nb = (int)cdiv(nst, P.cpb);
@@ -155,7 +156,9 @@ FwdWorkspace fwd_workspace_layout(int64_t M, int64_t N, int64_t K,
     L.total = align256(skinny_part_bytes(M, P));
     return L;
   }
-  const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r));
+  // (a general layout also fits the T pass with dropout, whose plan has at
+  // least as many column blocks)
+  const StreamPlan P = stream_plan(RS_ROWS, M, K, rank_tiles(r), general);
   size_t off = 0;
   L.split = off;   // status word first
   off += align256(gemm_split_bytes(split ? gemm_split_plan(M, N, K, false)
@@ -179,7 +182,8 @@ BwdWorkspace bwd_workspace_layout(int64_t M, int64_t N, int64_t K,
   L.rpad = 16 * jt;
   L.mp = cdiv(M, 8) * 8;
   const StreamPlan Pg = stream_plan(RS_ROWS | RS_COLS, M, N, jt);
-  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
+  // the dA pass with dropout may have more row blocks
+  const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt, true);
   const size_t pcol = std::max(size_t(Pg.mb) * N, size_t(Pa.mb) * K);
   size_t off = 0;
   L.split = off;   // status word first

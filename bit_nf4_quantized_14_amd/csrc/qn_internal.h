@@ -79,12 +79,24 @@ enum { RS_ROWS = 1, RS_COLS = 2 };
 // sums write one fp32 partial [C][rpad] per RM rows, so they keep RM = 256
 // up to r = 64 (with two buffers at r = 64: 64 KB of S, 16 KB of R and
 // 67.6 KB of U).
-constexpr int rs_rm(int mode, int jt) {
-  return mode == RS_ROWS ? 64 : (jt <= 4 ? 256 : 64);
+//
+// The passes over X with LoRA dropout (RS_ROWS: T, RS_COLS: dA) spend most
+// of their time in the generator's integer arithmetic, which one wave per
+// SIMD cannot overlap with its own loads, so they run two workgroups per
+// CU where the LDS allows: the T pass up to jt = 8 with half-width stages
+// (at most 72 KB each), the dA pass up to jt = 4 with 128-row blocks (at
+// most 67 KB each; twice the column-sum partials).
+constexpr int rs_wgs_per_cu(int mode, int jt, bool drop) {
+  return drop && ((mode == RS_ROWS && jt <= 8) || (mode == RS_COLS && jt <= 4)) ? 2 : 1;
 }
-constexpr int rs_sub(int mode, int jt) {
-  return jt >= 8 ? 1
-                 : (jt == 4 ? (mode == RS_ROWS ? 2 : 1) : (mode == RS_ROWS ? 4 : 1));
+constexpr int rs_rm(int mode, int jt, bool drop = false) {
+  return mode == RS_ROWS ? 64
+                         : (jt <= 4 ? (rs_wgs_per_cu(mode, jt, drop) == 2 ? 128 : 256) : 64);
+}
+constexpr int rs_sub(int mode, int jt, bool drop = false) {
+  return (jt >= 8 ? 1
+                  : (jt == 4 ? (mode == RS_ROWS ? 2 : 1) : (mode == RS_ROWS ? 4 : 1))) /
+         (mode == RS_ROWS && rs_wgs_per_cu(mode, jt, drop) == 2 && jt < 8 ? 2 : 1);
 }
 constexpr int rs_nbuf(int mode, int jt) {
   return jt >= 16 || (jt == 4 && mode != RS_ROWS) ? 2 : 3;
@@ -94,7 +106,7 @@ struct StreamPlan {
   int rm, sub, mb, nb, cpb;   // rows per block, stage width (x64), row
                               // blocks, column blocks, stages per block
 };
-StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt);
+StreamPlan stream_plan(int mode, int64_t M, int64_t C, int jt, bool drop = false);
 
 // ---- skinny forward (skinny.hip), M <= QN_SKINNY_M tokens.
 constexpr int64_t QN_SKINNY_M = 16;

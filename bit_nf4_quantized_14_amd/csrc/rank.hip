@@ -117,11 +117,11 @@ __device__ __forceinline__ u32x4 rs_read_colT(const char* tile, int row0,
   return v;
 }
 
-template <int MODE, int JT>
+template <int MODE, int JT, bool DROP>
 struct RsCfg {
   static constexpr bool ROWS = (MODE & RS_ROWS) != 0;
   static constexpr bool COLS = (MODE & RS_COLS) != 0;
-  static constexpr int RM = rs_rm(MODE, JT), SUB = rs_sub(MODE, JT);
+  static constexpr int RM = rs_rm(MODE, JT, DROP), SUB = rs_sub(MODE, JT, DROP);
   static constexpr int NBUF = rs_nbuf(MODE, JT);
   static constexpr int RP = 16 * JT, PU = RM + 8, TR = RM / 64;
   static constexpr int S_BYTES = SUB * RM * 128;
@@ -148,12 +148,12 @@ __device__ __forceinline__ void wg_barrier() {
 #define RS_WAIT_VM(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (((n) >> 4) << 14))
 
-template <int MODE, int JT>
+template <int MODE, int JT, bool DROP>
 __device__ __forceinline__ void rs_stage_dma(rsrc_t rs, rsrc_t rr, char* dS,
                                              char* dR, int64_t C, int nvalid,
                                              int r, int stage, int wave,
                                              int lane) {
-  using G = RsCfg<MODE, JT>;
+  using G = RsCfg<MODE, JT, DROP>;
 #pragma unroll
   for (int u = 0; u < G::SUB; ++u) {
     const int col0 = (stage * G::SUB + u) * 64;
@@ -173,10 +173,10 @@ __device__ __forceinline__ void rs_stage_dma(rsrc_t rs, rsrc_t rr, char* dS,
 template <int MODE, int JT, bool DROP>
 __device__ __forceinline__ void rs_stage_compute(
     const char* sS, const char* sR, const uint16_t* sUh, const uint16_t* sUl,
-    int wave, int lane, f32x4 (&accR)[RsCfg<MODE, JT>::TR][JT],
-    f32x4 (&accC)[RsCfg<MODE, JT>::SUB][JT], int stage, int m0,
+    int wave, int lane, f32x4 (&accR)[RsCfg<MODE, JT, DROP>::TR][JT],
+    f32x4 (&accC)[RsCfg<MODE, JT, DROP>::SUB][JT], int stage, int m0,
     const DropArgs& dp) {
-  using G = RsCfg<MODE, JT>;
+  using G = RsCfg<MODE, JT, DROP>;
 #pragma unroll
   for (int u = 0; u < G::SUB; ++u) {
     const char* tS = sS + u * G::RM * 128;
@@ -224,11 +224,11 @@ __device__ __forceinline__ void rs_stage_compute(
 // c = 64 (SUB stage + u) + 16 wave + 4 (l / 16) + v, j = 16 t + l % 16.
 // Buffer stores: columns past C fall outside the range and are dropped, so
 // every wave issues the same stores.
-template <int MODE, int JT>
+template <int MODE, int JT, bool DROP>
 __device__ __forceinline__ void rs_store_cols(
     rsrc_t rc, int stage, int C, int wave, int lane,
-    const f32x4 (&accC)[RsCfg<MODE, JT>::SUB][JT]) {
-  using G = RsCfg<MODE, JT>;
+    const f32x4 (&accC)[RsCfg<MODE, JT, DROP>::SUB][JT]) {
+  using G = RsCfg<MODE, JT, DROP>;
 #pragma unroll
   for (int u = 0; u < G::SUB; ++u) {
     const int cb = (stage * G::SUB + u) * 64 + 16 * wave + 4 * (lane >> 4);
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void k_rank_stream(
     const uint16_t* __restrict__ R, int r, const uint16_t* __restrict__ Uh,
     const uint16_t* __restrict__ Ul, int ldu, int cpb,
     float* __restrict__ prow, float* __restrict__ pcol, DropArgs dp) {
-  using G = RsCfg<MODE, JT>;
+  using G = RsCfg<MODE, JT, DROP>;
   // distinct buffers, so the compiler can tell the tile being filled from
   // the tiles being read
   __shared__ __attribute__((aligned(16))) char sS0[G::S_BYTES];
@@ -297,10 +297,10 @@ __global__ __launch_bounds__(256) void k_rank_stream(
       ul[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rul, off, 0, 0));
     }
   }
-  rs_stage_dma<MODE, JT>(rs, rr, sS0, sR0, C, nvalid, r, sb, wave, lane);
+  rs_stage_dma<MODE, JT, DROP>(rs, rr, sS0, sR0, C, nvalid, r, sb, wave, lane);
   const bool two = G::NBUF == 3 && sb + 1 < se;
   if (two)
-    rs_stage_dma<MODE, JT>(rs, rr, sS1, sR1, C, nvalid, r, sb + 1, wave, lane);
+    rs_stage_dma<MODE, JT, DROP>(rs, rr, sS1, sR1, C, nvalid, r, sb + 1, wave, lane);
   if constexpr (G::COLS) {
 #pragma unroll
     for (int k = 0; k < UL; ++k) {
@@ -324,15 +324,15 @@ __global__ __launch_bounds__(256) void k_rank_stream(
 #define RS_BODY(I, CS, CR, FS, FR)                                            \
   do {                                                                        \
     if (G::COLS && (I) > sb)                                                  \
-      rs_store_cols<MODE, JT>(rc, (I) - 1, C, wave, lane, accC);              \
+      rs_store_cols<MODE, JT, DROP>(rc, (I) - 1, C, wave, lane, accC);              \
     const bool ahead_ = (I) + G::NBUF - 1 < se;                               \
     if (G::NBUF == 2 && ahead_)                                               \
-      rs_stage_dma<MODE, JT>(rs, rr, FS, FR, C, nvalid, r, (I) + 1, wave,     \
+      rs_stage_dma<MODE, JT, DROP>(rs, rr, FS, FR, C, nvalid, r, (I) + 1, wave,     \
                              lane);                                           \
     rs_stage_compute<MODE, JT, DROP>(CS, CR, sUh, sUl, wave, lane, accR,      \
                                      accC, (I), m0, dp);                      \
     if (G::NBUF == 3 && ahead_) {                                             \
-      rs_stage_dma<MODE, JT>(rs, rr, FS, FR, C, nvalid, r, (I) + 2, wave,     \
+      rs_stage_dma<MODE, JT, DROP>(rs, rr, FS, FR, C, nvalid, r, (I) + 2, wave,     \
                              lane);                                           \
       RS_WAIT_VM(G::DMA);                                                     \
     } else {                                                                  \
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256) void k_rank_stream(
     }
   }
 #undef RS_BODY
-  if (G::COLS) rs_store_cols<MODE, JT>(rc, se - 1, C, wave, lane, accC);
+  if (G::COLS) rs_store_cols<MODE, JT, DROP>(rc, se - 1, C, wave, lane, accC);
   if (G::ROWS) {
     // accR[tr][t][v] = P[m = wave RM/4 + 16 tr + 4 (l / 16) + v][j = 16 t + l % 16]
     float* dst = prow + ((int64_t)blockIdx.x * M + m0) * G::RP;

@@ -16,6 +16,7 @@
 // * skinny_bounds: the slots' tile runs are contiguous, cover every tile, and
 //   each slot starts at the first tile whose cost starts at or after its
 //   share of the total (checked against a walk over every tile).
+#include <algorithm>
 #include <cstdio>
 #include <vector>
 
@@ -138,7 +139,10 @@ static void layouts() {
                 M, N, K);
           continue;
         }
-        const StreamPlan P = stream_plan(RS_ROWS, M, K, jt);
+        // a general layout holds the T pass of a forward with dropout too
+        const StreamPlan P = stream_plan(RS_ROWS, M, K, jt, general != 0);
+        check(P.nb >= stream_plan(RS_ROWS, M, K, jt).nb, "dropout T plan has fewer blocks",
+              M, N, K);
         check((long long)P.mb * P.rm >= M, "T stream rows", M, N, K);
         check((long long)P.nb * P.cpb * 64 * P.sub >= K, "T stream columns", M, N, K);
         const GemmSplit sp = gemm_split_plan(M, N, K, false);
@@ -153,12 +157,15 @@ static void layouts() {
       const BwdWorkspace b = bwd_workspace_layout(M, N, K, r);
       const StreamPlan Pg = stream_plan(RS_ROWS | RS_COLS, M, N, jt);
       const StreamPlan Pa = stream_plan(RS_COLS, M, K, jt);
-      check((long long)Pg.mb * Pg.rm >= M && (long long)Pa.mb * Pa.rm >= M,
+      const StreamPlan Pad = stream_plan(RS_COLS, M, K, jt, true);   // with dropout
+      check((long long)Pg.mb * Pg.rm >= M && (long long)Pa.mb * Pa.rm >= M &&
+                (long long)Pad.mb * Pad.rm >= M,
             "dY / dA stream rows", M, N, K);
+      check((long long)Pad.nb * Pad.cpb * 64 * Pad.sub >= K, "dA stream columns", M, N, K);
       check((long long)Pg.nb * Pg.cpb * 64 * Pg.sub >= N, "dY stream columns", M, N, K);
       check(b.mp % 8 == 0 && b.mp >= M, "Mp", M, N, K);
       check(b.split == 0, "split area not first (backward)", M, N, K);
-      const size_t pcol = std::max(size_t(Pg.mb) * N, size_t(Pa.mb) * K);
+      const size_t pcol = std::max({size_t(Pg.mb) * N, size_t(Pa.mb) * K, size_t(Pad.mb) * K});
       check_regions({{b.split, gemm_split_bytes(gemm_split_plan(M, K, N, false))},
                      {b.bt, size_t(r) * N * 2},
                      {b.uth, size_t(r) * b.mp * 2},
