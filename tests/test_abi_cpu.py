@@ -239,8 +239,11 @@ def test_dropout_validation():
         wd = capi.qlora_workspace_bytes(M, 4096, 4096, 16, capi.QN_FWD_DROPOUT)
         assert wd > 0
         assert wd != capi.qlora_workspace_bytes(M, 4096, 4096, 16, capi.QN_FWD)
+    # above the skinny threshold both take the general path; the dropout
+    # layout also holds the T pass with dropout (two workgroups per CU, so
+    # possibly more column-block partials)
     assert (capi.qlora_workspace_bytes(64, 256, 512, 8, capi.QN_FWD_DROPOUT)
-            == capi.qlora_workspace_bytes(64, 256, 512, 8, capi.QN_FWD))
+            >= capi.qlora_workspace_bytes(64, 256, 512, 8, capi.QN_FWD))
     assert capi.qlora_workspace_bytes(64, 256, 512, 8, 3) == 0
 
 
